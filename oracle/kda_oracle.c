@@ -1,0 +1,161 @@
+/*
+ * KDA oracle: a plain, slow fp64 CPU implementation of Kimi Delta Attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline do.  It shares no code with the HIP kernels.
+ *
+ * What it computes.  The kern page ("kern", section "The manifest") declares
+ * the KDA linear-attention state as memory that outlives a step, one slot per
+ * sequence; the K3 package page ("kern-k3-pp-prefill", section "P: the
+ * packed prefill") runs the KDA layers over up to 16 sequences packed back to
+ * back and split by cu_seqlens, each with its own state; the same page's
+ * section "D inside SGLang" stores that state as [slot][head][v][k] f32.
+ * The pages name the layer but never write its update.  This file takes the
+ * plainest reading, the gated delta rule with a per-key-channel decay that
+ * defines KDA:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * with S a d_k x d_v matrix per (sequence, head).  It is evaluated here in the
+ * equivalent loop form, one token at a time and in order:
+ *
+ *     S   <- Diag(exp(g_t)) S          decay, per key channel
+ *     r   <- S^T k_t                   what the state returns for k_t
+ *     S   <- S + beta_t k_t (v_t - r)^T
+ *     o_t <- scale * S^T q_t           inclusive of token t
+ *
+ * Expanding the first form gives exactly the second (the erase term
+ * beta k k^T Diag(a) S is beta k r^T), so the two agree up to rounding.
+ * The literal matrix-product form is pinned against this loop by the tests.
+ *
+ * Layouts (all row-major, all fp64):
+ *   q, k, g   [T][H][d_k]      v   [T][H][d_v]      beta [T][H]
+ *   o         [T][H][d_v]
+ *   s_in, s_out  [N][H][d_v][d_k]   (the pages' [v][k] order; entry (j, i)
+ *                                    holds S[i][j])
+ *   cu_seqlens [N+1], sequence n owns rows cu_seqlens[n] .. cu_seqlens[n+1]-1.
+ * s_in may be NULL (zero initial state).  Independent (sequence, head) pairs
+ * are spread over plain threads; each pair runs the loop above unchanged.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    const double *q, *k, *v, *g, *beta;
+    const int32_t *cu;
+    int32_t N, H, dk, dv;
+    const double *s_in;
+    double *s_out, *o;
+    double scale;
+    int32_t next_task;          /* guarded by mu */
+    pthread_mutex_t mu;
+} job_t;
+
+/* One (sequence n, head h) pair, token by token. */
+static void run_pair(const job_t *J, int32_t n, int32_t h, double *S, double *r)
+{
+    const int32_t H = J->H, dk = J->dk, dv = J->dv;
+    /* S is d_k x d_v, S[i*dv + j] */
+    if (J->s_in) {
+        const double *src = J->s_in + ((size_t)n * H + h) * (size_t)dv * dk;
+        for (int32_t i = 0; i < dk; ++i)
+            for (int32_t j = 0; j < dv; ++j)
+                S[(size_t)i * dv + j] = src[(size_t)j * dk + i];
+    } else {
+        memset(S, 0, sizeof(double) * (size_t)dk * dv);
+    }
+    for (int32_t t = J->cu[n]; t < J->cu[n + 1]; ++t) {
+        const double *qt = J->q + ((size_t)t * H + h) * dk;
+        const double *kt = J->k + ((size_t)t * H + h) * dk;
+        const double *gt = J->g + ((size_t)t * H + h) * dk;
+        const double *vt = J->v + ((size_t)t * H + h) * dv;
+        const double bt = J->beta[(size_t)t * H + h];
+        /* decay */
+        for (int32_t i = 0; i < dk; ++i) {
+            const double a = exp(gt[i]);
+            for (int32_t j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a;
+        }
+        /* retrieval r = S^T k */
+        for (int32_t j = 0; j < dv; ++j) r[j] = 0.0;
+        for (int32_t i = 0; i < dk; ++i)
+            for (int32_t j = 0; j < dv; ++j) r[j] += S[(size_t)i * dv + j] * kt[i];
+        /* delta-rule write */
+        for (int32_t i = 0; i < dk; ++i)
+            for (int32_t j = 0; j < dv; ++j)
+                S[(size_t)i * dv + j] += bt * kt[i] * (vt[j] - r[j]);
+        /* output o_t = scale * S^T q */
+        double *ot = J->o + ((size_t)t * H + h) * dv;
+        for (int32_t j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int32_t i = 0; i < dk; ++i) acc += S[(size_t)i * dv + j] * qt[i];
+            ot[j] = J->scale * acc;
+        }
+    }
+    double *dst = J->s_out + ((size_t)n * H + h) * (size_t)dv * dk;
+    for (int32_t i = 0; i < dk; ++i)
+        for (int32_t j = 0; j < dv; ++j)
+            dst[(size_t)j * dk + i] = S[(size_t)i * dv + j];
+}
+
+static void *worker(void *arg)
+{
+    job_t *J = (job_t *)arg;
+    double *S = (double *)malloc(sizeof(double) * (size_t)J->dk * J->dv);
+    double *r = (double *)malloc(sizeof(double) * (size_t)J->dv);
+    if (!S || !r) { free(S); free(r); return (void *)1; }
+    const int32_t ntask = J->N * J->H;
+    for (;;) {
+        pthread_mutex_lock(&J->mu);
+        const int32_t task = J->next_task++;
+        pthread_mutex_unlock(&J->mu);
+        if (task >= ntask) break;
+        run_pair(J, task / J->H, task % J->H, S, r);
+    }
+    free(S);
+    free(r);
+    return NULL;
+}
+
+/*
+ * Returns 0 on success, -1 on bad arguments, -2 on allocation or thread
+ * failure.  num_threads < 1 means 1.
+ */
+int kda_oracle_prefill(const double *q, const double *k, const double *v,
+                       const double *g, const double *beta,
+                       const int32_t *cu_seqlens, int32_t num_seqs,
+                       int32_t num_heads, int32_t d_k, int32_t d_v,
+                       const double *s_in, double *s_out, double *o,
+                       double scale, int32_t num_threads)
+{
+    if (num_seqs < 0 || num_heads < 1 || d_k < 1 || d_v < 1) return -1;
+    if (!cu_seqlens || !s_out || (num_seqs > 0 && !o && cu_seqlens[num_seqs] > 0)) return -1;
+    for (int32_t n = 0; n < num_seqs; ++n)
+        if (cu_seqlens[n + 1] < cu_seqlens[n]) return -1;
+    job_t J;
+    J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.cu = cu_seqlens;
+    J.N = num_seqs; J.H = num_heads; J.dk = d_k; J.dv = d_v;
+    J.s_in = s_in; J.s_out = s_out; J.o = o; J.scale = scale;
+    J.next_task = 0;
+    pthread_mutex_init(&J.mu, NULL);
+    if (num_threads < 1) num_threads = 1;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)num_threads);
+    if (!th) { pthread_mutex_destroy(&J.mu); return -2; }
+    int rc = 0, started = 0;
+    for (int32_t i = 0; i < num_threads; ++i) {
+        if (pthread_create(&th[i], NULL, worker, &J) != 0) { rc = -2; break; }
+        ++started;
+    }
+    for (int32_t i = 0; i < started; ++i) {
+        void *ret = NULL;
+        pthread_join(th[i], &ret);
+        if (ret) rc = -2;
+    }
+    free(th);
+    pthread_mutex_destroy(&J.mu);
+    return rc;
+}

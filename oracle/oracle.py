@@ -1,0 +1,170 @@
+"""KDA oracle: fp64 CPU reference for the chunked prefill and the decode step.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module.  It shares no code
+with the HIP path: the recurrence lives in ``kda_oracle.c`` (plain C, fp64),
+built with gcc, and this module only marshals numpy arrays and applies the
+state-pool bookkeeping that the boundary documents.
+
+The recurrence (see ``kda_oracle.c``) is the gated delta rule with a
+per-key-channel decay, run token by token:
+
+    S <- Diag(exp(g_t)) S;  S <- S + beta_t k_t (v_t - S^T k_t)^T;  o_t = scale S^T q_t
+
+State pools follow the kern-k3-pp-prefill page, section "D inside SGLang":
+``[slot][head][v][k]`` fp32, so pool entry ``(j, i)`` holds ``S[i][j]``.
+Sequence bookkeeping follows the same page, section "P: the packed prefill":
+sequences packed back to back, split by ``cu_seqlens``.
+
+Slot semantics (mirroring the boundary): sequence ``n`` uses slot
+``slots[n]`` (or ``n`` when ``slots`` is None).  When ``slots`` is given and
+``slots[n]`` lies outside ``[0, num_slots)``, the sequence is a padded row:
+its output rows are left untouched and no state is read or written, as the
+"D inside SGLang" section describes for slot -1.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc into ``oracle/libkda_oracle.so``."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        lib.kda_oracle_prefill.restype = ctypes.c_int
+        lib.kda_oracle_prefill.argtypes = [dp, dp, dp, dp, dp, ip, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, dp, dp, dp,
+                                           ctypes.c_double, ctypes.c_int32]
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _f64(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def recurrence(q, k, v, g, beta, cu_seqlens, s0=None, scale=1.0, threads=None):
+    """Run the token-by-token fp64 recurrence.
+
+    q, k, g: [T, H, d_k]; v: [T, H, d_v]; beta: [T, H]; cu_seqlens: [N+1];
+    s0: per-sequence initial states [N, H, d_v, d_k] or None (zeros).
+    Returns (o [T, H, d_v] fp64, s_final [N, H, d_v, d_k] fp64).
+    """
+    q, k, v, g, beta = (_f64(a) for a in (q, k, v, g, beta))
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = cu.shape[0] - 1
+    if k.shape != (T, H, dk) or g.shape != (T, H, dk) or v.shape[:2] != (T, H) or beta.shape != (T, H):
+        raise ValueError("shape mismatch")
+    if N < 0 or (N > 0 and (cu[0] != 0 or cu[-1] > T)):
+        raise ValueError("bad cu_seqlens")
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    s_out = np.zeros((max(N, 0), H, dv, dk), dtype=np.float64)
+    if s0 is not None:
+        s0 = _f64(s0)
+        if s0.shape != (N, H, dv, dk):
+            raise ValueError("s0 must be [N, H, d_v, d_k]")
+    if N == 0:
+        return o, s_out
+    nt = threads if threads is not None else default_threads()
+    dp = ctypes.c_double
+    rc = _load().kda_oracle_prefill(
+        _ptr(q, dp), _ptr(k, dp), _ptr(v, dp), _ptr(g, dp), _ptr(beta, dp),
+        _ptr(cu, ctypes.c_int32), N, H, dk, dv,
+        _ptr(s0, dp) if s0 is not None else None, _ptr(s_out, dp), _ptr(o, dp),
+        float(scale), int(nt))
+    if rc != 0:
+        raise RuntimeError("kda_oracle_prefill failed with %d" % rc)
+    return o, s_out
+
+
+def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool=None, slots=None, scale=1.0,
+                  o_init=None, threads=None):
+    """The boundary's prefill semantics on top of the recurrence.
+
+    state_pool: [num_slots, H, d_v, d_k] or None (zero initial states, final
+    states not kept).  slots: [N] or None (identity).  o_init: the contents of
+    the output buffer before the call (rows of skipped sequences keep them);
+    zeros when None.
+    Returns (o [T,H,d_v] fp64, pool_out [num_slots,H,d_v,d_k] fp64 or None,
+    s_final [N,H,d_v,d_k] fp64 with zeros for skipped sequences).
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    T, H, dk = np.shape(q)
+    dv = np.shape(v)[2]
+    num_slots = 0 if state_pool is None else np.shape(state_pool)[0]
+    if slots is None:
+        sl = np.arange(N, dtype=np.int64)
+        live = np.ones(N, dtype=bool)
+    else:
+        sl = np.asarray(slots, dtype=np.int64)
+        live = (sl >= 0) & (sl < num_slots) if state_pool is not None else np.ones(N, dtype=bool)
+    if state_pool is not None:
+        pool = _f64(state_pool)
+        s0 = np.zeros((N, H, dv, dk), dtype=np.float64)
+        s0[live] = pool[sl[live]]
+    else:
+        pool = None
+        s0 = None
+    o, s_fin = recurrence(q, k, v, g, beta, cu.astype(np.int32), s0=s0, scale=scale, threads=threads)
+    o_out = np.zeros((T, H, dv), dtype=np.float64) if o_init is None else _f64(o_init).copy()
+    for n in range(N):
+        if live[n]:
+            o_out[cu[n]:cu[n + 1]] = o[cu[n]:cu[n + 1]]
+    s_fin[~live] = 0.0
+    pool_out = None
+    if pool is not None:
+        pool_out = pool.copy()
+        pool_out[sl[live]] = s_fin[live]
+    return o_out, pool_out, s_fin
+
+
+def decode_step(q, k, v, g, beta, state_pool, slots, scale=1.0, o_init=None, threads=None):
+    """One token per sequence, state updated in place in the pool.
+
+    q, k, g: [N, H, d_k]; v: [N, H, d_v]; beta: [N, H]; state_pool:
+    [num_slots, H, d_v, d_k]; slots [N] (entries outside [0, num_slots) are
+    padded rows: o untouched, no state touched).
+    Returns (o [N,H,d_v] fp64, pool_out fp64).
+    """
+    N = np.shape(q)[0]
+    cu = np.arange(N + 1, dtype=np.int32)
+    o, pool_out, _ = chunk_prefill(q, k, v, g, beta, cu, state_pool=state_pool, slots=slots,
+                                   scale=scale, o_init=o_init, threads=threads)
+    return o, pool_out

@@ -1,0 +1,300 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test fixes one part of the recurrence so that a plausible slip (a dropped
+decay, decay after the write, output before the update, a wrong sign, a
+transposed state, exp2 for exp, a wrong head or sequence index) fails at least
+one of them:
+
+* hand-worked d=2 example (tests/golden/hand_worked_d2_t2.txt): order of decay
+  and write, sign, inclusive output, [v][k] state layout, natural exp;
+* literal matrix products (I - beta k k^T) Diag(exp g) S + beta k v^T on T <= 4
+  with random S0 over several heads and sequences: the whole algebra;
+* beta = 0: pure decay closed form; g = 0 and beta = 0: identity;
+* beta = 1, |k| = 1, q = k: o_t = v_t exactly, for any decay;
+* orthonormal keys e_i, beta = 1, g = 0: row i of S replaced by v_t;
+* split continuity, linearity in (v, S0), value-column independence;
+* varlen independence and permutation of the pack;
+* the chunk (WY) form in ``oracle/chunked.py`` against the recurrence.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import chunked, oracle
+from linear_attention_prefill_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_inputs(rng, T, H, dk, dv, unit_k=True):
+    q = rng.standard_normal((T, H, dk))
+    k = rng.standard_normal((T, H, dk))
+    if unit_k:
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, H, dv))
+    g = -np.logaddexp(0.0, rng.standard_normal((T, H, dk)))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal((T, H))))
+    return q, k, v, g, beta
+
+
+def _literal(q, k, v, g, beta, cu, s0):
+    """(I - beta k k^T) Diag(exp g) S + beta k v^T, o = S^T q, as explicit
+    matrix products per token (written independently of the oracle)."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    N = len(cu) - 1
+    o = np.zeros((T, H, dv))
+    sf = np.zeros((N, H, dv, dk))
+    for n in range(N):
+        for h in range(H):
+            S = s0[n, h].T.copy()
+            for t in range(cu[n], cu[n + 1]):
+                kt = k[t, h][:, None]
+                M = np.eye(dk) - beta[t, h] * (kt @ kt.T)
+                S = M @ np.diag(np.exp(g[t, h])) @ S + beta[t, h] * kt @ v[t, h][None, :]
+                o[t, h] = S.T @ q[t, h]
+            sf[n, h] = S.T
+    return o, sf
+
+
+def test_hand_worked_example():
+    vals = {}
+    with open(os.path.join(GOLDEN, "hand_worked_d2_t2.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *nums = line.split()
+            vals[key] = np.array([float(x) for x in nums])
+    T, H, d = 2, 1, 2
+    q = np.stack([vals["t1_q"], vals["t2_q"]])[:, None, :]
+    k = np.stack([vals["t1_k"], vals["t2_k"]])[:, None, :]
+    v = np.stack([vals["t1_v"], vals["t2_v"]])[:, None, :]
+    g = np.log(np.stack([vals["t1_expg"], vals["t2_expg"]]))[:, None, :]
+    beta = np.array([vals["t1_beta"][0], vals["t2_beta"][0]])[:, None]
+    s0 = vals["s0_pool"].reshape(1, 1, d, d)
+    o, sf = oracle.recurrence(q, k, v, g, beta, [0, 2], s0=s0)
+    np.testing.assert_allclose(o[0, 0], vals["o1"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o[1, 0], vals["o2"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(sf[0, 0].ravel(), vals["s2_pool"], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_brute_force_literal_products(T):
+    rng = np.random.default_rng(100 + T)
+    H, dk, dv = 3, 5, 4
+    # two sequences of length T, plus random initial states
+    q, k, v, g, beta = _rand_inputs(rng, 2 * T, H, dk, dv, unit_k=False)
+    cu = [0, T, 2 * T]
+    s0 = rng.standard_normal((2, H, dv, dk))
+    o_ref, s_ref = _literal(q, k, v, g, beta, cu, s0)
+    o, sf = oracle.recurrence(q, k, v, g, beta, cu, s0=s0)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(sf, s_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_beta_zero_is_pure_decay():
+    rng = np.random.default_rng(7)
+    T, H, dk, dv = 37, 2, 8, 6
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    beta[:] = 0.0
+    s0 = rng.standard_normal((1, H, dv, dk))
+    o, sf = oracle.recurrence(q, k, v, g, beta, [0, T], s0=s0)
+    gam = np.cumsum(g, axis=0)  # inclusive [T, H, dk]
+    for h in range(H):
+        S0 = s0[0, h].T
+        np.testing.assert_allclose(sf[0, h].T, np.exp(gam[-1, h])[:, None] * S0, rtol=1e-12, atol=1e-14)
+        o_cf = (q[:, h] * np.exp(gam[:, h])) @ S0
+        np.testing.assert_allclose(o[:, h], o_cf, rtol=1e-11, atol=1e-14)
+
+
+def test_identity_when_no_decay_no_write():
+    rng = np.random.default_rng(8)
+    T, H, dk, dv = 20, 2, 6, 7
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    g[:] = 0.0
+    beta[:] = 0.0
+    s0 = rng.standard_normal((1, H, dv, dk))
+    o, sf = oracle.recurrence(q, k, v, g, beta, [0, T], s0=s0)
+    np.testing.assert_array_equal(sf, s0)
+    for h in range(H):
+        np.testing.assert_allclose(o[:, h], q[:, h] @ s0[0, h].T, rtol=1e-13, atol=1e-14)
+
+
+def test_unit_key_full_write_returns_value():
+    """beta = 1, |k| = 1 and q = k give S_t^T k_t = v_t for any decay."""
+    rng = np.random.default_rng(9)
+    T, H, dk, dv = 50, 3, 16, 8
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    beta[:] = 1.0
+    q = k.copy()
+    s0 = rng.standard_normal((1, H, dv, dk))
+    o, _ = oracle.recurrence(q, k, v, g, beta, [0, T], s0=s0)
+    np.testing.assert_allclose(o, v, rtol=1e-11, atol=1e-11)
+
+
+def test_orthonormal_keys_replace_rows():
+    rng = np.random.default_rng(10)
+    T, H, dk, dv = 12, 1, 4, 3
+    q, _, v, _, _ = _rand_inputs(rng, T, H, dk, dv)
+    idx = rng.integers(0, dk, T)
+    k = np.zeros((T, H, dk))
+    k[np.arange(T), 0, idx] = 1.0
+    g = np.zeros((T, H, dk))
+    beta = np.ones((T, H))
+    S = rng.standard_normal((dk, dv))
+    s0 = S.T[None, None].copy()
+    o, sf = oracle.recurrence(q, k, v, g, beta, [0, T], s0=s0)
+    for t in range(T):
+        S[idx[t]] = v[t, 0]
+        np.testing.assert_allclose(o[t, 0], S.T @ q[t, 0], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(sf[0, 0], S.T, rtol=0, atol=1e-14)
+
+
+def test_split_continuity():
+    rng = np.random.default_rng(11)
+    T1, T2, H, dk, dv = 70, 45, 2, 16, 16
+    q, k, v, g, beta = _rand_inputs(rng, T1 + T2, H, dk, dv)
+    s0 = rng.standard_normal((1, H, dv, dk)) * 0.1
+    o_all, s_all = oracle.recurrence(q, k, v, g, beta, [0, T1 + T2], s0=s0)
+    o1, s1 = oracle.recurrence(q[:T1], k[:T1], v[:T1], g[:T1], beta[:T1], [0, T1], s0=s0)
+    o2, s2 = oracle.recurrence(q[T1:], k[T1:], v[T1:], g[T1:], beta[T1:], [0, T2], s0=s1)
+    np.testing.assert_allclose(np.concatenate([o1, o2]), o_all, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(s2, s_all, rtol=1e-12, atol=1e-13)
+
+
+def test_linearity_in_values_and_state():
+    rng = np.random.default_rng(12)
+    T, H, dk, dv = 40, 2, 8, 8
+    q, k, v1, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    v2 = rng.standard_normal(v1.shape)
+    s1 = rng.standard_normal((1, H, dv, dk))
+    s2 = rng.standard_normal((1, H, dv, dk))
+    a, b = 0.7, -1.3
+    oa, sa = oracle.recurrence(q, k, v1, g, beta, [0, T], s0=s1)
+    ob, sb = oracle.recurrence(q, k, v2, g, beta, [0, T], s0=s2)
+    oc, sc = oracle.recurrence(q, k, a * v1 + b * v2, g, beta, [0, T], s0=a * s1 + b * s2)
+    np.testing.assert_allclose(oc, a * oa + b * ob, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(sc, a * sa + b * sb, rtol=1e-11, atol=1e-12)
+
+
+def test_value_columns_are_independent():
+    """Column j of S depends only on column j of v and of S0: running on a
+    subset of value columns returns exactly those columns."""
+    rng = np.random.default_rng(13)
+    T, H, dk, dv = 60, 2, 8, 10
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    s0 = rng.standard_normal((1, H, dv, dk))
+    cols = np.array([1, 4, 9])
+    o, sf = oracle.recurrence(q, k, v, g, beta, [0, T], s0=s0)
+    o_s, sf_s = oracle.recurrence(q, k, v[:, :, cols], g, beta, [0, T], s0=s0[:, :, cols])
+    np.testing.assert_array_equal(o_s, o[:, :, cols])
+    np.testing.assert_array_equal(sf_s, sf[:, :, cols])
+
+
+def test_scale_multiplies_output_only():
+    rng = np.random.default_rng(14)
+    T, H, dk, dv = 30, 1, 8, 8
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    o1, s1 = oracle.recurrence(q, k, v, g, beta, [0, T])
+    o2, s2 = oracle.recurrence(q, k, v, g, beta, [0, T], scale=0.125)
+    np.testing.assert_allclose(o2, 0.125 * o1, rtol=1e-14, atol=0)
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_varlen_independence_and_permutation():
+    rng = np.random.default_rng(15)
+    L = [5, 0, 64, 1, 77, 13]
+    H, dk, dv = 2, 8, 8
+    cu = W.cu_from_lengths(L)
+    T = int(cu[-1])
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    s0 = rng.standard_normal((len(L), H, dv, dk))
+    o, sf = oracle.recurrence(q, k, v, g, beta, cu, s0=s0)
+    for n in range(len(L)):
+        a, b = cu[n], cu[n + 1]
+        on, sn = oracle.recurrence(q[a:b], k[a:b], v[a:b], g[a:b], beta[a:b], [0, b - a], s0=s0[n:n + 1])
+        np.testing.assert_array_equal(o[a:b], on)
+        np.testing.assert_array_equal(sf[n], sn[0])
+    # permuting the pack permutes the outputs
+    perm = rng.permutation(len(L))
+    rows = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in perm])
+    cu_p = W.cu_from_lengths([L[n] for n in perm])
+    op, sp = oracle.recurrence(q[rows], k[rows], v[rows], g[rows], beta[rows], cu_p, s0=s0[perm])
+    np.testing.assert_array_equal(op, o[rows])
+    np.testing.assert_array_equal(sp, sf[perm])
+
+
+def test_zero_length_sequence_copies_state():
+    rng = np.random.default_rng(16)
+    H, dk, dv = 2, 4, 4
+    q, k, v, g, beta = _rand_inputs(rng, 3, H, dk, dv)
+    s0 = rng.standard_normal((2, H, dv, dk))
+    _, sf = oracle.recurrence(q, k, v, g, beta, [0, 0, 3], s0=s0)
+    np.testing.assert_array_equal(sf[0], s0[0])
+
+
+@pytest.mark.parametrize("chunk", [1, 16, 64])
+@pytest.mark.parametrize("T", [1, 65, 77, 130, 200, 256])
+def test_chunk_form_matches_recurrence(chunk, T):
+    rng = np.random.default_rng(1000 + T + chunk)
+    H, dk, dv = 2, 16, 12
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    s0 = rng.standard_normal((1, H, dv, dk)) * 0.1
+    o_ref, s_ref = oracle.recurrence(q, k, v, g, beta, [0, T], s0=s0, scale=0.5)
+    o_c, s_c = chunked.chunk_prefill(q, k, v, g, beta, [0, T], s0=s0, chunk=chunk, scale=0.5)
+    np.testing.assert_allclose(o_c, o_ref, rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(s_c, s_ref, rtol=1e-10, atol=1e-11)
+
+
+def test_chunk_form_packed_varlen():
+    rng = np.random.default_rng(17)
+    L = [1, 63, 64, 65, 0, 130]
+    cu = W.cu_from_lengths(L)
+    T = int(cu[-1])
+    H, dk, dv = 2, 8, 8
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    s0 = rng.standard_normal((len(L), H, dv, dk)) * 0.1
+    o_ref, s_ref = oracle.recurrence(q, k, v, g, beta, cu, s0=s0)
+    o_c, s_c = chunked.chunk_prefill(q, k, v, g, beta, cu, s0=s0, chunk=64)
+    np.testing.assert_allclose(o_c, o_ref, rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(s_c, s_ref, rtol=1e-10, atol=1e-11)
+
+
+def test_pool_semantics_gather_scatter_and_padding():
+    """Slots gather the initial states and scatter the final ones; a slot
+    outside the pool marks a padded sequence that touches nothing."""
+    c = W.random_case(21, [3, 0, 9, 4], H=2, d_k=8, d_v=8, io_dtype="f32", num_slots=7)
+    slots = np.array([5, 2, -1, 0], dtype=np.int32)
+    o_init = np.full((c.T, c.H, c.d_v), 7.0)
+    o, pool_out, _ = oracle.chunk_prefill(c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens,
+                                          state_pool=c.state_pool, slots=slots, o_init=o_init)
+    cu = c.cu_seqlens
+    # padded sequence 2: output rows untouched
+    np.testing.assert_array_equal(o[cu[2]:cu[3]], o_init[cu[2]:cu[3]])
+    # untouched slots keep their bytes
+    for s in (1, 3, 4, 6):
+        np.testing.assert_array_equal(pool_out[s], c.state_pool[s])
+    # zero-length sequence 1 copies slot 2 through
+    np.testing.assert_array_equal(pool_out[2], c.state_pool[2].astype(np.float64))
+    # sequence 0 equals running it alone from slot 5
+    o0, s0 = oracle.recurrence(c.q[:3], c.k[:3], c.v[:3], c.g[:3], c.beta[:3], [0, 3],
+                               s0=c.state_pool[5:6])
+    np.testing.assert_array_equal(o[:3], o0)
+    np.testing.assert_array_equal(pool_out[5], s0[0])
+
+
+def test_decode_is_one_recurrence_step():
+    c = W.random_case(22, [1] * 6, H=2, d_k=8, d_v=8, io_dtype="f32", num_slots=9)
+    o, pool_out = oracle.decode_step(c.q, c.k, c.v, c.g, c.beta, c.state_pool, c.slots)
+    for n in range(6):
+        S = c.state_pool[c.slots[n]].astype(np.float64)  # [H, dv, dk]
+        for h in range(2):
+            St = S[h].T * np.exp(c.g[n, h].astype(np.float64))[:, None]
+            kk = c.k[n, h].astype(np.float64)
+            d = c.beta[n, h] * (c.v[n, h] - St.T @ kk)
+            St = St + np.outer(kk, d)
+            np.testing.assert_allclose(o[n, h], St.T @ c.q[n, h], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(pool_out[c.slots[n], h], St.T, rtol=1e-12, atol=1e-13)
