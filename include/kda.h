@@ -1,0 +1,167 @@
+/*
+ * kda.h - C ABI of the MI355X (gfx950) KDA library, libkda.so.
+ *
+ * KDA (Kimi Delta Attention) is the linear-attention layer whose per-sequence
+ * recurrent state the kern runtime keeps as a fixed slot ("kern" page,
+ * section "The manifest": a state declared by bytes per sequence and handed
+ * out as slots from one pool).  Per (sequence, head) the state S is a
+ * d_k x d_v fp32 matrix and each token t updates it by the gated delta rule
+ * with a per-key-channel decay:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t
+ *
+ * The pages name the layer without writing this update; the form above is the
+ * plainest reading and the one the fp64 test oracle implements.
+ *
+ * Memory layouts (row-major, element strides implied, no padding):
+ *   q, k      [T][H][d_k]   io dtype (bf16 or fp32)
+ *   v, o      [T][H][d_v]   io dtype
+ *   g         [T][H][d_k]   fp32, natural-log decay per key channel, g <= 0
+ *   beta      [T][H]        fp32
+ *   state     [num_slots][H][d_v][d_k] fp32: element (slot, h, j, i) holds
+ *             S[i][j], the "[slot][head][v][k] f32" layout of the
+ *             kern-k3-pp-prefill page, section "D inside SGLang".
+ *   cu_seqlens [N+1] int32 on the device: sequence n owns rows
+ *             cu_seqlens[n] .. cu_seqlens[n+1]-1 (the packed prefill of the
+ *             same page, section "P: the packed prefill": up to 16 sequences
+ *             back to back, split by cu_seqlens).
+ *   slots     [N] int32 on the device, or NULL for slot n = n.
+ *
+ * Ownership and execution.  The caller owns every buffer, including the
+ * workspace; the library allocates nothing, keeps no mutable global state and
+ * caches no tensors.  Every call validates its arguments on the host and
+ * returns a status before anything is launched; then it enqueues its kernels
+ * on `stream` (a hipStream_t; NULL is the null stream) and returns without
+ * synchronising.  It never reads device memory on the host, so a call can be
+ * captured into a HIP graph (the "kern" page, section "Hosts": launches
+ * enqueue on the host's stream, inside its graphs).  All pointers are device
+ * pointers and must be 16-byte aligned.
+ *
+ * Device data is not validated on the host (that would need a sync).  The
+ * kernels clamp it so that no access leaves the buffers: cu_seqlens entries
+ * are clamped to [0, T] and each sequence to [cu[n], T]; a slot outside
+ * [0, num_slots) marks a padded sequence.  Results for non-monotone
+ * cu_seqlens or duplicate slots are unspecified.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL */
+    KDA_ERR_SHAPE = 2,       /* a size is out of range */
+    KDA_ERR_DTYPE = 3,       /* unknown io dtype */
+    KDA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    KDA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
+    KDA_ERR_UNSUPPORTED = 6, /* d_k or d_v not 64 or 128 */
+    KDA_ERR_HIP = 7          /* a kernel launch failed */
+} kda_status_t;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+
+/* Sizes of one prefill call.  T = total_rows, N = num_seqs, H = num_heads. */
+typedef struct {
+    int32_t total_rows;  /* T >= 0 */
+    int32_t num_seqs;    /* N >= 1 */
+    int32_t num_heads;   /* H >= 1 */
+    int32_t d_k;         /* 64 or 128 */
+    int32_t d_v;         /* 64 or 128 */
+    int32_t num_slots;   /* rows of the state pools (the slot index space) */
+    int32_t io_dtype;    /* kda_dtype_t of q, k, v and o */
+    float scale;         /* multiplies o only */
+} kda_prefill_desc_t;
+
+/*
+ * Bytes of device workspace kda_chunk_prefill needs for `desc` (0 if desc is
+ * invalid).  The workspace holds the per-chunk operands that pass from the
+ * intra-chunk kernel to the state scan; it is scratch for one call.
+ */
+size_t kda_prefill_workspace_size(const kda_prefill_desc_t *desc);
+
+/*
+ * Chunked prefill over a packed batch of sequences (the "P: the packed
+ * prefill" section of the kern-k3-pp-prefill page; the chunk geometry of 64
+ * rows with 16-row sub-blocks follows the prhub report on SGLang PR #32890,
+ * section "关键源码片段").  Chunks never straddle sequences; the varlen
+ * bookkeeping is done on the device, with no host sync (same report, section
+ * "关键文件", chunk_fwd.py).
+ *
+ * For each sequence n with slot s = slots ? slots[n] : n:
+ *   - if 0 <= s < num_slots: the initial state is state_in[s] (zeros when
+ *     state_in is NULL); rows cu[n]..cu[n+1]-1 of o are written; the final
+ *     state is written to state_out[s] (skipped when state_out is NULL).
+ *     state_out may equal state_in (updated in place).  A zero-length
+ *     sequence copies its state through.
+ *   - otherwise the sequence is a padded row: its o rows and every state slot
+ *     are left untouched.
+ * Slots not named by any live sequence are never read or written.
+ *
+ * Errors (returned before any launch): KDA_ERR_NULL for NULL desc, q, k, v,
+ * g, beta, cu_seqlens, or o (when T > 0), or a NULL workspace of nonzero
+ * required size; KDA_ERR_SHAPE for T < 0, N < 1, H < 1, num_slots < 0, or
+ * slots == NULL with a state pool given and num_slots < N; KDA_ERR_DTYPE;
+ * KDA_ERR_UNSUPPORTED; KDA_ERR_ALIGN; KDA_ERR_WORKSPACE when ws_bytes is below
+ * kda_prefill_workspace_size(desc); KDA_ERR_HIP if a launch fails.
+ */
+kda_status_t kda_chunk_prefill(const void *q, const void *k, const void *v,
+                               const float *g, const float *beta,
+                               const int32_t *cu_seqlens,
+                               const float *state_in, float *state_out,
+                               void *o, const int32_t *slots,
+                               const kda_prefill_desc_t *desc,
+                               void *workspace, size_t ws_bytes,
+                               void *stream);
+
+/*
+ * kda_chunk_prefill with per-kernel timing: when `events` is not NULL it
+ * points to three hipEvent_t that are recorded on `stream` before the
+ * intra-chunk kernel, between it and the state scan, and after the scan, so
+ * the caller can read each kernel's duration with hipEventElapsedTime.  The
+ * events are created and owned by the caller.  Results and errors are those of
+ * kda_chunk_prefill.
+ */
+kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v,
+                                     const float *g, const float *beta,
+                                     const int32_t *cu_seqlens,
+                                     const float *state_in, float *state_out,
+                                     void *o, const int32_t *slots,
+                                     const kda_prefill_desc_t *desc,
+                                     void *workspace, size_t ws_bytes,
+                                     void *stream, void *const *events);
+
+/*
+ * One decode token per sequence, state updated in place (the KDA step of the
+ * kern-k3-pp-prefill page, section "D: TP8 / EP8 / DCP8"; padded rows with
+ * slot -1 are skipped as in its section "D inside SGLang").
+ *   q, k, g [N][H][d_k]; v, o [N][H][d_v]; beta [N][H];
+ *   state_pool [num_slots][H][d_v][d_k] fp32, read and written in place;
+ *   slots [N] int32 (required): a slot outside [0, num_slots) leaves that
+ *   sequence's o rows and all state untouched.
+ * Errors as for kda_chunk_prefill (N, H >= 1; num_slots >= 1).
+ */
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
+                             const float *g, const float *beta,
+                             float *state_pool, const int32_t *slots, void *o,
+                             int32_t num_seqs, int32_t num_heads,
+                             int32_t d_k, int32_t d_v, int32_t num_slots,
+                             int32_t io_dtype, float scale, void *stream);
+
+/* Static description of a status code. */
+const char *kda_status_string(kda_status_t status);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,1 +1,7 @@
-"""MI355X-native KDA (Kimi Delta Attention) chunked prefill and decode."""
+"""MI355X-native KDA (Kimi Delta Attention): chunked prefill and decode.
+
+The computation runs in hand-written HIP kernels for gfx950 behind the C ABI
+of ``libkda.so`` (``include/kda.h``); ``kda`` is its thin binding.
+"""
+from .kda import (KdaError, chunk_prefill, decode_step, load_library,  # noqa: F401
+                  prefill_workspace_size)

@@ -1,0 +1,84 @@
+"""Ahead-of-time build of libkda.so for gfx950 (hipcc, no JIT at first call).
+
+    python -m linear_attention_prefill_amd.build [--resource-usage]
+
+Compiles every HIP source under csrc/ plus the C ABI into
+``linear_attention_prefill_amd/libkda.so``.  Object files go to ``_build/``.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libkda.so")
+ARCH = "gfx950"
+
+HIP_SOURCES = ["kda_prefill.hip", "kda_decode.hip"]
+CXX_SOURCES = ["kda_api.cpp"]
+
+# Packed fp32 VALU ops are disabled for all device code.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",
+          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
+
+
+def _hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def _rocm() -> str:
+    return os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build(resource_usage: bool = False, verbose: bool = False) -> str:
+    hipcc = _hipcc()
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        cmd = [hipcc, "-x", "hip", "--offload-arch=" + ARCH, *COMMON, *DEVICE_FLAGS,
+               "-c", os.path.join(CSRC, src), "-o", obj]
+        if resource_usage:
+            cmd.append("-Rpass-analysis=kernel-resource-usage")
+        jobs.append((src, obj, cmd))
+    for src in CXX_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        cmd = [hipcc, "-x", "c++", *COMMON, "-D__HIP_PLATFORM_AMD__",
+               "-I" + os.path.join(_rocm(), "include"), "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        jobs.append((src, obj, cmd))
+    procs = [(src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT))
+             for src, obj, cmd in jobs]
+    failed = []
+    for src, obj, p in procs:
+        out = p.communicate()[0].decode(errors="replace")
+        lines = [ln for ln in out.splitlines() if "not a recognized feature" not in ln]
+        if resource_usage or verbose or p.returncode != 0:
+            sys.stdout.write("\n".join(lines) + ("\n" if lines else ""))
+        if p.returncode != 0:
+            failed.append(src)
+    if failed:
+        raise RuntimeError("hipcc failed for: " + ", ".join(failed))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    link = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp,
+            *[obj for _, obj, _ in jobs]]
+    subprocess.check_call(link)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--resource-usage", action="store_true")
+    args = ap.parse_args()
+    print(build(resource_usage=args.resource_usage))

@@ -1,0 +1,138 @@
+// C ABI of libkda.so: host-side validation, workspace sizing and dispatch.
+// Nothing here touches device memory or synchronises; every error is
+// returned before the first launch.
+#include "../../include/kda.h"
+#include "kda_launch.h"
+
+#include <limits.h>
+
+namespace {
+
+using bf16 = __bf16;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dims_supported(int dk, int dv) {
+    return (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
+}
+
+template <typename E>
+hipError_t dispatch_prefill(const kda::PrefillArgs &a, int dk, int dv, hipStream_t s) {
+    if (dk == 64 && dv == 64) return kda::launch_prefill<E, 64, 64>(a, s);
+    if (dk == 64 && dv == 128) return kda::launch_prefill<E, 64, 128>(a, s);
+    if (dk == 128 && dv == 64) return kda::launch_prefill<E, 128, 64>(a, s);
+    return kda::launch_prefill<E, 128, 128>(a, s);
+}
+
+template <typename E>
+hipError_t dispatch_decode(const kda::DecodeArgs &a, int dk, int dv, hipStream_t s) {
+    if (dk == 64 && dv == 64) return kda::launch_decode<E, 64, 64>(a, s);
+    if (dk == 64 && dv == 128) return kda::launch_decode<E, 64, 128>(a, s);
+    if (dk == 128 && dv == 64) return kda::launch_decode<E, 128, 64>(a, s);
+    return kda::launch_decode<E, 128, 128>(a, s);
+}
+
+// Shape checks shared by the workspace query and the call.
+kda_status_t check_desc(const kda_prefill_desc_t *d) {
+    if (!d) return KDA_ERR_NULL;
+    if (d->io_dtype != KDA_F32 && d->io_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (!dims_supported(d->d_k, d->d_v)) return KDA_ERR_UNSUPPORTED;
+    if (d->total_rows < 0 || d->num_seqs < 1 || d->num_heads < 1 || d->num_slots < 0)
+        return KDA_ERR_SHAPE;
+    if (d->num_heads > 65535) return KDA_ERR_SHAPE;                       // grid.y of the intra kernel
+    const long long chunks = (long long)d->total_rows / 64 + d->num_seqs;
+    if (chunks > INT_MAX) return KDA_ERR_SHAPE;
+    if ((long long)d->num_seqs * d->num_heads * (d->d_v / 16) > INT_MAX) return KDA_ERR_SHAPE;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_prefill_workspace_size(const kda_prefill_desc_t *desc) {
+    if (check_desc(desc) != KDA_OK) return 0;
+    return kda::prefill_workspace_bytes(desc->total_rows, desc->num_seqs, desc->num_heads,
+                                        desc->d_k, desc->d_v, desc->io_dtype == KDA_BF16);
+}
+
+kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v,
+                                     const float *g, const float *beta,
+                                     const int32_t *cu_seqlens, const float *state_in,
+                                     float *state_out, void *o, const int32_t *slots,
+                                     const kda_prefill_desc_t *desc, void *workspace,
+                                     size_t ws_bytes, void *stream, void *const *events) {
+    const kda_status_t st = check_desc(desc);
+    if (st != KDA_OK) return st;
+    const kda_prefill_desc_t d = *desc;
+    if (!slots && (state_in || state_out) && d.num_slots < d.num_seqs) return KDA_ERR_SHAPE;
+    if (!q || !k || !v || !g || !beta || !cu_seqlens) return KDA_ERR_NULL;
+    if (!o && d.total_rows > 0) return KDA_ERR_NULL;
+    const size_t need = kda::prefill_workspace_bytes(d.total_rows, d.num_seqs, d.num_heads,
+                                                     d.d_k, d.d_v, d.io_dtype == KDA_BF16);
+    if (need > 0 && !workspace) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g, beta, cu_seqlens, state_in, state_out, o, slots, workspace};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    if (ws_bytes < need) return KDA_ERR_WORKSPACE;
+
+    kda::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens;
+    a.state_in = state_in; a.state_out = state_out; a.o = o; a.slots = slots;
+    a.workspace = workspace;
+    a.T = d.total_rows; a.N = d.num_seqs; a.H = d.num_heads; a.num_slots = d.num_slots;
+    a.scale = d.scale;
+    for (int i = 0; i < 3; ++i) a.events[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = d.io_dtype == KDA_BF16 ? dispatch_prefill<bf16>(a, d.d_k, d.d_v, s)
+                                                : dispatch_prefill<float>(a, d.d_k, d.d_v, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_chunk_prefill(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const int32_t *cu_seqlens,
+                               const float *state_in, float *state_out, void *o,
+                               const int32_t *slots, const kda_prefill_desc_t *desc,
+                               void *workspace, size_t ws_bytes, void *stream) {
+    return kda_chunk_prefill_timed(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, slots,
+                                   desc, workspace, ws_bytes, stream, nullptr);
+}
+
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, float *state_pool, const int32_t *slots, void *o,
+                             int32_t num_seqs, int32_t num_heads, int32_t d_k, int32_t d_v,
+                             int32_t num_slots, int32_t io_dtype, float scale, void *stream) {
+    if (io_dtype != KDA_F32 && io_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (!dims_supported(d_k, d_v)) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs < 1 || num_heads < 1 || num_slots < 1) return KDA_ERR_SHAPE;
+    if ((long long)num_seqs * num_heads * (d_v / 64) > INT_MAX) return KDA_ERR_SHAPE;
+    if (!q || !k || !v || !g || !beta || !state_pool || !slots || !o) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g, beta, state_pool, slots, o};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.pool = state_pool; a.slots = slots;
+    a.o = o; a.N = num_seqs; a.H = num_heads; a.num_slots = num_slots; a.scale = scale;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = io_dtype == KDA_BF16 ? dispatch_decode<bf16>(a, d_k, d_v, s)
+                                              : dispatch_decode<float>(a, d_k, d_v, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+const char *kda_status_string(kda_status_t status) {
+    switch (status) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL: return "a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "a size is out of range";
+        case KDA_ERR_DTYPE: return "unknown io dtype";
+        case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case KDA_ERR_WORKSPACE: return "workspace too small";
+        case KDA_ERR_UNSUPPORTED: return "d_k and d_v must be 64 or 128";
+        case KDA_ERR_HIP: return "a HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int32_t kda_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+// Device-side building blocks shared by the KDA kernels (gfx950, wave64).
+//
+// Matrix-core fragments.  Every contraction in the chunked prefill is issued
+// as 16x16 output tiles over 32-wide slabs of the contraction index:
+//   bf16: one v_mfma_f32_16x16x32_bf16 per slab;
+//   fp32: eight v_mfma_f32_16x16x4_f32 per slab (exact fp32 products).
+// Lane l = 16*g + i (i = l % 16, g = l / 16) of a wave holds, for a slab:
+//   A operand (16 x 32): row i, eight contraction indices kk(g, 0..7);
+//   B operand (32 x 16): column i, the same eight contraction indices;
+//   C/D (16 x 16):       column i, rows 4g + 0..3.
+// The contraction index order inside a slab is free as long as A and B agree,
+// so all operands use kk(g, e) = 4g + (e & 3) + 16 (e >> 2).  With this order
+// two stacked 16x16 accumulator tiles (rows 0..15 and 16..31 of a slab) are
+// already a B operand lane for lane, which lets the state and the corrected
+// values stay in registers between contractions with no shuffles.
+// Swapping the A and B registers of a product yields its transpose, with lane
+// (i, g) holding D[i][4g + r]; that layout is the A operand of a later
+// product, which is how the intra-chunk kernel writes w in the scan's order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 64;      // rows per chunk
+constexpr int kSub = 16;        // rows per sub-block / MFMA tile edge
+constexpr int kSlab = 32;       // contraction slab
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int kk_of(int g, int e) { return 4 * g + (e & 3) + 16 * (e >> 2); }
+
+// Eight-element operand fragment in the io element type.
+template <typename E> struct Frag;
+template <> struct Frag<bf16> {
+    bf16x8 x;
+    __device__ __forceinline__ void set(int e, float v) { x[e] = (bf16)v; }
+    __device__ __forceinline__ float get(int e) const { return (float)x[e]; }
+};
+template <> struct Frag<float> {
+    f32x4 lo, hi;
+    __device__ __forceinline__ void set(int e, float v) {
+        if (e < 4) lo[e] = v; else hi[e - 4] = v;
+    }
+    __device__ __forceinline__ float get(int e) const { return e < 4 ? lo[e] : hi[e - 4]; }
+};
+
+__device__ __forceinline__ void mma(f32x4 &acc, const Frag<bf16> &a, const Frag<bf16> &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.x, b.x, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4 &acc, const Frag<float> &a, const Frag<float> &b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[0], b.lo[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[1], b.lo[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[2], b.lo[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[3], b.lo[3], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[0], b.hi[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[1], b.hi[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[2], b.hi[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[3], b.hi[3], acc, 0, 0, 0);
+}
+
+// Two stacked C tiles (slab rows 0..15 in t0, 16..31 in t1) as a B operand.
+template <typename E>
+__device__ __forceinline__ Frag<E> frag_from_tiles(const f32x4 &t0, const f32x4 &t1) {
+    Frag<E> f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { f.set(r, t0[r]); f.set(4 + r, t1[r]); }
+    return f;
+}
+
+// Global fragment load/store: one fragment is 64 lanes x 8 elements,
+// contiguous per lane, so a wave moves 1 KiB (bf16) or 2 KiB (fp32) with
+// perfectly coalesced 16-byte accesses.
+template <typename E>
+__device__ __forceinline__ Frag<E> load_frag(const E *base, int lane);
+template <>
+__device__ __forceinline__ Frag<bf16> load_frag<bf16>(const bf16 *base, int lane) {
+    Frag<bf16> f;
+    f.x = *reinterpret_cast<const bf16x8 *>(base + 8 * lane);
+    return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> load_frag<float>(const float *base, int lane) {
+    Frag<float> f;
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(base + 8 * lane);
+    f.lo = p[0];
+    f.hi = p[1];
+    return f;
+}
+template <typename E>
+__device__ __forceinline__ void store_frag(E *base, int lane, const Frag<E> &f);
+template <>
+__device__ __forceinline__ void store_frag<bf16>(bf16 *base, int lane, const Frag<bf16> &f) {
+    *reinterpret_cast<bf16x8 *>(base + 8 * lane) = f.x;
+}
+template <>
+__device__ __forceinline__ void store_frag<float>(float *base, int lane, const Frag<float> &f) {
+    f32x4 *p = reinterpret_cast<f32x4 *>(base + 8 * lane);
+    p[0] = f.lo;
+    p[1] = f.hi;
+}
+
+// Four consecutive io elements <-> float4.
+template <typename E> __device__ __forceinline__ f32x4 load4(const E *p);
+template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16 *p) {
+    bf16x4 x = *reinterpret_cast<const bf16x4 *>(p);
+    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+template <> __device__ __forceinline__ f32x4 load4<float>(const float *p) {
+    return *reinterpret_cast<const f32x4 *>(p);
+}
+template <typename E> __device__ __forceinline__ void store4(E *p, const f32x4 &v);
+template <> __device__ __forceinline__ void store4<bf16>(bf16 *p, const f32x4 &v) {
+    bf16x4 x;
+    x[0] = (bf16)v[0]; x[1] = (bf16)v[1]; x[2] = (bf16)v[2]; x[3] = (bf16)v[3];
+    *reinterpret_cast<bf16x4 *>(p) = x;
+}
+template <> __device__ __forceinline__ void store4<float>(float *p, const f32x4 &v) {
+    *reinterpret_cast<f32x4 *>(p) = v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Varlen bookkeeping shared by the prefill kernels.  Sequence n starts at
+// row clamp(cu[n], 0, T) and ends at clamp(cu[n+1], start, T).  Its chunks
+// take the ids floor(start / 64) + n + j, j = 0 .. ceil(len / 64) - 1; these
+// ranges are disjoint across sequences and all ids are below T / 64 + N, so
+// every chunk has a workspace record without any prefix sum over sequences.
+struct SeqSpan {
+    int start, len, first_chunk;
+};
+__device__ __forceinline__ int clamp_row(int x, int T) { return x < 0 ? 0 : (x > T ? T : x); }
+__device__ __forceinline__ SeqSpan seq_span(const int32_t *cu, int n, int T) {
+    SeqSpan s;
+    s.start = clamp_row(cu[n], T);
+    int end = clamp_row(cu[n + 1], T);
+    s.len = end > s.start ? end - s.start : 0;
+    s.first_chunk = s.start / kChunk + n;
+    return s;
+}
+
+// Workspace record layout: one record per (chunk id, head), all fragments in
+// the scan's lane order.  Offsets are in elements of type E except `dec`.
+template <typename E, int DK, int DV> struct WsLayout {
+    static constexpr int kWElems = kChunk * DK;           // w:    4 x (DK/32) frags
+    static constexpr int kQElems = kChunk * DK;           // q*exp(Gamma): same
+    static constexpr int kKElems = DK * kChunk;           // K~^T: (DK/16) x 2 frags
+    static constexpr int kAElems = kChunk * kChunk;       // A_qk: 4 x 2 frags
+    static constexpr int kUElems = kChunk * DV;           // u: (DV/16) tiles x 64 lanes x 16
+    static constexpr int kRecElems = kWElems + kQElems + kKElems + kAElems + kUElems;
+};
+
+}  // namespace kda

@@ -1,0 +1,42 @@
+// Internal launch interface between the C ABI (kda_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const int32_t *cu_seqlens;
+    const float *state_in;
+    float *state_out;
+    void *o;
+    const int32_t *slots;
+    void *workspace;
+    int T, N, H, num_slots;
+    float scale;
+    hipEvent_t events[3];   // optional: before intra, between, after scan
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float *pool;
+    const int32_t *slots;
+    void *o;
+    int N, H, num_slots;
+    float scale;
+};
+
+template <typename E, int DK, int DV>
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+template <typename E, int DK, int DV>
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+size_t prefill_workspace_bytes(int T, int N, int H, int dk, int dv, bool bf16);
+
+}  // namespace kda

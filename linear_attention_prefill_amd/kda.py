@@ -1,0 +1,204 @@
+"""Python binding of libkda.so: argument marshalling only.
+
+Every step of the computation runs in the HIP kernels behind the C ABI
+(``include/kda.h``).  PyTorch supplies device memory and the current stream;
+nothing here computes.  If the library is missing the calls raise: there is
+no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_F32 = 0
+KDA_BF16 = 1
+
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
+          4: "KDA_ERR_ALIGN", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_HIP"}
+
+
+class PrefillDesc(ctypes.Structure):
+    _fields_ = [("total_rows", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("num_slots", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s (%d): %s" % (STATUS.get(status, "?"), status, msg))
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libkda.so (built by ``python -m linear_attention_prefill_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError("libkda.so is not built (%s); run "
+                           "`python -m linear_attention_prefill_amd.build`" % p)
+    lib = ctypes.CDLL(p)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.kda_prefill_workspace_size.restype = sz
+    lib.kda_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillDesc)]
+    lib.kda_chunk_prefill.restype = ctypes.c_int
+    lib.kda_chunk_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      ctypes.POINTER(PrefillDesc), vp, sz, vp]
+    lib.kda_chunk_prefill_timed.restype = ctypes.c_int
+    lib.kda_chunk_prefill_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            ctypes.POINTER(PrefillDesc), vp, sz, vp,
+                                            ctypes.POINTER(ctypes.c_void_p)]
+    lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
+                                    i32, i32, i32, i32, i32, i32, f32, vp]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_version.restype = i32
+    lib.kda_version.argtypes = []
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise KdaError(status, load_library().kda_status_string(status).decode())
+
+
+def _io_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return KDA_BF16
+    if dt == torch.float32:
+        return KDA_F32
+    raise ValueError("q, k, v must be bfloat16 or float32, got %s" % dt)
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_desc(T, N, H, d_k, d_v, num_slots, io_dtype, scale=1.0) -> PrefillDesc:
+    return PrefillDesc(int(T), int(N), int(H), int(d_k), int(d_v), int(num_slots),
+                       int(io_dtype), float(scale))
+
+
+def prefill_workspace_size(T, N, H, d_k, d_v, dtype=torch.bfloat16) -> int:
+    d = make_desc(T, N, H, d_k, d_v, N, _io_code(dtype))
+    return int(load_library().kda_prefill_workspace_size(ctypes.byref(d)))
+
+
+def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o=None,
+                  slots=None, num_slots=None, scale=1.0, workspace=None, stream=None,
+                  events=None):
+    """KDA chunked prefill over packed sequences (see ``kda_chunk_prefill``).
+
+    q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype); g: [T, H, d_k]
+    fp32; beta: [T, H] fp32; cu_seqlens: [N+1] int32 (device); state_in /
+    state_out: [num_slots, H, d_v, d_k] fp32 pools or None (may be the same
+    tensor); slots: [N] int32 or None.  events: optional three recorded
+    torch.cuda.Event(enable_timing=True) objects, recorded before the
+    intra-chunk kernel, between the kernels and after the scan
+    (``kda_chunk_prefill_timed``).  Returns o [T, H, d_v].
+    """
+    lib = load_library()
+    _dev(q, "q")
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    io = _io_code(q.dtype)
+    _dev(k, "k", q.dtype, (T, H, dk))
+    _dev(v, "v", q.dtype, (T, H, dv))
+    _dev(g, "g", torch.float32, (T, H, dk))
+    _dev(beta, "beta", torch.float32, (T, H))
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    N = cu_seqlens.shape[0] - 1
+    pools = [p for p in (state_in, state_out) if p is not None]
+    if num_slots is None:
+        num_slots = pools[0].shape[0] if pools else N
+    for name, p in (("state_in", state_in), ("state_out", state_out)):
+        _dev(p, name, torch.float32, (num_slots, H, dv, dk) if p is not None else None)
+    _dev(slots, "slots", torch.int32, (N,) if slots is not None else None)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+    _dev(o, "o", q.dtype, (T, H, dv))
+    desc = make_desc(T, N, H, dk, dv, num_slots, io, scale)
+    need = int(lib.kda_prefill_workspace_size(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(state_in),
+            _ptr(state_out), _ptr(o), _ptr(slots), ctypes.byref(desc), _ptr(workspace),
+            workspace.numel(), _stream(stream))
+    if events is None:
+        _check(lib.kda_chunk_prefill(*args))
+    else:
+        if len(events) != 3:
+            raise ValueError("events must hold three torch.cuda.Event objects")
+        handles = (ctypes.c_void_p * 3)(*[_event_handle(e) for e in events])
+        _check(lib.kda_chunk_prefill_timed(*args, handles))
+    return o
+
+
+def _event_handle(ev) -> int:
+    """The hipEvent_t behind a torch.cuda.Event (created on first record)."""
+    h = ev.cuda_event
+    if not h:
+        raise ValueError("record each event once before passing it (torch creates it lazily)")
+    return h
+
+
+def decode_step(q, k, v, g, beta, state_pool, slots, o=None, scale=1.0, stream=None):
+    """One token per sequence; state_pool [num_slots, H, d_v, d_k] updated in
+    place (see ``kda_decode_step``).  q, k, g: [N, H, d_k]; v: [N, H, d_v];
+    beta: [N, H]; slots: [N] int32.  Returns o [N, H, d_v]."""
+    lib = load_library()
+    _dev(q, "q")
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    io = _io_code(q.dtype)
+    _dev(k, "k", q.dtype, (N, H, dk))
+    _dev(v, "v", q.dtype, (N, H, dv))
+    _dev(g, "g", torch.float32, (N, H, dk))
+    _dev(beta, "beta", torch.float32, (N, H))
+    _dev(state_pool, "state_pool", torch.float32)
+    num_slots = state_pool.shape[0]
+    _dev(state_pool, "state_pool", torch.float32, (num_slots, H, dv, dk))
+    _dev(slots, "slots", torch.int32, (N,))
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    _dev(o, "o", q.dtype, (N, H, dv))
+    _check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                               _ptr(slots), _ptr(o), N, H, dk, dv, num_slots, io, float(scale),
+                               _stream(stream)))
+    return o

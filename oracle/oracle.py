@@ -62,11 +62,15 @@ def _load():
     return _lib
 
 
+MAX_THREADS = 16   # the host CPU share one GPU job may use
+
+
 def default_threads() -> int:
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    return max(1, min(MAX_THREADS, n))
 
 
 def _f64(x):
@@ -114,11 +118,13 @@ def recurrence(q, k, v, g, beta, cu_seqlens, s0=None, scale=1.0, threads=None):
 
 
 def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool=None, slots=None, scale=1.0,
-                  o_init=None, threads=None):
+                  o_init=None, threads=None, num_slots=None):
     """The boundary's prefill semantics on top of the recurrence.
 
     state_pool: [num_slots, H, d_v, d_k] or None (zero initial states, final
-    states not kept).  slots: [N] or None (identity).  o_init: the contents of
+    states not kept).  slots: [N] or None (identity).  num_slots: the slot
+    index space (default: the pool's rows, or N without a pool); with slots
+    given, a slot outside [0, num_slots) is a padded sequence.  o_init: the contents of
     the output buffer before the call (rows of skipped sequences keep them);
     zeros when None.
     Returns (o [T,H,d_v] fp64, pool_out [num_slots,H,d_v,d_k] fp64 or None,
@@ -128,13 +134,14 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_pool=None, slots=None, sca
     N = cu.shape[0] - 1
     T, H, dk = np.shape(q)
     dv = np.shape(v)[2]
-    num_slots = 0 if state_pool is None else np.shape(state_pool)[0]
+    if num_slots is None:
+        num_slots = N if state_pool is None else np.shape(state_pool)[0]
     if slots is None:
         sl = np.arange(N, dtype=np.int64)
         live = np.ones(N, dtype=bool)
     else:
         sl = np.asarray(slots, dtype=np.int64)
-        live = (sl >= 0) & (sl < num_slots) if state_pool is not None else np.ones(N, dtype=bool)
+        live = (sl >= 0) & (sl < num_slots)
     if state_pool is not None:
         pool = _f64(state_pool)
         s0 = np.zeros((N, H, dv, dk), dtype=np.float64)

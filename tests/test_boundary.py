@@ -1,0 +1,123 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol that
+include/kda.h declares, and rejects bad arguments before any launch.
+
+Only error paths are exercised here (they return before any HIP call), so no
+GPU is needed.  Fake device addresses are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_prefill_amd import kda as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(K.LIB_PATH):
+        from linear_attention_prefill_amd import build
+        build.build()
+    return K.load_library()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    for n in ("kda_chunk_prefill", "kda_decode_step", "kda_prefill_workspace_size",
+              "kda_status_string", "kda_version", "kda_chunk_prefill_timed"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kda_version() == 100
+    for code in range(8):
+        s = lib.kda_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.kda_status_string(99).decode() == "unknown status"
+
+
+def _desc(**kw):
+    d = dict(T=8192, N=16, H=32, dk=128, dv=128, slots=64, io=K.KDA_BF16, scale=1.0)
+    d.update(kw)
+    return K.make_desc(d["T"], d["N"], d["H"], d["dk"], d["dv"], d["slots"], d["io"], d["scale"])
+
+
+def _ws_formula(T, N, H, dk, dv, es):
+    rec = 64 * (3 * dk + 64 + dv) * es + dk * 4
+    return (T // 64 + N) * H * rec
+
+
+def test_workspace_size(lib):
+    for T, N, H, dk, dv, io, es in [(8192, 16, 32, 128, 128, K.KDA_BF16, 2),
+                                    (256, 1, 2, 64, 64, K.KDA_F32, 4),
+                                    (0, 3, 1, 64, 128, K.KDA_BF16, 2),
+                                    (77, 5, 3, 128, 64, K.KDA_F32, 4)]:
+        d = K.make_desc(T, N, H, dk, dv, N, io, 1.0)
+        assert lib.kda_prefill_workspace_size(ctypes.byref(d)) == _ws_formula(T, N, H, dk, dv, es)
+    assert lib.kda_prefill_workspace_size(None) == 0
+    d = _desc(dk=96)
+    assert lib.kda_prefill_workspace_size(ctypes.byref(d)) == 0
+
+
+A = 0x10000  # a 16-byte aligned fake address, never dereferenced
+
+
+def _prefill(lib, desc, q=A, k=A, v=A, g=A, beta=A, cu=A, sin=None, sout=None, o=A, slots=None,
+             ws=A, ws_bytes=1 << 40):
+    return lib.kda_chunk_prefill(q, k, v, g, beta, cu, sin, sout, o, slots,
+                                 ctypes.byref(desc) if desc is not None else None, ws, ws_bytes, None)
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    assert _prefill(lib, None) == 1                                   # NULL desc
+    assert _prefill(lib, _desc(io=7)) == 3                            # dtype
+    assert _prefill(lib, _desc(dk=96)) == 6                           # unsupported d_k
+    assert _prefill(lib, _desc(dv=256)) == 6                          # unsupported d_v
+    assert _prefill(lib, _desc(T=-1)) == 2
+    assert _prefill(lib, _desc(N=0)) == 2
+    assert _prefill(lib, _desc(H=0)) == 2
+    assert _prefill(lib, _desc(slots=-1)) == 2
+    assert _prefill(lib, _desc(H=70000)) == 2
+    # identity slots with a pool smaller than N
+    assert _prefill(lib, _desc(N=16, slots=8), sin=A) == 2
+    for key in ("q", "k", "v", "g", "beta", "cu"):
+        assert _prefill(lib, _desc(), **{key: None}) == 1, key
+    assert _prefill(lib, _desc(), o=None) == 1
+    assert _prefill(lib, _desc(), ws=None) == 1
+    assert _prefill(lib, _desc(), q=A + 8) == 4                       # misaligned
+    assert _prefill(lib, _desc(), sin=A + 4) == 4
+    assert _prefill(lib, _desc(), slots=A + 2) == 4
+    d = _desc()
+    need = lib.kda_prefill_workspace_size(ctypes.byref(d))
+    assert _prefill(lib, d, ws_bytes=need - 1) == 5
+
+
+def _decode(lib, q=A, k=A, v=A, g=A, beta=A, pool=A, slots=A, o=A, N=64, H=32, dk=128, dv=128,
+            ns=64, io=K.KDA_BF16):
+    return lib.kda_decode_step(q, k, v, g, beta, pool, slots, o, N, H, dk, dv, ns, io, 1.0, None)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    assert _decode(lib, io=5) == 3
+    assert _decode(lib, dk=32) == 6
+    assert _decode(lib, N=0) == 2
+    assert _decode(lib, H=0) == 2
+    assert _decode(lib, ns=0) == 2
+    for key in ("q", "k", "v", "g", "beta", "pool", "slots", "o"):
+        assert _decode(lib, **{key: None}) == 1, key
+    assert _decode(lib, pool=A + 4) == 4
+    assert _decode(lib, o=A + 2) == 4

@@ -1,0 +1,247 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances: normwise max|x - ref| / max|ref| per sequence, <= 2e-2 with bf16
+q/k/v/o and <= 1e-4 with fp32 throughout, for o and for the final states.
+Small cases span several 64-row chunks with ragged tails; the five full-size
+workloads run in the configuration bench.py times.
+"""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_prefill_amd import workloads as W
+from oracle import oracle
+from kda_testlib import (TOL, announce, dev, gpu_prefill, oracle_prefill, per_sequence_errors,
+                         rel_err, torch_dtype)
+import linear_attention_prefill_amd as lap
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _check_case(case, tol=None, **kw):
+    tol = TOL[case.io_dtype] if tol is None else tol
+    o_init = np.full((case.T, case.H, case.d_v), 3.0, dtype=np.float32)
+    announce("prefill %s" % case.name)
+    o_g, pool_g = gpu_prefill(case, o_init=o_init, **kw)
+    o_r, pool_r, _ = oracle_prefill(case, o_init=o_init, num_slots=kw.get("num_slots"))
+    live = None
+    if case.slots is not None:
+        ns = kw.get("num_slots") or (case.state_pool.shape[0] if case.state_pool is not None
+                                     else case.N)
+        live = (case.slots >= 0) & (case.slots < ns)
+    eo, es = per_sequence_errors(case, o_g, o_r, pool_g, pool_r, live=live)
+    assert eo <= tol, "o error %.3g > %.3g" % (eo, tol)
+    assert es <= tol, "state error %.3g > %.3g" % (es, tol)
+    return o_g, pool_g, o_r, pool_r, live
+
+
+def test_tiny_prefill_fp32():
+    """1 x 256 rows, H=2, d=64, fp32 throughout, zero initial state."""
+    c = W.tiny_prefill()
+    announce("prefill %s" % c.name)
+    pool = np.zeros((1, c.H, c.d_v, c.d_k), dtype=np.float32)
+    o_g, pool_g = gpu_prefill(c, pool=pool, state_in_null=True)
+    o_r, s_r = oracle.recurrence(c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens)
+    assert rel_err(o_g, o_r) <= 1e-4
+    assert rel_err(pool_g[0], s_r[0]) <= 1e-4
+
+
+SWEEP = [
+    # (seed, lengths, H, d_k, d_v, io)
+    (1, [1], 1, 64, 64, "bf16"),
+    (2, [63], 2, 128, 128, "bf16"),
+    (3, [64], 2, 128, 128, "bf16"),
+    (4, [65], 2, 128, 128, "bf16"),
+    (5, [200, 1, 0, 129, 64, 7], 2, 128, 128, "bf16"),
+    (6, [130, 77, 1, 63], 3, 64, 64, "bf16"),
+    (7, [191, 5], 2, 64, 128, "bf16"),
+    (8, [100, 64, 0, 3], 2, 128, 64, "bf16"),
+    (9, [1, 63, 64, 65, 2, 127, 128, 129, 0, 31, 33, 96, 250, 1, 17, 60], 2, 128, 128, "bf16"),
+    (10, [200, 1, 0, 129, 64, 7], 2, 128, 128, "f32"),
+    (11, [130, 77, 1, 63], 3, 64, 64, "f32"),
+    (12, [191, 5], 2, 64, 128, "f32"),
+    (13, [100, 64, 0, 3], 2, 128, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("seed,lengths,H,dk,dv,io", SWEEP)
+def test_random_sweep(seed, lengths, H, dk, dv, io):
+    c = W.random_case(seed, lengths, H=H, d_k=dk, d_v=dv, io_dtype=io)
+    o_g, pool_g, o_r, pool_r, live = _check_case(c)
+    # slots not named by the call keep their bytes
+    used = set(int(s) for s in c.slots)
+    for s in range(c.state_pool.shape[0]):
+        if s not in used:
+            np.testing.assert_array_equal(pool_g[s], c.state_pool[s])
+
+
+def test_state_in_and_out_separate_buffers():
+    c = W.random_case(21, [70, 3, 129], H=2, d_k=128, d_v=128, io_dtype="bf16")
+    _check_case(c, in_place=False)
+
+
+def test_null_state_in_and_null_state_out():
+    c = W.random_case(22, [70, 3, 129], H=2, d_k=64, d_v=64, io_dtype="f32")
+    announce("prefill %s state_in=NULL" % c.name)
+    o_g, pool_g = gpu_prefill(c, state_in_null=True, in_place=False)
+    zero_pool = np.zeros_like(c.state_pool)
+    o_r, pool_r, _ = oracle_prefill(c, pool=zero_pool)
+    eo, es = per_sequence_errors(c, o_g, o_r, pool_g, pool_r)
+    assert eo <= 1e-4 and es <= 1e-4
+    announce("prefill %s state_out=NULL" % c.name)
+    o_g2, _ = gpu_prefill(c, state_out_null=True)
+    o_r2, _, _ = oracle_prefill(c)
+    assert per_sequence_errors(c, o_g2, o_r2)[0] <= 1e-4
+
+
+def test_padded_sequences_touch_nothing():
+    c = W.random_case(23, [40, 65, 9, 0, 77], H=2, d_k=128, d_v=128, io_dtype="bf16",
+                      num_slots=8, slots=[3, -1, 5, 9, 0])
+    o_g, pool_g, o_r, pool_r, live = _check_case(c)
+    cu = c.cu_seqlens
+    # padded sequences 1 (slot -1) and 3 (slot 9 >= 8): o rows keep the sentinel
+    assert np.all(o_g[cu[1]:cu[2]] == 3.0)
+    for s in (1, 2, 4, 6, 7):
+        np.testing.assert_array_equal(pool_g[s], c.state_pool[s])
+
+
+def test_identity_slots():
+    c = W.random_case(24, [33, 100], H=2, d_k=64, d_v=64, io_dtype="bf16", num_slots=2)
+    c.slots = None
+    _check_case(c)
+
+
+def test_scale_applies_to_output_only():
+    c = W.random_case(25, [90, 14], H=2, d_k=128, d_v=128, io_dtype="f32", scale=0.088)
+    _check_case(c)
+
+
+def test_deterministic_reruns():
+    c = W.random_case(26, [300, 1, 70], H=4, d_k=128, d_v=128, io_dtype="bf16")
+    announce("prefill %s twice" % c.name)
+    o1, p1 = gpu_prefill(c)
+    o2, p2 = gpu_prefill(c)
+    assert np.array_equal(o1, o2) and np.array_equal(p1, p2)
+
+
+def test_split_continuity_across_calls():
+    """Feeding a sequence as two calls equals one call (state carried)."""
+    c = W.random_case(27, [150, 90], H=2, d_k=128, d_v=128, io_dtype="f32", num_slots=1,
+                      slots=[0, 0])
+    whole = W.Case("whole", c.q, c.k, c.v, c.g, c.beta, W.cu_from_lengths([240]), "f32",
+                   state_pool=c.state_pool, slots=np.zeros(1, np.int32))
+    announce("prefill split-continuity whole")
+    o_w, p_w = gpu_prefill(whole)
+    first = W.Case("first", c.q[:150], c.k[:150], c.v[:150], c.g[:150], c.beta[:150],
+                   W.cu_from_lengths([150]), "f32", state_pool=c.state_pool,
+                   slots=np.zeros(1, np.int32))
+    announce("prefill split-continuity first")
+    o_1, p_1 = gpu_prefill(first)
+    second = W.Case("second", c.q[150:], c.k[150:], c.v[150:], c.g[150:], c.beta[150:],
+                    W.cu_from_lengths([90]), "f32", state_pool=p_1, slots=np.zeros(1, np.int32))
+    announce("prefill split-continuity second")
+    o_2, p_2 = gpu_prefill(second)
+    assert rel_err(np.concatenate([o_1, o_2]), o_w) <= 1e-5
+    assert rel_err(p_2, p_w) <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads
+# ---------------------------------------------------------------------------
+
+def test_single_sequence_prefill_full():
+    """1 x 8192 rows, H=32, d=128, bf16; whole o and final state vs the oracle."""
+    c = W.single_seq_prefill()
+    pool = np.zeros((1, c.H, c.d_v, c.d_k), dtype=np.float32)
+    announce("prefill %s" % c.name)
+    o_g, pool_g = gpu_prefill(c, pool=pool, state_in_null=True)
+    o_r, s_r = oracle.recurrence(c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens)
+    eo, es = rel_err(o_g, o_r), rel_err(pool_g[0], s_r[0])
+    announce("  o err %.3e  state err %.3e" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_packed_varlen_prefill_full():
+    """16 Dirichlet-length sequences in 8192 rows, 64-slot pool gathered and
+    scattered; untouched slots keep their bytes."""
+    c = W.packed_varlen_prefill()
+    o_g, pool_g, o_r, pool_r, live = _check_case(c)
+    used = set(int(s) for s in c.slots)
+    for s in range(c.state_pool.shape[0]):
+        if s not in used:
+            np.testing.assert_array_equal(pool_g[s], c.state_pool[s])
+
+
+@pytest.mark.timeout(900)
+def test_long_context_continuation():
+    """262144 tokens as 32 consecutive 8192-row calls, state carried in a
+    one-slot pool; slow decay.  The oracle checks sampled (head, value
+    column) pairs over the whole sequence (value columns evolve
+    independently), on the final state and on the last call's o."""
+    heads = [0, 13, 31]
+    cols = [0, 37, 64, 127]
+    H, d, n_calls = 32, 128, W.LONG_CONTEXT_CALLS
+    pool = torch.zeros((1, H, d, d), dtype=torch.float32, device="cuda")
+    qs, ks, vs, gs, bs = [], [], [], [], []
+    o_last = None
+    for c_idx in range(n_calls):
+        c = W.long_context_call(c_idx)
+        announce("prefill %s (carried state)" % c.name)
+        o = lap.chunk_prefill(dev(c.q, torch.bfloat16), dev(c.k, torch.bfloat16),
+                              dev(c.v, torch.bfloat16), dev(c.g), dev(c.beta),
+                              dev(c.cu_seqlens), state_in=pool, state_out=pool,
+                              slots=dev(c.slots))
+        torch.cuda.synchronize()
+        if c_idx == n_calls - 1:
+            o_last = o.float().cpu().numpy()
+        qs.append(c.q[:, heads]); ks.append(c.k[:, heads]); gs.append(c.g[:, heads])
+        vs.append(c.v[:, heads][:, :, cols]); bs.append(c.beta[:, heads])
+    q, k, v, g, b = (np.concatenate(x) for x in (qs, ks, vs, gs, bs))
+    T = q.shape[0]
+    announce("oracle over %d tokens, heads %s, columns %s" % (T, heads, cols))
+    o_r, s_r = oracle.recurrence(q, k, v, g, b, [0, T])
+    s_g = pool.cpu().numpy()[0][heads][:, cols, :]
+    es = rel_err(s_g, s_r[0])
+    eo = rel_err(o_last[:, heads][:, :, cols], o_r[-8192:])
+    announce("  final-state err %.3e  last-call o err %.3e" % (es, eo))
+    assert es <= TOL["bf16"] and eo <= TOL["bf16"]
+
+
+def _check_decode(c, tol):
+    dt = torch_dtype(c.io_dtype)
+    pool = dev(c.state_pool)
+    o = torch.full((c.N, c.H, c.d_v), 5.0, dtype=dt, device="cuda")
+    announce("decode %s" % c.name)
+    lap.decode_step(dev(c.q, dt), dev(c.k, dt), dev(c.v, dt), dev(c.g), dev(c.beta), pool,
+                    dev(c.slots), o=o, scale=c.scale)
+    torch.cuda.synchronize()
+    o_g, pool_g = o.float().cpu().numpy(), pool.cpu().numpy()
+    o_init = np.full((c.N, c.H, c.d_v), 5.0)
+    o_r, pool_r = oracle.decode_step(c.q, c.k, c.v, c.g, c.beta, c.state_pool, c.slots,
+                                     scale=c.scale, o_init=o_init)
+    ns = c.state_pool.shape[0]
+    for n in range(c.N):
+        s = int(c.slots[n])
+        if 0 <= s < ns:
+            assert rel_err(o_g[n], o_r[n]) <= tol
+            assert rel_err(pool_g[s], pool_r[s]) <= tol
+        else:
+            assert np.all(o_g[n] == 5.0)
+    used = set(int(s) for s in c.slots)
+    for s in range(ns):
+        if s not in used:
+            np.testing.assert_array_equal(pool_g[s], c.state_pool[s])
+
+
+def test_decode_full():
+    """64 sequences x 1 token, H=32, d=128, bf16, 64-slot pool in place."""
+    _check_decode(W.decode_case(), TOL["bf16"])
+
+
+@pytest.mark.parametrize("dk,dv,io", [(64, 64, "f32"), (128, 64, "f32"), (64, 128, "bf16"),
+                                      (128, 128, "f32")])
+def test_decode_small_with_padding(dk, dv, io):
+    c = W.random_case(30 + dk + dv, [1] * 9, H=3, d_k=dk, d_v=dv, io_dtype=io, num_slots=12,
+                      slots=[4, -1, 0, 11, 7, 12, 2, 9, 5], scale=0.7)
+    _check_decode(c, TOL[io])
