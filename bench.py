@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""KDA prefill throughput on one MI355X, with the roofline of the dominant kernel.
+
+    python bench.py [--steps K] [--warmup W] [--workload single|packed]
+
+A step is one kda_chunk_prefill call (intra-chunk kernel + state scan) over
+one 8192-row chunk, with inputs already resident in HBM.  The default
+workload is one sequence of 8192 rows, H=32, d_k=d_v=128, bf16 q/k/v/o, fp32
+g/beta/state, zero initial state.  Inputs rotate over several device copies so
+that the 256 MB last-level cache cannot serve a step from the previous one.
+
+Prints ONE JSON line.  Besides the throughput it reports:
+  roofline      the dominant kernel's algorithmic bytes per launch over its
+                average duration (HIP events recorded between the kernels on
+                the launch stream, inside the timed region), against 8 TB/s;
+  cpu_baseline  the fp64 oracle timed on the host cores on the same inputs;
+  kernels       both kernels' average durations and algorithmic bytes;
+  path          the whole step's algorithmic bytes per token against HBM;
+  extra         the packed 16-sequence chunk and the 64-sequence decode step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "KDA prefill tokens/s on 1 MI355X (8192-row packed chunk) + % MFMA/HBM roof"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_prefill_amd", "csrc", f)
+                  for f in ("kda_prefill.hip", "kda_device.h", "kda_decode.hip")]
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic bytes (what each kernel must move given its inputs and outputs)
+# ---------------------------------------------------------------------------
+
+def chunk_count(lengths):
+    return int(sum((int(L) + 63) // 64 for L in lengths))
+
+
+def record_bytes(dk, dv, es):
+    """Workspace record of one (chunk, head): w, Q e^Gam, K~^T, A_qk, u in the
+    io element size, plus e^{Gam_C} in fp32."""
+    return (64 * (3 * dk + dv) + 6 * 512) * es + dk * 4
+
+
+def intra_bytes(T, H, dk, dv, es, n_chunks):
+    reads = T * H * (2 * dk * es + dv * es + dk * 4 + 4)
+    writes = n_chunks * H * record_bytes(dk, dv, es)
+    return reads + writes
+
+
+def scan_bytes(T, H, dk, dv, es, n_chunks, n_live, state_in, state_out):
+    reads = n_chunks * H * record_bytes(dk, dv, es)
+    state = H * dk * dv * 4
+    reads += n_live * state if state_in else 0
+    writes = T * H * dv * es + (n_live * state if state_out else 0)
+    return reads + writes
+
+
+def path_bytes(T, H, dk, dv, es, n_live, state_in, state_out):
+    """The method's own traffic: q, k, v, g, beta in, o out, states in/out."""
+    state = H * dk * dv * 4
+    return (T * H * (2 * dk * es + dv * es + dk * 4 + 4 + dv * es)
+            + (n_live * state if state_in else 0) + (n_live * state if state_out else 0))
+
+
+def path_flops(lengths, H, dk, dv):
+    """Triangle-aware flops of the chunk form per (chunk, head), summed."""
+    total = 0
+    for L in lengths:
+        for c0 in range(0, int(L), 64):
+            C = min(64, int(L) - c0)
+            tri = C * (C + 1) // 2
+            f = 2 * tri * dk * 2                 # A_kk, A_qk
+            f += 2 * tri * (dk + dv)             # w, u (triangular Tm)
+            f += 2 * C * dk * dv * 2             # w S, Q~ S
+            f += 2 * tri * dv                    # A_qk U
+            f += 2 * C * dk * dv                 # K~^T U
+            f += C * C * C // 3                  # inverse (approx.)
+            total += f
+    return total * H
+
+
+# ---------------------------------------------------------------------------
+
+def to_dev(case, copies, torch):
+    dt = torch.bfloat16 if case.io_dtype == "bf16" else torch.float32
+    base = {
+        "q": torch.from_numpy(case.q).to("cuda").to(dt),
+        "k": torch.from_numpy(case.k).to("cuda").to(dt),
+        "v": torch.from_numpy(case.v).to("cuda").to(dt),
+        "g": torch.from_numpy(case.g).to("cuda"),
+        "beta": torch.from_numpy(case.beta).to("cuda"),
+    }
+    sets = [base] + [{k: t.clone() for k, t in base.items()} for _ in range(copies - 1)]
+    return sets, dt
+
+
+def time_prefill(case, steps, warmup, copies, torch, lap):
+    sets, dt = to_dev(case, copies, torch)
+    T, H, dk, dv = case.T, case.H, case.d_k, case.d_v
+    cu = torch.from_numpy(case.cu_seqlens).to("cuda")
+    slots = torch.from_numpy(case.slots).to("cuda") if case.slots is not None else None
+    if case.state_pool is not None:
+        pools = [torch.from_numpy(case.state_pool).to("cuda") for _ in range(copies)]
+        state_in = True
+    else:
+        pools = [torch.zeros((1, H, dv, dk), dtype=torch.float32, device="cuda")
+                 for _ in range(copies)]
+        state_in = False
+    outs = [torch.empty((T, H, dv), dtype=dt, device="cuda") for _ in range(copies)]
+    ws = torch.empty(max(lap.prefill_workspace_size(T, case.N, H, dk, dv, dt), 16),
+                     dtype=torch.uint8, device="cuda")
+
+    def call(i, events=None):
+        s = sets[i % copies]
+        p = pools[i % copies]
+        lap.chunk_prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], cu,
+                          state_in=p if state_in else None, state_out=p, o=outs[i % copies],
+                          slots=slots, scale=case.scale, workspace=ws, events=events)
+
+    for i in range(warmup):
+        call(i)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for trio in evs:          # torch creates the underlying hipEvents on first record
+        for e in trio:
+            e.record()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        call(i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    intra = [e[0].elapsed_time(e[1]) for e in evs]
+    scan = [e[1].elapsed_time(e[2]) for e in evs]
+    return {
+        "ms_per_step": total_ms / steps,
+        "intra_ms": float(np.mean(intra)), "scan_ms": float(np.mean(scan)),
+        "intra_ms_median": float(np.median(intra)), "scan_ms_median": float(np.median(scan)),
+        "state_in": state_in,
+    }
+
+
+def time_decode(case, steps, warmup, copies, torch, lap):
+    dt = torch.bfloat16 if case.io_dtype == "bf16" else torch.float32
+    q = torch.from_numpy(case.q).to("cuda").to(dt)
+    k = torch.from_numpy(case.k).to("cuda").to(dt)
+    v = torch.from_numpy(case.v).to("cuda").to(dt)
+    g = torch.from_numpy(case.g).to("cuda")
+    beta = torch.from_numpy(case.beta).to("cuda")
+    slots = torch.from_numpy(case.slots).to("cuda")
+    pools = [torch.from_numpy(case.state_pool).to("cuda") for _ in range(copies)]
+    o = torch.empty((case.N, case.H, case.d_v), dtype=dt, device="cuda")
+    for i in range(warmup):
+        lap.decode_step(q, k, v, g, beta, pools[i % copies], slots, o=o)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(steps):
+        lap.decode_step(q, k, v, g, beta, pools[i % copies], slots, o=o)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    state = case.H * case.d_k * case.d_v * 4
+    es = 2 if case.io_dtype == "bf16" else 4
+    nbytes = case.N * (2 * state + case.H * (2 * case.d_k * es + case.d_v * es + case.d_k * 4
+                                             + 4 + case.d_v * es))
+    return {"us": ms * 1e3, "bytes": nbytes, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def cpu_baseline(case, seconds):
+    """The fp64 oracle on the same inputs, repeated until `seconds` elapse
+    (a bounded sample; heads are subsampled if one call would take longer)."""
+    from oracle import oracle
+    threads = oracle.default_threads()
+    H = case.H
+    # probe one head to size the sample
+    t0 = time.perf_counter()
+    oracle.recurrence(case.q[:, :1], case.k[:, :1], case.v[:, :1], case.g[:, :1],
+                      case.beta[:, :1], case.cu_seqlens, threads=1)
+    per_head = time.perf_counter() - t0
+    est_call = per_head * H / threads
+    heads = H if est_call <= seconds else max(1, int(H * seconds / est_call))
+    sl = slice(0, heads)
+    args = (case.q[:, sl], case.k[:, sl], case.v[:, sl], case.g[:, sl], case.beta[:, sl])
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.recurrence(*args, case.cu_seqlens, threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    tok_s = case.T * reps * (heads / H) / el
+    return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%s: %d of %d heads, %d rows, %d repetition(s) in %.1f s (fp64 "
+                      "token-by-token recurrence in C; tokens/s scaled to all heads)"
+                      % (case.name, heads, H, case.T, reps, el),
+            "seconds": el}
+
+
+def stored_traffic(kernel_name, src_hash):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != src_hash:
+        return None
+    k = t.get("kernels", {}).get(kernel_name)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["single", "packed"], default="single")
+    ap.add_argument("--copies", type=int, default=3, help="rotated device copies of the inputs")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one elementwise copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        sys.stderr.write("bench.py measures one GPU only: the KDA path here is built and "
+                         "measured on a single MI355X (no multi-GPU sharding); run with --gpus 1.\n")
+        sys.exit(2)
+
+    import torch
+    import linear_attention_prefill_amd as lap
+    from linear_attention_prefill_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        sys.stderr.write("bench.py needs a GPU\n")
+        sys.exit(1)
+    lap.load_library()
+
+    t0 = time.time()
+    case = W.single_seq_prefill() if args.workload == "single" else W.packed_varlen_prefill()
+    log("generated %s in %.1f s" % (case.name, time.time() - t0))
+    lengths = np.diff(case.cu_seqlens).tolist()
+    T, H, dk, dv = case.T, case.H, case.d_k, case.d_v
+    es = 2 if case.io_dtype == "bf16" else 4
+    n_chunks = chunk_count(lengths)
+
+    r = time_prefill(case, args.steps, args.warmup, args.copies, torch, lap)
+    log("prefill %.1f us/step (intra %.1f us, scan %.1f us)"
+        % (r["ms_per_step"] * 1e3, r["intra_ms"] * 1e3, r["scan_ms"] * 1e3))
+    n_live = case.N
+    ib = intra_bytes(T, H, dk, dv, es, n_chunks)
+    sb = scan_bytes(T, H, dk, dv, es, n_chunks, n_live, r["state_in"], True)
+    pb = path_bytes(T, H, dk, dv, es, n_live, r["state_in"], True)
+    pf = path_flops(lengths, H, dk, dv)
+    kern = {
+        "kda_intra_kernel": {"us": r["intra_ms"] * 1e3, "us_median": r["intra_ms_median"] * 1e3,
+                             "bytes_per_launch": ib,
+                             "GB/s": ib / (r["intra_ms"] * 1e-3) / 1e9},
+        "kda_scan_kernel": {"us": r["scan_ms"] * 1e3, "us_median": r["scan_ms_median"] * 1e3,
+                            "bytes_per_launch": sb,
+                            "GB/s": sb / (r["scan_ms"] * 1e-3) / 1e9},
+    }
+    dom = max(kern, key=lambda n: kern[n]["us"])
+    achieved = kern[dom]["GB/s"]
+    src_hash = kernel_source_hash()
+    traffic = stored_traffic(dom, src_hash)
+    value = T / (r["ms_per_step"] * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": case.name, "total_rows": T, "num_seqs": case.N, "heads": H,
+                   "d_k": dk, "d_v": dv, "chunk": 64, "io_dtype": case.io_dtype,
+                   "state": "fp32", "initial_state": "pool" if r["state_in"] else "zero",
+                   "input_copies_rotated": args.copies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom},
+        "kernels": kern,
+        "path": {"bytes_per_step": pb, "GB/s": pb / (r["ms_per_step"] * 1e-3) / 1e9,
+                 "frac_hbm": pb / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "flops_per_step": pf,
+                 "frac_mfma_bf16": pf / (r["ms_per_step"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_extra:
+        extra = {}
+        if args.workload == "single":
+            pc = W.packed_varlen_prefill()
+            rp = time_prefill(pc, max(5, args.steps // 2), 2, args.copies, torch, lap)
+            extra["packed"] = {"workload": pc.name, "us": rp["ms_per_step"] * 1e3,
+                               "tokens/s": pc.T / (rp["ms_per_step"] * 1e-3),
+                               "intra_us": rp["intra_ms"] * 1e3, "scan_us": rp["scan_ms"] * 1e3}
+            log("packed %.1f us/step" % (rp["ms_per_step"] * 1e3))
+        dc = W.decode_case()
+        rd = time_decode(dc, max(10, args.steps), 3, 4, torch, lap)
+        rd["workload"] = dc.name
+        extra["decode"] = rd
+        log("decode %.1f us, %.0f GB/s" % (rd["us"], rd["GB/s"]))
+        out["extra"] = extra
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        torch.add(x, 1.0, out=y)
+        torch.cuda.synchronize()
+        out["calibration"] = {"kernel": "torch add (elementwise)", "read_bytes": 4 * n,
+                              "write_bytes": 4 * n}
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(case, args.cpu_seconds)
+        log("cpu baseline %.0f tokens/s on %d threads" % (cb["value"], cb["cores"]))
+        out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

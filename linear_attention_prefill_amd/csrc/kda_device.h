@@ -144,13 +144,17 @@ __device__ __forceinline__ SeqSpan seq_span(const int32_t *cu, int n, int T) {
     return s;
 }
 
+// Index of the lower-triangular fragment (row tile m, 32-row slab s <= m/2)
+// of a 64x64 lower-triangular matrix: 0, 1, (2, 3), (4, 5).
+__device__ __forceinline__ constexpr int tri_frag(int m, int s) { return m < 2 ? m : 2 * m - 2 + s; }
+
 // Workspace record layout: one record per (chunk id, head), all fragments in
 // the scan's lane order.  Offsets are in elements of type E except `dec`.
 template <typename E, int DK, int DV> struct WsLayout {
     static constexpr int kWElems = kChunk * DK;           // w:    4 x (DK/32) frags
     static constexpr int kQElems = kChunk * DK;           // q*exp(Gamma): same
     static constexpr int kKElems = DK * kChunk;           // K~^T: (DK/16) x 2 frags
-    static constexpr int kAElems = kChunk * kChunk;       // A_qk: 4 x 2 frags
+    static constexpr int kAElems = 6 * 512;               // A_qk: the 6 lower frags
     static constexpr int kUElems = kChunk * DV;           // u: (DV/16) tiles x 64 lanes x 16
     static constexpr int kRecElems = kWElems + kQElems + kKElems + kAElems + kUElems;
 };

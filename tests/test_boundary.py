@@ -57,7 +57,7 @@ def _desc(**kw):
 
 
 def _ws_formula(T, N, H, dk, dv, es):
-    rec = 64 * (3 * dk + 64 + dv) * es + dk * 4
+    rec = (64 * (3 * dk + dv) + 6 * 512) * es + dk * 4
     return (T // 64 + N) * H * rec
 
 

@@ -245,3 +245,13 @@ def test_decode_small_with_padding(dk, dv, io):
     c = W.random_case(30 + dk + dv, [1] * 9, H=3, d_k=dk, d_v=dv, io_dtype=io, num_slots=12,
                       slots=[4, -1, 0, 11, 7, 12, 2, 9, 5], scale=0.7)
     _check_decode(c, TOL[io])
+
+
+@pytest.mark.parametrize("mu_g,io", [(5.0, "bf16"), (5.0, "f32"), (2.0, "bf16"), (-4.0, "f32")])
+def test_decay_range_paths(mu_g, io):
+    """Fast decay pushes diagonal 16-row blocks onto the exact path (mu_g = 5:
+    about 100 log2 units of decay per block), mu_g = 2 mixes both paths
+    across channels and blocks, slow decay (mu_g = -4) keeps the state large."""
+    c = W.random_case(40 + int(mu_g), [150, 64, 37], H=3, d_k=128, d_v=128, io_dtype=io,
+                      mu_g=mu_g)
+    _check_case(c)
