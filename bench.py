@@ -242,7 +242,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["single", "packed"], default="single")
+    ap.add_argument("--workload", choices=["single", "packed", "decode"], default="single",
+                    help="single: 1 x 8192 rows (default); packed: 16 sequences in 8192 rows; "
+                         "decode: 64 sequences x 1 token (profiling the decode kernel)")
     ap.add_argument("--copies", type=int, default=3, help="rotated device copies of the inputs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -265,6 +267,21 @@ def main():
         sys.stderr.write("bench.py needs a GPU\n")
         sys.exit(1)
     lap.load_library()
+
+    if args.workload == "decode":
+        dc = W.decode_case()
+        rd = time_decode(dc, args.steps, args.warmup, 4, torch, lap)
+        out = {"metric": "KDA decode step: state read-modify-write bandwidth on 1 MI355X",
+               "value": rd["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+               "warmup": args.warmup, "ms_per_step": rd["us"] * 1e-3, "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+               "config": {"workload": dc.name, "num_seqs": dc.N, "heads": dc.H, "d_k": dc.d_k,
+                          "d_v": dc.d_v, "pools_rotated": 4},
+               "roofline": {"bound": "hbm", "achieved": rd["GB/s"], "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": rd["frac_hbm"], "traffic": None,
+                            "kernel": "kda_decode_kernel"}}
+        print(json.dumps(out), flush=True)
+        return
 
     t0 = time.time()
     case = W.single_seq_prefill() if args.workload == "single" else W.packed_varlen_prefill()

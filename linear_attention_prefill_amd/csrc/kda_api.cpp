@@ -32,6 +32,15 @@ hipError_t dispatch_decode(const kda::DecodeArgs &a, int dk, int dv, hipStream_t
     return kda::launch_decode<E, 128, 128>(a, s);
 }
 
+// Compute units of the current device (persistent grids are sized by it).
+int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        return 256;
+    return n;
+}
+
 // Shape checks shared by the workspace query and the call.
 kda_status_t check_desc(const kda_prefill_desc_t *d) {
     if (!d) return KDA_ERR_NULL;
@@ -83,6 +92,7 @@ kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v
     a.T = d.total_rows; a.N = d.num_seqs; a.H = d.num_heads; a.num_slots = d.num_slots;
     a.scale = d.scale;
     for (int i = 0; i < 3; ++i) a.events[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
+    a.num_cus = device_cus();
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = d.io_dtype == KDA_BF16 ? dispatch_prefill<bf16>(a, d.d_k, d.d_v, s)
                                                 : dispatch_prefill<float>(a, d.d_k, d.d_v, s);

@@ -73,6 +73,26 @@ __device__ __forceinline__ Frag<E> frag_from_tiles(const f32x4 &t0, const f32x4 
     return f;
 }
 
+// A fragment from two runs of four consecutive elements (e < 4 from p0,
+// e >= 4 from p1), e.g. two 8-byte LDS reads for bf16.
+template <typename E>
+__device__ __forceinline__ Frag<E> frag_from_runs(const E *p0, const E *p1);
+template <>
+__device__ __forceinline__ Frag<bf16> frag_from_runs<bf16>(const bf16 *p0, const bf16 *p1) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(p0);
+    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(p1);
+    Frag<bf16> f;
+    f.x = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> frag_from_runs<float>(const float *p0, const float *p1) {
+    Frag<float> f;
+    f.lo = *reinterpret_cast<const f32x4 *>(p0);
+    f.hi = *reinterpret_cast<const f32x4 *>(p1);
+    return f;
+}
+
 // Global fragment load/store: one fragment is 64 lanes x 8 elements,
 // contiguous per lane, so a wave moves 1 KiB (bf16) or 2 KiB (fp32) with
 // perfectly coalesced 16-byte accesses.

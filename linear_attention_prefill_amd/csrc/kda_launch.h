@@ -18,6 +18,7 @@ struct PrefillArgs {
     void *workspace;
     int T, N, H, num_slots;
     float scale;
+    int num_cus;            // compute units of the device (persistent grids)
     hipEvent_t events[3];   // optional: before intra, between, after scan
 };
 
