@@ -1,7 +1,7 @@
 // C ABI of libkda.so: host-side validation, workspace sizing and dispatch.
 // Nothing here touches device memory or synchronises; every error is
 // returned before the first launch.
-#include "../../include/kda.h"
+#include "kda.h"
 #include "kda_launch.h"
 
 #include <limits.h>

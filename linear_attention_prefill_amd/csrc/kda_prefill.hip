@@ -571,7 +571,8 @@ template <typename E, int DK> struct ScanStage {
     static constexpr int KS = DK / kSlab;
     static constexpr int TPW = DK / 64;
     Frag<E> wf[KS], qf[KS], af[2], kf[TPW][2];
-    f32x4 u, d[TPW];
+    typename Raw4<E>::type u;                  // raw: converted where it is used
+    f32x4 d[TPW];
 };
 
 template <typename E, int DK, int DV>
@@ -590,14 +591,35 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    // Keep the d_v slices of one (sequence, head) on one XCD: workgroups are
-    // dealt to the 8 XCDs round robin, so block b runs on XCD b % 8.
+    // Work order.  Sequences are taken longest first (for up to 64 sequences;
+    // every wave ranks them the same way), then head by head; (sequence,
+    // head) pairs are dealt round robin to the 8 XCDs (workgroups go to XCD
+    // b % 8), so each XCD gets an equal share of every sequence, while the
+    // d_v slices of one pair stay on one XCD and share its L2.
     const int B = gridDim.x, b = blockIdx.x;
-    const int lin = (B % 8 == 0) ? (b % 8) * (B / 8) + b / 8 : b;
-    const int jt = lin % VT;
-    const int h = (lin / VT) % H;
-    const int n = lin / (VT * H);
-    if (n >= N) return;
+    const int NP = N * H;
+    int q, jt;
+    if (NP % 8 == 0) {
+        const int k = b >> 3;
+        jt = k % VT;
+        q = (k / VT) * 8 + (b & 7);
+    } else {
+        jt = b % VT;
+        q = b / VT;
+    }
+    if (q >= NP || b >= B) return;
+    const int h = q % H;
+    int n = q / H;                                      // rank of the sequence
+    if (N <= 64) {
+        const int lane_len = lane < N ? seq_span(cu, lane, T).len : -1;
+        int rank = 0;
+        for (int m = 0; m < N; ++m) {
+            const int lm = __shfl(lane_len, m);
+            rank += (lm > lane_len || (lm == lane_len && m < lane)) ? 1 : 0;
+        }
+        const unsigned long long hit = __ballot(lane < N && rank == n);
+        n = hit ? __ffsll((long long)hit) - 1 : n;
+    }
     const int slot = slots ? slots[n] : n;
     if (slots && (slot < 0 || slot >= num_slots)) return;   // padded sequence
     const SeqSpan sp = seq_span(cu, n, T);
@@ -614,17 +636,41 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(
 #pragma unroll
         for (int i = 0; i < TPW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // Settle the state load here: otherwise the wait inserted for it at the
+    // top of the chunk loop would also drain every prefetched chunk.
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float x = S[i][r];
+            asm volatile("" : "+v"(x));
+            S[i][r] = x;
+        }
+    }
 
-    auto load_stage = [&](Stage &X, int cc) {
-        const size_t rec = (size_t)(sp.first_chunk + cc) * H + h;
-        const E *Rw = ws + rec * L::kRecElems;
-        const E *Rq = Rw + L::kWElems;
-        const E *Rk = Rq + L::kQElems;
-        const E *Ra = Rk + L::kKElems;
-        const E *Ru = Ra + L::kAElems;
+    // Record of chunk cc, by part; each part of a stage is refilled with the
+    // chunk three ahead as soon as its last use in the current step has been
+    // issued, so loads trickle out between the matrix-core products instead
+    // of queueing behind them in one burst.
+    auto rec_of = [&](int cc) { return (size_t)(sp.first_chunk + cc) * H + h; };
+    auto load_w = [&](Stage &X, int cc) {
+        const E *Rw = ws + rec_of(cc) * L::kRecElems;
 #pragma unroll
         for (int s = 0; s < KS; ++s) X.wf[s] = load_frag<E>(Rw + (wave * KS + s) * 512, lane);
-        X.u = load4<E>(Ru + jt * (64 * 16) + lane * 16 + 4 * wave);
+        const E *Ru = Rw + L::kWElems + L::kQElems + L::kKElems + L::kAElems;
+        X.u = *reinterpret_cast<const typename Raw4<E>::type *>(Ru + jt * (64 * 16) + lane * 16 + 4 * wave);
+    };
+    auto load_q = [&](Stage &X, int cc) {
+        const E *Rq = ws + rec_of(cc) * L::kRecElems + L::kWElems;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) X.qf[s] = load_frag<E>(Rq + (wave * KS + s) * 512, lane);
+    };
+    auto load_k = [&](Stage &X, int cc) {
+        const size_t rec = rec_of(cc);
+        const E *Rk = ws + rec * L::kRecElems + L::kWElems + L::kQElems;
+        const E *Ra = Rk + L::kKElems;
+        X.af[0] = load_frag<E>(Ra + tri_frag(wave, 0) * 512, lane);
+        X.af[1] = load_frag<E>(Ra + tri_frag(wave, 1) * 512, lane);   // unused by waves 0, 1
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int t = wave * TPW + i;
@@ -632,13 +678,20 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(
             X.kf[i][1] = load_frag<E>(Rk + (t * 2 + 1) * 512, lane);
             X.d[i] = *reinterpret_cast<const f32x4 *>(ws_dec + rec * DK + t * kSub + 4 * lg);
         }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) X.qf[s] = load_frag<E>(Rq + (wave * KS + s) * 512, lane);
-        X.af[0] = load_frag<E>(Ra + tri_frag(wave, 0) * 512, lane);
-        if (wave >= 2) X.af[1] = load_frag<E>(Ra + tri_frag(wave, 1) * 512, lane);
+    };
+    auto load_stage = [&](Stage &X, int cc) {
+        load_w(X, cc);
+        load_k(X, cc);
+        load_q(X, cc);
     };
 
-    auto step = [&](const Stage &X, int cc) {
+    const int nch = (sp.len + kChunk - 1) / kChunk;
+    // Refills are unconditional (clamped to the last chunk) inside the main
+    // loop: a conditional load would leave a stage register holding either
+    // the old or the new value, and the copy that merges them waits for
+    // every load in flight.
+    auto step = [&](Stage &X, int cc, bool refill) {
+        const int nx = cc + 3 < nch ? cc + 3 : nch - 1;
         // publish my state tiles (rounded to E) and read every slab
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
@@ -656,7 +709,8 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(
             mma(a0, X.wf[s], Sb[s]);
             mma(a1, X.wf[s + 1], Sb[s + 1]);
         }
-        const f32x4 un = X.u - (a0 + a1);
+        const f32x4 un = to_f32<E>(X.u) - (a0 + a1);
+        if (refill) load_w(X, nx);
         store4<E>(sUb + ((wave >> 1) * 64 + lane) * 8 + (wave & 1) * 4, un);
         // Q~ S part of the output does not need U: issue it before the barrier
         f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
@@ -665,6 +719,7 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(
             mma(o0, Sb[s], X.qf[s]);
             mma(o1, Sb[s + 1], X.qf[s + 1]);
         }
+        if (refill) load_q(X, nx);
 #pragma unroll
         for (int i = 0; i < TPW; ++i) S[i] *= X.d[i];
         __syncthreads();
@@ -681,28 +736,26 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(
             mma(S[i], X.kf[i][0], ub[0]);
             mma(S[i], X.kf[i][1], ub[1]);
         }
+        if (refill) load_k(X, nx);
         const int row = wave * kSub + li;
         if (row < sp.len - cc * kChunk)
             store4<E>(o + ((size_t)(sp.start + cc * kChunk + row) * H + h) * DV + j0 + 4 * lg,
                       (o0 + o1) * scale);
     };
 
-    const int nch = (sp.len + kChunk - 1) / kChunk;
-    Stage A, Bs, Cs;
-    if (nch > 0) load_stage(A, 0);
-    if (nch > 1) load_stage(Bs, 1);
-    if (nch > 2) load_stage(Cs, 2);
-    for (int cc = 0; cc < nch; cc += 3) {
-        step(A, cc);
-        if (cc + 3 < nch) load_stage(A, cc + 3);
-        if (cc + 1 < nch) {
-            step(Bs, cc + 1);
-            if (cc + 4 < nch) load_stage(Bs, cc + 4);
+    if (nch > 0) {
+        Stage A, Bs, Cs;
+        load_stage(A, 0);
+        load_stage(Bs, nch > 1 ? 1 : 0);
+        load_stage(Cs, nch > 2 ? 2 : nch - 1);
+        int cc = 0;
+        for (; cc + 2 < nch; cc += 3) {
+            step(A, cc, true);
+            step(Bs, cc + 1, true);
+            step(Cs, cc + 2, true);
         }
-        if (cc + 2 < nch) {
-            step(Cs, cc + 2);
-            if (cc + 5 < nch) load_stage(Cs, cc + 5);
-        }
+        if (cc < nch) step(A, cc, false);
+        if (cc + 1 < nch) step(Bs, cc + 1, false);
     }
 
     if (state_out) {
