@@ -93,6 +93,37 @@ __device__ __forceinline__ Frag<float> frag_from_runs<float>(const float *p0, co
     return f;
 }
 
+// B-operand fragment of a row-major LDS tile M (pitch P elements): lane
+// (i, g) receives M[k0 + kk(g, e)][n0 + i], i.e. column n0 + i with the
+// contraction running down the rows.  For bf16 this is two transposing LDS
+// reads (ds_read_b64_tr_b16).  Within each group of 16 lanes that read hands
+// lane l element (l & 3) of the 8-byte runs addressed by lanes (l >> 2) + 4j,
+// j = 0..3; so lane m of group g addresses row k0 + 4g + (m >> 2), columns
+// n0 + 4 (m & 3) .. + 3, and a second read 16 rows further down supplies
+// elements 4..7.  Rows of M must be 8-byte aligned (P, n0 multiples of 4).
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+template <typename E>
+__device__ __forceinline__ Frag<E> frag_cols(const E *M, int P, int k0, int n0, int lane);
+template <>
+__device__ __forceinline__ Frag<bf16> frag_cols<bf16>(const bf16 *M, int P, int k0, int n0, int lane) {
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const int m = lane & 15, g = lane >> 4;
+    bf16 *p = const_cast<bf16 *>(M) + (k0 + 4 * g + (m >> 2)) * P + n0 + 4 * (m & 3);
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)p);
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p + 16 * P));
+    Frag<bf16> f;
+    f.x = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    return f;
+}
+template <>
+__device__ __forceinline__ Frag<float> frag_cols<float>(const float *M, int P, int k0, int n0, int lane) {
+    const int i = lane & 15, g = lane >> 4;
+    Frag<float> f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.set(e, M[(k0 + kk_of(g, e)) * P + n0 + i]);
+    return f;
+}
+
 // Global fragment load/store: one fragment is 64 lanes x 8 elements,
 // contiguous per lane, so a wave moves 1 KiB (bf16) or 2 KiB (fp32) with
 // perfectly coalesced 16-byte accesses.

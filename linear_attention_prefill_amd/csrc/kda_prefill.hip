@@ -26,13 +26,19 @@
 // K e^{Gam_C - Gam} = k Qf e^{Gam_C - Gam_e}.  Two exps per element replace
 // one exp per element per use.
 //
-// kda_intra_kernel: one workgroup (4 waves) per (chunk, head), fully
-// parallel, two workgroups per CU for bf16.  kda_scan_kernel: one workgroup
-// of 4 waves per (sequence, head, 16-column slice of d_v); the d_v columns of
-// S evolve independently, so slices need no exchange.  Wave w owns chunk rows
-// 16w..16w+15 and a quarter of the key channels, swaps the rounded copies of
-// its S and U tiles with the other waves through LDS, and keeps the operands
-// of the next two chunks in flight in registers.
+// kda_intra_kernel: a persistent grid of one 8-wave workgroup per CU (two
+// waves per SIMD) walks the (chunk, head) items; the next item's raw inputs
+// are fetched into registers a part per phase while the current one is
+// computed.  Per item: row factors (lanes hold four consecutive rows, DPP row
+// scans give the block prefixes), A blocks and the four diagonal inverses in
+// parallel, the off-diagonal inverse blocks in two levels on fp32 matrix
+// cores, then w and u; workspace fragments are written in the scan's order.
+// kda_scan_kernel: one workgroup of 4 waves per (sequence, head, 16-column
+// slice of d_v); the d_v columns of S evolve independently, so slices need no
+// exchange.  Wave w owns chunk rows 16w..16w+15 and a quarter of the key
+// channels, swaps the rounded copies of its S and U tiles with the other
+// waves through LDS, and keeps the operands of the next chunks in flight in
+// registers.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -45,19 +51,25 @@ namespace kda {
 // Decay span (log2 units) of a 16-row block above which its diagonal block is
 // computed exactly instead of with split factors.
 constexpr float kDiagSpanLimit = 64.f;
+constexpr int kIntraThreads = 512;     // 8 waves: two per SIMD
+constexpr int kCuCache = 256;          // sequence bounds kept in LDS when N < this
 
+// LDS of the intra-chunk kernel.  For bf16, K e^Gam, Q e^Gam and V are staged
+// as row-major tiles and read back as fragments; for fp32 (twice the bytes)
+// K e^Gam and Q e^Gam are rebuilt from k P, q P and e^{Gam_s}, and V is read
+// from global memory in fragment order.
 template <typename E, int DK, int DV> struct IntraLds {
-    static constexpr int PAD = sizeof(E) == 2 ? 8 : 4;
-    static constexpr int KPP = DK + PAD;             // pitch of k P, q P (E)
-    static constexpr int KQP = DK + 4;               // pitch of k Qf (fp32)
-    static constexpr int VP = DV + PAD;              // pitch of V (E)
-    static constexpr int AP = 68;                    // pitch of A_kk / Tm (fp32)
-    static constexpr int AQP = sizeof(E) == 2 ? 72 : 68;   // pitch of A_qk (E)
-    static constexpr int max_(int a, int b) { return a > b ? a : b; }
-    // byte sizes of the three regions and their later tenants
-    static constexpr int R1 = max_(kChunk * KPP * (int)sizeof(E), kChunk * AQP * (int)sizeof(E));
-    static constexpr int R2 = max_(kChunk * KPP * (int)sizeof(E), kChunk * AP * 4);
-    static constexpr int R3 = max_(kChunk * KQP * 4, kChunk * VP * (int)sizeof(E));
+    static constexpr bool kStage = sizeof(E) == 2;  // K e^Gam and V staged in LDS
+    static constexpr int PAD = sizeof(E) == 2 ? 8 : 0;
+    static constexpr int KPP = DK + PAD;            // pitch of k P, q P, K e^Gam (E)
+    static constexpr int KQP = DK + 4;              // pitch of k Qf (fp32)
+    static constexpr int VP = DV + PAD;             // pitch of V (E)
+    static constexpr int AP = 68;                   // pitch of A_kk -> Tm (fp32)
+    static constexpr int T2P = 36;                  // pitch of Tm[32:64, 0:32] (fp32)
+    static constexpr int DP = 16;                   // pitch of the diagonal A_kk blocks (fp32)
+    static constexpr int T2D_BYTES = 32 * T2P * 4 > 4 * kSub * DP * 4 ? 32 * T2P * 4 : 4 * kSub * DP * 4;
+    static constexpr int X_ELEMS = kStage ? kChunk * KPP : 8;   // also the size of Q e^Gam
+    static constexpr int V_ELEMS = kStage ? kChunk * VP : 8;
 };
 
 // Raw inputs of one chunk held by one thread (prefetched for the next chunk).
@@ -69,32 +81,44 @@ template <typename E> __device__ __forceinline__ f32x4 to_f32(const bf16x4 &x) {
 }
 template <typename E> __device__ __forceinline__ f32x4 to_f32(const f32x4 &x) { return x; }
 
+// Completes the load that produced x at this point of the program (an empty
+// asm statement that consumes and redefines every 32-bit word of x).
+template <typename T> __device__ __forceinline__ void settle(T &x) {
+    static_assert(sizeof(T) % 4 == 0, "settle");
+    uint32_t w[sizeof(T) / 4];
+    __builtin_memcpy(w, &x, sizeof(T));
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" : "+v"(w[i]));
+    __builtin_memcpy(&x, w, sizeof(T));
+}
+
+// Cross-lane moves inside a DPP row (16 lanes): row_shr:N brings lane i - N
+// (0 below the row's first lane), row_newbcast:L brings lane L of the row.
+template <int CTRL> __device__ __forceinline__ float dpp_row(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+// Inclusive prefix sum over the 16 lanes of each row.
+__device__ __forceinline__ float row_scan(float x) {
+    x += dpp_row<0x111>(x);
+    x += dpp_row<0x112>(x);
+    x += dpp_row<0x114>(x);
+    x += dpp_row<0x118>(x);
+    return x;
+}
+template <int L> __device__ __forceinline__ float row_bcast(float x) { return dpp_row<0x150 + L>(x); }
+// Lane L of each quad of lanes, to the whole quad (quad_perm [L, L, L, L]).
+template <int L> __device__ __forceinline__ float quad_bcast(float x) { return dpp_row<L * 0x55>(x); }
+
 // A chunk of one head: item = cid * H + h; valid when item >= 0.
 struct ChunkRef {
     int item, cid, h, row0, C;
 };
 
-// First chunk at or after `item` in steps of `stride` that belongs to a
-// sequence (ids between sequences' chunk ranges are skipped).
-__device__ __forceinline__ ChunkRef find_chunk(int item, int stride, int n_items,
-                                               const int32_t *cu, int T, int N, int H) {
-    for (; item < n_items; item += stride) {
-        const int cid = item / H;
-        int lo = 0, hi = N - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (clamp_row(cu[mid], T) / kChunk + mid <= cid) lo = mid; else hi = mid - 1;
-        }
-        const SeqSpan sp = seq_span(cu, lo, T);
-        const int jc = cid - sp.first_chunk;
-        if (jc >= 0 && jc * kChunk < sp.len)
-            return ChunkRef{item, cid, item - cid * H, sp.start + jc * kChunk, min(kChunk, sp.len - jc * kChunk)};
-    }
-    return ChunkRef{-1, 0, 0, 0, 0};
-}
+// Index p = I (I + 1) / 2 + J of the block pair (I, J), J <= I < 4.
+__device__ __forceinline__ int pair_row(int p) { return p < 1 ? 0 : (p < 3 ? 1 : (p < 6 ? 2 : 3)); }
 
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256, 1) void kda_intra_kernel(
+__global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu, int T, int N, int H,
@@ -104,75 +128,128 @@ __global__ __launch_bounds__(256, 1) void kda_intra_kernel(
     using LD = IntraLds<E, DK, DV>;
     using L = WsLayout<E, DK, DV>;
     using R4 = typename Raw4<E>::type;
-    constexpr int NTH = 256;
-    constexpr int KPP = LD::KPP, KQP = LD::KQP, VP = LD::VP, AP = LD::AP, AQP = LD::AQP;
+    constexpr int NTH = kIntraThreads;
+    constexpr int KPP = LD::KPP, KQP = LD::KQP, VP = LD::VP, AP = LD::AP, T2P = LD::T2P, DP = LD::DP;
     constexpr int KS = DK / kSlab;                     // d_k slabs
-    constexpr int KT = DK / kSub;                      // d_k tiles
     constexpr int VT = DV / kSub;                      // d_v tiles
     constexpr int C4 = DK / 4;                         // 4-channel columns
-    constexpr int RG = NTH / C4;                       // row groups (prefix sum)
-    constexpr int RPG = kChunk / RG;                   // rows per group
-    constexpr int BPG = kSub / RPG;                    // groups per 16-row block
+    constexpr int FW = C4 / 4;                         // waves of the factor phase
+    constexpr int KT = DK / kSub;                      // d_k tiles
     constexpr int EPU = 16 / sizeof(E);
-    constexpr int VPT = kChunk * DV / EPU / NTH;
+    constexpr int VPT = LD::kStage ? kChunk * DV / EPU / NTH : 1;
+    constexpr int MPW = KS / 2;                        // w row tiles per wave
+    static_assert(FW <= NTH / 64 && VT <= 8, "thread mapping");
 
-    __shared__ __align__(16) char sR1[LD::R1];         // k P;  later A_qk
-    __shared__ __align__(16) char sR2[LD::R2];         // q P (and prefix totals); later A_kk -> Tm
-    __shared__ __align__(16) char sR3[LD::R3];         // k Qf (fp32); later V
+    __shared__ __align__(16) E sKP[kChunk * KPP];      // k P
+    __shared__ __align__(16) E sQP[kChunk * KPP];      // q P
+    __shared__ __align__(16) E sX[LD::X_ELEMS];        // K e^Gam
+    __shared__ __align__(16) E sQh[LD::X_ELEMS];       // Q e^Gam
+    __shared__ __align__(16) E sV[LD::V_ELEMS];        // V
+    __shared__ __align__(16) float sKQ[kChunk * KQP];  // k Qf (fp32)
+    __shared__ __align__(16) float sA[kChunk * AP];    // A_kk -> Tm
+    __shared__ __align__(16) char sT2D[LD::T2D_BYTES];  // diagonal A_kk blocks; later Tm[32:64, 0:32]
+    __shared__ __align__(16) float sBs[4 * DK];        // e^{Gam} at each block's first row
+    __shared__ __align__(16) float sCe[4 * DK];        // e^{Gam_C - Gam} at each block's last row
     __shared__ __align__(16) float sF[10 * DK];        // F_IJ, J <= I, index I(I+1)/2 + J
-    __shared__ __align__(16) float sBs[4 * DK];        // e^{Gam_16I}
-    __shared__ __align__(16) float sCe[4 * DK];        // e^{Gam_C - Gam_16I+15}
-    __shared__ float sBeta[kChunk];
-    __shared__ int sExact[4];
-    E *const sKP = reinterpret_cast<E *>(sR1);
-    E *const sQP = reinterpret_cast<E *>(sR2);
-    float *const sKQ = reinterpret_cast<float *>(sR3);
-    float *const sTot = reinterpret_cast<float *>(sR2);   // [RG][DK] totals, then [4][DK] firsts
-    E *const sAqk = reinterpret_cast<E *>(sR1);
-    float *const sA = reinterpret_cast<float *>(sR2);
-    E *const sV = reinterpret_cast<E *>(sR3);
+    __shared__ __align__(16) float sBeta[kChunk];
+    __shared__ int sExact[4 * C4];                     // per block and 4-channel column
+    __shared__ int sCu[kCuCache];
 
+    float *const sT2 = reinterpret_cast<float *>(sT2D);
+    float *const sD = reinterpret_cast<float *>(sT2D);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    // thread (c4, rg): channels 4 c4 .. 4 c4 + 3 of rows RPG rg .. RPG rg + RPG - 1
-    const int c4 = tid % C4, rg = tid / C4, ch0 = 4 * c4;
+    // factor phase: lane (r, c) of wave w < FW (r = lane % 16, c = lane / 16)
+    // owns channels 4 cq .. + 3, cq = 4 w + c, of rows 4 r .. 4 r + 3: a DPP
+    // row of 16 lanes spans the chunk and a quad of lanes one 16-row block.
+    const int r4 = lane & 15, cq = 4 * wave + lg, ch0 = 4 * cq;
+    const bool fthread = wave < FW;
     const int n_items = (T / kChunk + N) * H;
     const int stride = gridDim.x;
 
+    // Sequence bounds: up to 64 in one register (lane i holds cu[i], read
+    // back with readlane), else up to kCuCache in LDS, else scalar loads.
+    const bool cu_reg = N < 64, cu_lds = N < kCuCache;
+    const int cu_v = (cu_reg && lane <= N) ? cu[lane] : 0;
+    if (!cu_reg && cu_lds)
+        for (int i = tid; i <= N; i += NTH) sCu[i] = cu[i];
+    __syncthreads();
+    // (scalar loads for the uncached case: no vector-memory wait in the loop)
+    const int32_t __attribute__((address_space(4))) *cu_s =
+        (const int32_t __attribute__((address_space(4))) *)cu;
+    auto cu_at = [&](int i) {
+        if (cu_reg) return __builtin_amdgcn_readlane(cu_v, i);
+        return __builtin_amdgcn_readfirstlane(cu_lds ? sCu[i] : cu_s[i]);
+    };
+    // First chunk at or after `item` in steps of the grid that belongs to a
+    // sequence (ids between sequences' chunk ranges are skipped).
+    auto find_chunk = [&](int item) -> ChunkRef {
+        for (; item < n_items; item += stride) {
+            const int cid = item / H;
+            int lo = 0, hi = N - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (clamp_row(cu_at(mid), T) / kChunk + mid <= cid) lo = mid; else hi = mid - 1;
+            }
+            const int start = clamp_row(cu_at(lo), T), end = clamp_row(cu_at(lo + 1), T);
+            const int len = end > start ? end - start : 0;
+            const int jc = cid - (start / kChunk + lo);
+            if (jc >= 0 && jc * kChunk < len)
+                return ChunkRef{item, cid, item - cid * H, start + jc * kChunk, min(kChunk, len - jc * kChunk)};
+        }
+        return ChunkRef{-1, 0, 0, 0, 0};
+    };
+
     // registers holding the next chunk's raw inputs
-    R4 kr[RPG], qr[RPG];
-    f32x4 gr[RPG];
+    R4 kr[4], qr[4];
+    f32x4 gr[4];
     uint4 xv[VPT];
     float bt = 0.f;
-    auto load_kqg = [&](const ChunkRef &ck) {
-#pragma unroll
-        for (int r = 0; r < RPG; ++r) {
-            const int row = rg * RPG + r;
-            kr[r] = qr[r] = R4{};
-            gr[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (ck.item >= 0 && row < ck.C) {
-                const size_t off = ((size_t)(ck.row0 + row) * H + ck.h) * DK + ch0;
-                kr[r] = *reinterpret_cast<const R4 *>(k + off);
-                qr[r] = *reinterpret_cast<const R4 *>(q + off);
-                gr[r] = *reinterpret_cast<const f32x4 *>(g + off);
-            }
+    // k, q, g of row 4 r4 + r (one of this lane's four rows)
+    auto load_row = [&](const ChunkRef &ck, int r) {
+        const int row = 4 * r4 + r;
+        kr[r] = qr[r] = R4{};
+        gr[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (fthread && ck.item >= 0 && row < ck.C) {
+            const size_t off = ((size_t)(ck.row0 + row) * H + ck.h) * DK + ch0;
+            kr[r] = *reinterpret_cast<const R4 *>(k + off);
+            qr[r] = *reinterpret_cast<const R4 *>(q + off);
+            gr[r] = *reinterpret_cast<const f32x4 *>(g + off);
         }
+    };
+    auto load_beta = [&](const ChunkRef &ck) {
         bt = (ck.item >= 0 && tid < ck.C) ? beta[(size_t)(ck.row0 + tid) * H + ck.h] : 0.f;
     };
     auto load_v = [&](const ChunkRef &ck) {
+        if constexpr (LD::kStage) {
 #pragma unroll
-        for (int p = 0; p < VPT; ++p) {
-            const int u = tid + p * NTH;
-            const int r = u / (DV / EPU), c = (u % (DV / EPU)) * EPU;
-            xv[p] = uint4{0, 0, 0, 0};
-            if (ck.item >= 0 && r < ck.C)
-                xv[p] = *reinterpret_cast<const uint4 *>(v + ((size_t)(ck.row0 + r) * H + ck.h) * DV + c);
+            for (int p = 0; p < VPT; ++p) {
+                const int u = tid + p * NTH;
+                const int r = u / (DV / EPU), c = (u % (DV / EPU)) * EPU;
+                xv[p] = uint4{0, 0, 0, 0};
+                if (ck.item >= 0 && r < ck.C)
+                    xv[p] = *reinterpret_cast<const uint4 *>(v + ((size_t)(ck.row0 + r) * H + ck.h) * DV + c);
+            }
         }
     };
 
-    ChunkRef cur = find_chunk(blockIdx.x, stride, n_items, cu, T, N, H);
-    load_kqg(cur);
+    ChunkRef cur = find_chunk(blockIdx.x);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) load_row(cur, r);
+    load_beta(cur);
     load_v(cur);
+    // Settle the first chunk's loads here, so that the loop's own prefetches
+    // are the only loads in flight at its top.
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        settle(kr[r]);
+        settle(qr[r]);
+        settle(gr[r]);
+    }
+#pragma unroll
+    for (int p = 0; p < VPT; ++p) settle(xv[p]);
+    settle(bt);
+
     while (cur.item >= 0) {
         const int C = cur.C;
         const size_t rec = (size_t)cur.item;           // = cid * H + h
@@ -181,134 +258,100 @@ __global__ __launch_bounds__(256, 1) void kda_intra_kernel(
         E *const Rk = Rq + L::kQElems;
         E *const Ra = Rk + L::kKElems;
         E *const Ru = Ra + L::kAElems;
-        const ChunkRef nxt = find_chunk(cur.item + stride, stride, n_items, cu, T, N, H);
+        const ChunkRef nxt = find_chunk(cur.item + stride);
 
-        // ---- prefix sums of g (log2 units): group totals and block-first values ----
-        f32x4 gl[RPG];
-#pragma unroll
-        for (int r = 0; r < RPG; ++r) gl[r] = gr[r] * kLog2e;
-#pragma unroll
-        for (int r = 1; r < RPG; ++r) gl[r] += gl[r - 1];
-        *reinterpret_cast<f32x4 *>(sTot + rg * DK + ch0) = gl[RPG - 1];
-        if (rg % BPG == 0) *reinterpret_cast<f32x4 *>(sTot + RG * DK + (rg / BPG) * DK + ch0) = gl[0];
+        // ---- per-row factors (log2 units); everything derived from k, q, V
+        // leaves the registers ----
         if (tid < kChunk) sBeta[tid] = bt;
-        if (tid < 4) sExact[tid] = 0;
-        __syncthreads();
-
-        // ---- per-row factors (registers), per-block factors (threads c < DK) ----
-        const int blk = rg / BPG;
-        f32x4 pre = {0.f, 0.f, 0.f, 0.f}, btot = pre, before = pre;
-        for (int p = 0; p < blk * BPG; ++p) before += *reinterpret_cast<const f32x4 *>(sTot + p * DK + ch0);
+        if (fthread) {
+            // gl: inclusive prefix of g over this lane's 4 rows; ex: the sum over
+            // the lanes before it (exclusive row scan); Gs, Ge: Gam at the
+            // block's first and last rows; total: Gam at the chunk's last row.
+            f32x4 gl[4];
 #pragma unroll
-        for (int p = 0; p < BPG; ++p) {
-            const f32x4 t = *reinterpret_cast<const f32x4 *>(sTot + (blk * BPG + p) * DK + ch0);
-            btot += t;
-            if (p < rg % BPG) pre += t;
-        }
-        const f32x4 gs = *reinterpret_cast<const f32x4 *>(sTot + RG * DK + blk * DK + ch0);
-        f32x4 ebs;                                     // e^{Gam} at the block's first row
+            for (int r = 0; r < 4; ++r) gl[r] = gr[r] * kLog2e;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) ebs[x] = fast_exp2(before[x] + gs[x]);
-        // k P and k Qf go to LDS at once (their regions hold nothing live);
-        // Q e^Gam goes straight to the workspace in the scan's fragment order;
-        // q P waits for the barrier, since its region holds the prefix totals.
-        R4 qpk[RPG];
-#pragma unroll
-        for (int r = 0; r < RPG; ++r) {
-            const int row = rg * RPG + r;
-            const f32x4 bp = pre + gl[r];              // block-local inclusive prefix
-            const f32x4 kf = to_f32<E>(kr[r]), qf = to_f32<E>(qr[r]);
-            f32x4 kp, qp, kq, qh;
+            for (int r = 1; r < 4; ++r) gl[r] += gl[r - 1];
+            f32x4 ex, Gs, Ge, total;
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                const float P = fast_exp2(bp[x] - gs[x]);
-                const float Qf = fast_exp2(btot[x] - bp[x]);
-                kp[x] = kf[x] * P;
-                qp[x] = qf[x] * P;
-                kq[x] = kf[x] * Qf;
-                qh[x] = qp[x] * ebs[x];
+                const float inc = row_scan(gl[3][x]);
+                ex[x] = inc - gl[3][x];
+                Gs[x] = quad_bcast<0>(ex[x] + gl[0][x]);
+                Ge[x] = quad_bcast<3>(inc);
+                total[x] = row_bcast<15>(inc);
             }
-            store4<E>(sKP + row * KPP + ch0, kp);
-            *reinterpret_cast<f32x4 *>(sKQ + row * KQP + ch0) = kq;
-            // fragment (m, s) = (row / 16, ch0 / 32); lane (row % 16) + 16 g with
-            // g = (ch0 % 16) / 4; half (ch0 % 32) / 16 selects elements 4..7
-            const int m = row >> 4, s = ch0 >> 5;
-            const int fl = (row & 15) + 16 * ((ch0 & 15) >> 2);
-            store4<E>(Rq + (m * KS + s) * 512 + fl * 8 + 4 * ((ch0 & 31) >> 4), qh);
-            store4<E>(reinterpret_cast<E *>(&qpk[r]), qp);
-        }
-        float fF[10], fBs[4], fCe[4], fdec = 0.f;
-        bool exact[4] = {false, false, false, false};
-        if (tid < DK) {
-            const int c = tid;
-            float Gs[4], Ge[4], run = 0.f;
+            const int I = r4 >> 2;
+            f32x4 ebs, ce;                             // e^{Gam_s}, e^{Gam_C - Gam_e} of the block
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                float bt2 = 0.f;
+            for (int x = 0; x < 4; ++x) {
+                ebs[x] = fast_exp2(Gs[x]);
+                ce[x] = fast_exp2(total[x] - Ge[x]);
+            }
+            if ((r4 & 3) == 0) {
+                *reinterpret_cast<f32x4 *>(sBs + I * DK + ch0) = ebs;
+                *reinterpret_cast<f32x4 *>(sCe + I * DK + ch0) = ce;
+                bool exd = false;
 #pragma unroll
-                for (int p = 0; p < BPG; ++p) bt2 += sTot[(I * BPG + p) * DK + c];
-                Gs[I] = run + sTot[RG * DK + I * DK + c];
-                Ge[I] = run + bt2;
-                run = Ge[I];
+                for (int x = 0; x < 4; ++x) exd |= (Gs[x] - Ge[x]) > kDiagSpanLimit;
+                sExact[I * C4 + cq] = exd ? 1 : 0;
             }
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * r4 + r;
+                const f32x4 gam = ex + gl[r];
+                const f32x4 kf = to_f32<E>(kr[r]), qf = to_f32<E>(qr[r]);
+                f32x4 kp, qp, kq, qh, xh;
 #pragma unroll
-                for (int J = 0; J <= I; ++J) fF[I * (I + 1) / 2 + J] = fast_exp2(Gs[I] - Ge[J]);
-                fBs[I] = fast_exp2(Gs[I]);
-                fCe[I] = fast_exp2(Ge[3] - Ge[I]);
-                exact[I] = (Gs[I] - Ge[I]) > kDiagSpanLimit;
-            }
-            fdec = fast_exp2(Ge[3]);
-        }
-        __syncthreads();   // prefix totals are no longer read; their region takes q P
-
-#pragma unroll
-        for (int r = 0; r < RPG; ++r)
-            *reinterpret_cast<R4 *>(sQP + (rg * RPG + r) * KPP + ch0) = qpk[r];
-        if (tid < DK) {
-#pragma unroll
-            for (int i = 0; i < 10; ++i) sF[i * DK + tid] = fF[i];
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                sBs[I * DK + tid] = fBs[I];
-                sCe[I * DK + tid] = fCe[I];
-                if (exact[I]) sExact[I] = 1;
-            }
-            ws_dec[rec * DK + tid] = fdec;
-        }
-        // the raw k, q, g registers are free: fetch the next chunk's
-        load_kqg(nxt);
-        __syncthreads();
-
-        // ---- K~^T fragments: (t, s) holds key channels 16t.. over chunk rows 32s.. ----
-        for (int f = wave; f < KT * 2; f += 4) {
-            const int t = f >> 1, s = f & 1;
-            const int ch = t * kSub + li;
-            Frag<E> fr;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int row = s * kSlab + kk_of(lg, e);
-                fr.set(e, sKQ[row * KQP + ch] * sCe[(row >> 4) * DK + ch]);
-            }
-            store_frag<E>(Rk + (t * 2 + s) * 512, lane, fr);
-        }
-        // ---- X = diag(beta) K e^Gam for w, kept in registers (wave w: d_k slab w) ----
-        Frag<E> xf[2][2];
-        if (wave < KS) {
-#pragma unroll
-            for (int nn = 0; nn < 2; ++nn) {
-                const int ch = (2 * wave + nn) * kSub + li;
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int row = s * kSlab + kk_of(lg, e);
-                        xf[nn][s].set(e, sBeta[row] * (float)sKP[row * KPP + ch] * sBs[(row >> 4) * DK + ch]);
-                    }
+                for (int x = 0; x < 4; ++x) {
+                    const float P = fast_exp2(gam[x] - Gs[x]);
+                    const float Qf = fast_exp2(Ge[x] - gam[x]);
+                    kp[x] = kf[x] * P;
+                    qp[x] = qf[x] * P;
+                    kq[x] = kf[x] * Qf;
+                    qh[x] = qp[x] * ebs[x];
+                    xh[x] = kp[x] * ebs[x];
                 }
+                store4<E>(sKP + row * KPP + ch0, kp);
+                store4<E>(sQP + row * KPP + ch0, qp);
+                if constexpr (LD::kStage) {
+                    store4<E>(sX + row * KPP + ch0, xh);
+                    store4<E>(sQh + row * KPP + ch0, qh);
+                }
+                *reinterpret_cast<f32x4 *>(sKQ + row * KQP + ch0) = kq;
+            }
+            // F_IJ = e^{Gam_s(I) - Gam_e(J)}, pair I (I + 1) / 2 + J = r, on lanes r < 10
+            {
+                const int p = r4 < 10 ? r4 : 0;
+                const int pI = pair_row(p), pJ = p - pI * (pI + 1) / 2;
+                f32x4 F;
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    F[x] = fast_exp2(__shfl(Gs[x], (lane & 48) + 4 * pI) - __shfl(Ge[x], (lane & 48) + 4 * pJ));
+                if (r4 < 10) *reinterpret_cast<f32x4 *>(sF + r4 * DK + ch0) = F;
+            }
+            if (r4 == 15) {
+                f32x4 d;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) d[x] = fast_exp2(total[x]);
+                *reinterpret_cast<f32x4 *>(ws_dec + rec * DK + ch0) = d;
             }
         }
+        if constexpr (LD::kStage) {
+#pragma unroll
+            for (int p = 0; p < VPT; ++p) {
+                const int u = tid + p * NTH;
+                const int r = u / (DV / EPU), c = (u % (DV / EPU)) * EPU;
+                *reinterpret_cast<uint4 *>(sV + r * VP + c) = xv[p];
+            }
+        }
+        // The raw registers are free: fetch the next chunk's, a part at a time
+        // (V, beta and the first row here, one row in each later phase), so
+        // that no wave stalls behind a burst of loads.
+        load_v(nxt);
+        load_beta(nxt);
+        load_row(nxt, 0);
+        __syncthreads();
 
         // ---- A_kk and A_qk blocks, transposed products: lane (i, g) receives
         // A[16I + i][16J + 4g + r] ----
@@ -331,141 +374,130 @@ __global__ __launch_bounds__(256, 1) void kda_intra_kernel(
                 mma(accQ, bK, aQ);
             }
         };
-        // Exact diagonal block (decay span beyond the split-factor range): lane
-        // (row li, channel quarter lg) sums one exp per (column, channel) over
-        // its quarter, reading the chunk from global memory, then the quarters
-        // are reduced.
+        // Exact diagonal block I, for decay spans beyond the split-factor
+        // range: lane (i, g) sums A[16I + i][16I + 4g + r] over every channel
+        // with one exp per term.  Row 16I + i of the chunk sits in lane i of
+        // each 16-lane group, whose shuffle scan yields the prefix sums of g.
+        // Slow but light on registers; unscaled, unmasked.
         auto diag_exact = [&](int I, f32x4 &accK, f32x4 &accQ) {
-            constexpr int CQ = DK / 4;
-            float aK[kSub], aQ[kSub];
+            accK = f32x4{0.f, 0.f, 0.f, 0.f};
+            accQ = accK;
+            const int row = I * kSub + li;
+            const bool in = row < C;
+            const size_t base = ((size_t)(cur.row0 + (in ? row : 0)) * H + cur.h) * DK;
+#pragma unroll 1
+            for (int c0 = 0; c0 < DK; c0 += 4) {
+                f32x4 gv = {0.f, 0.f, 0.f, 0.f}, kv = gv, qv = gv;
+                if (in) {
+                    gv = *reinterpret_cast<const f32x4 *>(g + base + c0);
+                    kv = to_f32<E>(*reinterpret_cast<const R4 *>(k + base + c0));
+                    qv = to_f32<E>(*reinterpret_cast<const R4 *>(q + base + c0));
+                }
 #pragma unroll
-            for (int jj = 0; jj < kSub; ++jj) { aK[jj] = 0.f; aQ[jj] = 0.f; }
-            const int ri = I * kSub + li;
-            for (int c = lg * CQ; c < (lg + 1) * CQ; ++c) {
-                float gcum[kSub], kc[kSub];
-                float run = 0.f;
+                for (int x = 0; x < 4; ++x) {
+                    float G = gv[x] * kLog2e;
 #pragma unroll
-                for (int jj = 0; jj < kSub; ++jj) {
-                    const int row = I * kSub + jj;
-                    float gg = 0.f, kk = 0.f;
-                    if (row < C) {
-                        const size_t off = ((size_t)(cur.row0 + row) * H + cur.h) * DK + c;
-                        gg = g[off];
-                        kk = (float)k[off];
+                    for (int d = 1; d < kSub; d <<= 1) {
+                        const float t = __shfl_up(G, d, kSub);
+                        if (li >= d) G += t;
                     }
-                    run += gg * kLog2e;
-                    gcum[jj] = run;
-                    kc[jj] = kk;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 4 * lg + r;
+                        const float Gj = __shfl(G, 16 * lg + j);
+                        const float kj = __shfl(kv[x], 16 * lg + j);
+                        const float e = j <= li ? fast_exp2(G - Gj) : 0.f;
+                        accK[r] = fmaf(kv[x] * kj, e, accK[r]);
+                        accQ[r] = fmaf(qv[x] * kj, e, accQ[r]);
+                    }
                 }
-                float gi = 0.f, ki = 0.f, qi = 0.f;
-#pragma unroll
-                for (int jj = 0; jj < kSub; ++jj) {
-                    if (jj == li) { gi = gcum[jj]; ki = kc[jj]; }
-                }
-                if (ri < C) qi = (float)q[((size_t)(cur.row0 + ri) * H + cur.h) * DK + c];
-#pragma unroll
-                for (int jj = 0; jj < kSub; ++jj) {
-                    const float e = jj <= li ? fast_exp2(gi - gcum[jj]) : 0.f;
-                    const float t = kc[jj] * e;
-                    aK[jj] = fmaf(ki, t, aK[jj]);
-                    aQ[jj] = fmaf(qi, t, aQ[jj]);
-                }
-            }
-#pragma unroll
-            for (int jj = 0; jj < kSub; ++jj) {
-                aK[jj] += __shfl_xor(aK[jj], 16);
-                aK[jj] += __shfl_xor(aK[jj], 32);
-                aQ[jj] += __shfl_xor(aQ[jj], 16);
-                aQ[jj] += __shfl_xor(aQ[jj], 32);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float sk = 0.f, sq = 0.f;
-#pragma unroll
-                for (int jj = 0; jj < kSub; ++jj) {
-                    if (jj == 4 * lg + r) { sk = aK[jj]; sq = aQ[jj]; }
-                }
-                accK[r] = sk;
-                accQ[r] = sq;
             }
         };
-        // wave w: diagonal block w, and off-diagonal pairs w and w + 4 of
-        // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-        auto pair_i = [](int p) { return p == 0 ? 1 : (p < 3 ? 2 : 3); };
-        auto pair_j = [](int p) { return p == 0 ? 0 : (p < 3 ? p - 1 : p - 3); };
-        const int p0 = wave, p1 = wave + 4;
-        f32x4 dK, dQ, oK[2], oQ[2];
-        if (sExact[wave]) diag_exact(wave, dK, dQ);
-        else ablock(wave, wave, dK, dQ);
-        ablock(pair_i(p0), pair_j(p0), oK[0], oQ[0]);
-        if (p1 < 6) ablock(pair_i(p1), pair_j(p1), oK[1], oQ[1]);
-        __syncthreads();   // k P, q P, k Qf are no longer read
+        // A_qk block (I, J) is half J % 2 of the scan's fragment (I, J / 2):
+        // lane (i, g) holds its elements 4 (J % 2) .. + 3.
+        auto put_aqk = [&](int I, int J, const f32x4 &vq) {
+            store4<E>(Ra + tri_frag(I, J >> 1) * 512 + lane * 8 + 4 * (J & 1), vq);
+        };
 
-        // ---- A_kk (beta-scaled) -> sA, A_qk -> sAqk, V -> where k Qf was ----
-        for (int idx = tid; idx < 6 * 256; idx += NTH) {     // blocks above the diagonal
-            const int b = idx >> 8, e = idx & 255;
-            const int I = b < 3 ? 0 : (b < 5 ? 1 : 2);
-            const int J = b < 3 ? b + 1 : (b < 5 ? b - 1 : 3);
-            const int r = I * kSub + (e >> 4), c = J * kSub + (e & 15);
-            sA[r * AP + c] = 0.f;
-            sAqk[r * AQP + c] = (E)0.f;
-        }
-        {
-            auto put = [&](int I, int J, const f32x4 &aK, const f32x4 &aQ, bool diag) {
-                const int row = I * kSub + li;
-                const float b = sBeta[row];
-                f32x4 vk, vq;
+        // Waves 0..3: diagonal block I = wave and its inverse by forward
+        // substitution (every 16-lane group computes columns 0..15; group 0
+        // stores them).  Waves 4..7: the six blocks below the diagonal,
+        // (1,0) (3,2) | (2,0) (3,1) | (2,1) | (3,0), and the zero blocks
+        // (0,1) and (2,3), which are read as parts of 32-column slabs.
+        if (wave < 4) {
+            const int I = wave;
+            f32x4 dK, dQ;
+            if (__any(lane < C4 && sExact[I * C4 + (lane & (C4 - 1))] != 0)) diag_exact(I, dK, dQ);
+            else ablock(I, I, dK, dQ);
+            const float b = sBeta[I * kSub + li];
+            f32x4 vk, vq;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int col = 4 * lg + r;
-                    vk[r] = (!diag || col < li) ? aK[r] * b : 0.f;
-                    vq[r] = (!diag || col <= li) ? aQ[r] : 0.f;
-                }
-                *reinterpret_cast<f32x4 *>(sA + row * AP + J * kSub + 4 * lg) = vk;
-                store4<E>(sAqk + row * AQP + J * kSub + 4 * lg, vq);
-            };
-            put(wave, wave, dK, dQ, true);
-            put(pair_i(p0), pair_j(p0), oK[0], oQ[0], false);
-            if (p1 < 6) put(pair_i(p1), pair_j(p1), oK[1], oQ[1], false);
-        }
-#pragma unroll
-        for (int p = 0; p < VPT; ++p) {
-            const int u = tid + p * NTH;
-            const int r = u / (DV / EPU), c = (u % (DV / EPU)) * EPU;
-            *reinterpret_cast<uint4 *>(sV + r * VP + c) = xv[p];
-        }
-        load_v(nxt);
-        __syncthreads();
-
-        // ---- A_qk fragments; diagonal 16x16 inverses of I + A_kk in place ----
-        {
-            const int m = wave;
-            const int row = m * kSub + li;
-            for (int s = 0; s <= (m >> 1); ++s) {
-                const int c0 = s * kSlab + 4 * lg;
-                store_frag<E>(Ra + tri_frag(m, s) * 512, lane,
-                              frag_from_runs<E>(sAqk + row * AQP + c0, sAqk + row * AQP + c0 + 16));
+            for (int r = 0; r < 4; ++r) {
+                const int col = 4 * lg + r;
+                vk[r] = col < li ? dK[r] * b : 0.f;
+                vq[r] = col <= li ? dQ[r] : 0.f;
             }
-        }
-        if (wave == 0) {
-            // Tm_II by forward substitution, lane = (block, column); every read of
-            // A_II precedes the writes, all within this wave.
-            const int I = lane >> 4, jj = lane & 15;
-            float t[kSub];
+            put_aqk(I, I, vq);
+            if (!(I & 1)) put_aqk(I, I + 1, f32x4{0.f, 0.f, 0.f, 0.f});
+            float *D = sD + I * kSub * DP;
+            *reinterpret_cast<f32x4 *>(D + li * DP + 4 * lg) = vk;
+            // the block was written by this wave only; LDS accesses of a wave
+            // complete in order
+            const int jj = li;
+            float tcol[kSub];
 #pragma unroll
             for (int ii = 0; ii < kSub; ++ii) {
                 float s = 0.f;
 #pragma unroll
-                for (int mm = 0; mm < ii; ++mm) s = fmaf(sA[(I * kSub + ii) * AP + I * kSub + mm], t[mm], s);
-                t[ii] = ii < jj ? 0.f : (ii == jj ? 1.f : -s);
+                for (int mm = 0; mm < ii; ++mm) s = fmaf(D[ii * DP + mm], tcol[mm], s);
+                tcol[ii] = ii < jj ? 0.f : (ii == jj ? 1.f : -s);
             }
+            if (lg == 0) {
 #pragma unroll
-            for (int ii = 0; ii < kSub; ++ii) sA[(I * kSub + ii) * AP + I * kSub + jj] = t[ii];
+                for (int ii = 0; ii < kSub; ++ii) sA[(I * kSub + ii) * AP + I * kSub + li] = tcol[ii];
+            }
+        } else {
+            const int w4 = wave - 4;
+            const int nb = w4 < 2 ? 2 : 1;
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi) {
+                if (bi >= nb) break;
+                const int I = bi == 0 ? (w4 == 0 ? 1 : (w4 == 3 ? 3 : 2)) : 3;
+                const int J = bi == 0 ? (w4 == 2 ? 1 : 0) : (w4 == 0 ? 2 : 1);
+                f32x4 oK, oQ;
+                ablock(I, J, oK, oQ);
+                put_aqk(I, J, oQ);
+                *reinterpret_cast<f32x4 *>(sA + (I * kSub + li) * AP + J * kSub + 4 * lg) =
+                    oK * sBeta[I * kSub + li];
+            }
+            if (w4 >= 2) {
+                const int I = w4 == 2 ? 0 : 2;
+                *reinterpret_cast<f32x4 *>(sA + (I * kSub + li) * AP + (I + 1) * kSub + 4 * lg) =
+                    f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
-        __syncthreads();
+        load_row(nxt, 1);
+        __syncthreads();   // sA holds A_kk below the diagonal and the diagonal inverses
 
-        // ---- off-diagonal blocks of Tm on fp32 matrix cores, in place ----
-        // level 1 (waves 0, 1): Tm_10 = -Tm_11 (A_10 Tm_00), Tm_32 = -Tm_33 (A_32 Tm_22)
+        // ---- off-diagonal blocks of Tm on fp32 matrix cores ----
+        // level 1 (waves 0, 1), in place: Tm_10 = -Tm_11 (A_10 Tm_00), Tm_32 = -Tm_33 (A_32 Tm_22).
+        // Meanwhile waves 2..7 write Q e^Gam in the scan's fragment order:
+        // fragment (m, s) holds row 16m + i, channels 32s + kk(g, e).
+        if (wave >= 2) {
+            for (int f = wave - 2; f < 4 * KS; f += 6) {
+                const int row = (f / KS) * kSub + li, c0 = (f % KS) * kSlab + 4 * lg;
+                Frag<E> fr;
+                if constexpr (LD::kStage) {
+                    fr = frag_from_runs<E>(sQh + row * KPP + c0, sQh + row * KPP + c0 + 16);
+                } else {
+                    fr = frag_from_runs<E>(sQP + row * KPP + c0, sQP + row * KPP + c0 + 16);
+                    const float *eb = sBs + (f / KS) * DK + c0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) fr.set(e, fr.get(e) * eb[(e & 3) + 16 * (e >> 2)]);
+                }
+                store_frag<E>(Rq + f * 512, lane, fr);
+            }
+        }
         if (wave < 2) {
             const int I = wave ? 3 : 1, J = I - 1;
             f32x4 P = {0.f, 0.f, 0.f, 0.f};
@@ -481,9 +513,27 @@ __global__ __launch_bounds__(256, 1) void kda_intra_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) sA[(I * kSub + 4 * lg + r) * AP + J * kSub + li] = -Tt[r];
         }
+        load_row(nxt, 2);
         __syncthreads();
-        // level 2 (wave = output tile (ti, tj)): Tm[32:64, 0:32] = -Tm_hi (A[32:64, 0:32] Tm_lo)
-        {
+        // level 2 (waves 0..3, output tile (ti, tj)) into sT2:
+        // Tm[32:64, 0:32] = -Tm_hi (A[32:64, 0:32] Tm_lo).
+        // Meanwhile waves 4..7 write K e^{Gam_C - Gam}, transposed, in the
+        // scan's order: fragment (t, s) holds key channels 16t + i over chunk
+        // rows 32s + kk(g, e).
+        if (wave >= 4) {
+            for (int f = wave - 4; f < 2 * KT; f += 4) {
+                const int ch = (f >> 1) * kSub + li;
+                const float ce0 = sCe[(2 * (f & 1)) * DK + ch], ce1 = sCe[(2 * (f & 1) + 1) * DK + ch];
+                Frag<E> fr;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int row = (f & 1) * kSlab + kk_of(lg, e);
+                    fr.set(e, sKQ[row * KQP + ch] * (e < 4 ? ce0 : ce1));
+                }
+                store_frag<E>(Rk + f * 512, lane, fr);
+            }
+        }
+        if (wave < 4) {
             const int ti = wave >> 1, tj = wave & 1;
             f32x4 Qt[2];
 #pragma unroll
@@ -503,58 +553,85 @@ __global__ __launch_bounds__(256, 1) void kda_intra_kernel(
                     Tt = __builtin_amdgcn_mfma_f32_16x16x4f32(
                         sA[(32 + ti * kSub + li) * AP + 32 + kt * kSub + 4 * lg + r], Qt[kt][r], Tt, 0, 0, 0);
             }
-            __syncthreads();   // every wave has read A[32:64, 0:32]
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sA[(32 + ti * kSub + 4 * lg + r) * AP + tj * kSub + li] = -Tt[r];
+            for (int r = 0; r < 4; ++r) sT2[(ti * kSub + 4 * lg + r) * T2P + tj * kSub + li] = -Tt[r];
         }
+        load_row(nxt, 3);
         __syncthreads();
 
-        // ---- w and u on the matrix cores ----
-        Frag<E> tf[6];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-#pragma unroll
-            for (int s = 0; s <= (m >> 1); ++s) {
-                const int row = m * kSub + li, c0 = s * kSlab + 4 * lg;
-                tf[tri_frag(m, s)] = frag_from_tiles<E>(*reinterpret_cast<const f32x4 *>(sA + row * AP + c0),
-                                                        *reinterpret_cast<const f32x4 *>(sA + row * AP + c0 + 16));
-            }
-        }
-        if (wave < KS) {
-            // w slab `wave` (key channels 32 wave ..), computed transposed as
-            // X^T Tm^T: lane (i, g) receives w[16m + i][16n + 4g + r], the scan's
-            // A-operand order.
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-#pragma unroll
-                for (int s = 0; s <= (m >> 1); ++s) {
-                    mma(acc0, xf[0][s], tf[tri_frag(m, s)]);
-                    mma(acc1, xf[1][s], tf[tri_frag(m, s)]);
-                }
-                store_frag<E>(Rw + (m * KS + wave) * 512, lane, frag_from_tiles<E>(acc0, acc1));
-            }
-        }
-        for (int jt = wave; jt < VT; jt += 4) {
-            // u tile (value columns 16 jt ..): Tm diag(beta) V, lane (i, g) holds
-            // u[16m + 4g + r][16 jt + i].
-            const int ch = jt * kSub + li;
+        // ---- w and u on the matrix cores, with diag(beta) folded into Tm ----
+        // fragment (m, s) of Tm diag(beta): row 16 m + i, columns 32 s + kk(g, e)
+        auto tm_frag = [&](int m, int s) {
+            const int row = m * kSub + li, c0 = s * kSlab + 4 * lg;
+            const float *src = (m >= 2 && s == 0) ? sT2 + (row - 32) * T2P + c0 : sA + row * AP + c0;
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(src) * *reinterpret_cast<const f32x4 *>(sBeta + c0);
+            const f32x4 b = *reinterpret_cast<const f32x4 *>(src + 16) *
+                            *reinterpret_cast<const f32x4 *>(sBeta + c0 + 16);
+            return frag_from_tiles<E>(a, b);
+        };
+        // w: wave owns d_k slab `wslab` of row tiles wm0 .. wm0 + MPW - 1;
+        // u: wave owns value tile `wave` (if any)
+        const int wslab = wave % KS, wm0 = (wave / KS) * MPW;
+        const int smax = (wm0 + MPW - 1) >> 1;
+        if (wave < VT) {
+            // u tile (value columns 16 wave ..): Tm diag(beta) V, lane (i, g)
+            // holds u[16m + 4g + r][16 wave + i]; V fragments: value column
+            // 16 wave + i, rows 32 s + kk(g, e)
             Frag<E> vf[2];
+            if constexpr (LD::kStage) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
+                for (int s = 0; s < 2; ++s) vf[s] = frag_cols<E>(sV, VP, s * kSlab, wave * kSub, lane);
+            } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int row = s * kSlab + kk_of(lg, e);
-                    vf[s].set(e, sBeta[row] * (float)sV[row * VP + ch]);
-                }
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int row = s * kSlab + kk_of(lg, e);
+                        vf[s].set(e, row < C ? (float)v[((size_t)(cur.row0 + row) * H + cur.h) * DV + wave * kSub + li]
+                                             : 0.f);
+                    }
             }
-            E *dst = Ru + jt * (64 * 16) + lane * 16;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                mma(acc, tm_frag(m, 0), vf[0]);
+                if (m >= 2) mma(acc, tm_frag(m, 1), vf[1]);
+                store4<E>(Ru + wave * (64 * 16) + lane * 16 + 4 * m, acc);
+            }
+        }
+        {
+            // w slab `wslab`, computed transposed as X^T Tm^T: lane (i, g)
+            // receives w[16m + i][32 wslab + kk(g, e)], the scan's A-operand
+            // order.  K e^Gam fragments: channel 16 (2 wslab + nn) + i, rows
+            // 32 s + kk(g, e).
+            Frag<E> xf[2][2];
 #pragma unroll
-                for (int s = 0; s <= (m >> 1); ++s) mma(acc, tf[tri_frag(m, s)], vf[s]);
-                store4<E>(dst + 4 * m, acc);
+            for (int nn = 0; nn < 2; ++nn)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (s > smax) continue;
+                    const int n0 = (2 * wslab + nn) * kSub;
+                    if constexpr (LD::kStage) {
+                        xf[nn][s] = frag_cols<E>(sX, KPP, s * kSlab, n0, lane);
+                    } else {
+                        xf[nn][s] = frag_cols<E>(sKP, KPP, s * kSlab, n0, lane);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            xf[nn][s].set(e, xf[nn][s].get(e) * sBs[(2 * s + (e >> 2)) * DK + n0 + li]);
+                    }
+                }
+#pragma unroll
+            for (int mi = 0; mi < MPW; ++mi) {
+                const int m = wm0 + mi;
+                f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (s > (m >> 1)) break;
+                    const Frag<E> t = tm_frag(m, s);
+                    mma(acc0, xf[0][s], t);
+                    mma(acc1, xf[1][s], t);
+                }
+                store_frag<E>(Rw + (m * KS + wslab) * 512, lane, frag_from_tiles<E>(acc0, acc1));
             }
         }
         __syncthreads();   // LDS is rewritten by the next chunk
@@ -776,9 +853,8 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     if (a.events[0]) (void)hipEventRecord(a.events[0], stream);
     if (max_chunks > 0) {
         const long long items = (long long)max_chunks * a.H;
-        const int per_cu = 1;
-        const int grid = (int)(items < (long long)a.num_cus * per_cu ? items : (long long)a.num_cus * per_cu);
-        kda_intra_kernel<E, DK, DV><<<dim3(grid), dim3(256), 0, stream>>>(
+        const int grid = (int)(items < (long long)a.num_cus ? items : (long long)a.num_cus);
+        kda_intra_kernel<E, DK, DV><<<dim3(grid), dim3(kIntraThreads), 0, stream>>>(
             static_cast<const E *>(a.q), static_cast<const E *>(a.k), static_cast<const E *>(a.v),
             a.g, a.beta, a.cu_seqlens, a.T, a.N, a.H, ws, ws_dec);
     }
