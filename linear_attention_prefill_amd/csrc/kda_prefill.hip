@@ -649,7 +649,7 @@ template <typename E, int DK> struct ScanStage {
     static constexpr int TPW = DK / 64;
     Frag<E> wf[KS], qf[KS], af[2], kf[TPW][2];
     typename Raw4<E>::type u;                  // raw: converted where it is used
-    f32x4 d[TPW];
+    float d;                                   // e^{Gam_C} of key row 16 TPW wave + (lane % (16 TPW))
 };
 
 template <typename E, int DK, int DV>
@@ -753,8 +753,9 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(
             const int t = wave * TPW + i;
             X.kf[i][0] = load_frag<E>(Rk + (t * 2) * 512, lane);
             X.kf[i][1] = load_frag<E>(Rk + (t * 2 + 1) * 512, lane);
-            X.d[i] = *reinterpret_cast<const f32x4 *>(ws_dec + rec * DK + t * kSub + 4 * lg);
         }
+        // this wave's 16 TPW decay factors, one per lane (lanes repeat them)
+        X.d = ws_dec[rec * DK + wave * (TPW * kSub) + (lane & (TPW * kSub - 1))];
     };
     auto load_stage = [&](Stage &X, int cc) {
         load_w(X, cc);
@@ -798,7 +799,9 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(
         }
         if (refill) load_q(X, nx);
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) S[i] *= X.d[i];
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[i][r] *= __shfl(X.d, i * kSub + 4 * lg + r);
         __syncthreads();
         Frag<E> ub[2];
         ub[0] = load_frag<E>(sUb, lane);
