@@ -10,17 +10,26 @@
 //   S[:, j] = s' + d_j k                     write back in place
 //   o_j = scale (s'.q + d_j (k.q))           = scale S_new[:, j].q
 // so each 4 * d_k-byte row is read once and written once.  A workgroup of 256
-// threads covers 64 rows of one (sequence, head); d_k / 4 lanes share a row,
-// each lane holding four key channels, and the two dot products are reduced
-// across those lanes with cross-lane shuffles.  Every lane issues all of its
-// row loads before any arithmetic, so each workgroup keeps 64 rows
-// (16-32 KiB) in flight.
+// threads covers 64 rows of one (sequence, head); a row is spread over the 16
+// lanes of a DPP row, each lane holding d_k / 16 key channels, and the two dot
+// products are summed across those lanes with four row rotations.  Every lane
+// issues all of its row loads before any arithmetic, so each workgroup keeps
+// 64 rows (16-32 KiB) in flight.
 #include "kda_device.h"
 #include "kda_launch.h"
 
 namespace kda {
 
 constexpr int kDecodeRows = 64;
+
+// Sum over the 16 lanes of a DPP row, left in every lane (row_ror 8, 4, 2, 1).
+__device__ __forceinline__ float row_allreduce(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));
+    return x;
+}
 
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256) void kda_decode_kernel(
@@ -29,8 +38,9 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     const int32_t *__restrict__ slots, E *__restrict__ o, int N, int H, int num_slots,
     float scale) {
     constexpr int PARTS = DV / kDecodeRows;
-    constexpr int LPR = DK / 4;          // lanes per state row
-    constexpr int RPI = 256 / LPR;       // rows covered by one pass of the workgroup
+    constexpr int CPL = DK / 16;         // key channels per lane
+    constexpr int V4 = CPL / 4;          // float4 per lane and row
+    constexpr int RPI = 256 / 16;        // rows covered by one pass of the workgroup
     constexpr int P = kDecodeRows / RPI; // passes
     const int tid = threadIdx.x;
     const int part = blockIdx.x % PARTS;
@@ -39,45 +49,66 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     if (n >= N) return;
     const int slot = slots[n];
     if (slot < 0 || slot >= num_slots) return;   // padded row: touch nothing
-    const int c4 = tid % LPR, rr = tid / LPR;
+    const int c = tid & 15, rr = tid >> 4;
     const size_t tok = (size_t)n * H + h;
 
-    const f32x4 k4 = load4<E>(k + tok * DK + 4 * c4);
-    const f32x4 q4 = load4<E>(q + tok * DK + 4 * c4);
-    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(g + tok * DK + 4 * c4);
+    // lane c holds key channels 4 (c + 16 x) .. + 3, x < V4, so that a row's
+    // lanes read consecutive 16-byte pieces
+    f32x4 k4[V4], q4[V4], a4[V4];
+#pragma unroll
+    for (int x = 0; x < V4; ++x) {
+        const int ch = 4 * (c + 16 * x);
+        k4[x] = load4<E>(k + tok * DK + ch);
+        q4[x] = load4<E>(q + tok * DK + ch);
+        a4[x] = *reinterpret_cast<const f32x4 *>(g + tok * DK + ch);
+    }
     const float bt = beta[tok];
     float *S = pool + ((size_t)slot * H + h) * (size_t)DV * DK;
 
-    f32x4 s[P];
+    f32x4 s[P][V4];
     float vv[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         const int row = part * kDecodeRows + p * RPI + rr;
-        s[p] = *reinterpret_cast<const f32x4 *>(S + (size_t)row * DK + 4 * c4);
+#pragma unroll
+        for (int x = 0; x < V4; ++x)
+            s[p][x] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)row * DK + 4 * (c + 16 * x)));
         vv[p] = (float)v[tok * DV + row];
     }
 
-    f32x4 a4;
+    float kq = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) a4[r] = fast_exp2(g4[r] * kLog2e);
-    float kq = k4[0] * q4[0] + k4[1] * q4[1] + k4[2] * q4[2] + k4[3] * q4[3];
+    for (int x = 0; x < V4; ++x) {
 #pragma unroll
-    for (int m = 1; m < LPR; m <<= 1) kq += __shfl_xor(kq, m);
+        for (int r = 0; r < 4; ++r) {
+            a4[x][r] = fast_exp2(a4[x][r] * kLog2e);
+            kq += k4[x][r] * q4[x][r];
+        }
+    }
+    kq = row_allreduce(kq);
 
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         const int row = part * kDecodeRows + p * RPI + rr;
-        const f32x4 sp = s[p] * a4;
-        float dk = sp[0] * k4[0] + sp[1] * k4[1] + sp[2] * k4[2] + sp[3] * k4[3];
-        float dq = sp[0] * q4[0] + sp[1] * q4[1] + sp[2] * q4[2] + sp[3] * q4[3];
+        f32x4 sp[V4];
+        float dk = 0.f, dq = 0.f;
 #pragma unroll
-        for (int m = 1; m < LPR; m <<= 1) {
-            dk += __shfl_xor(dk, m);
-            dq += __shfl_xor(dq, m);
+        for (int x = 0; x < V4; ++x) {
+            sp[x] = s[p][x] * a4[x];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                dk += sp[x][r] * k4[x][r];
+                dq += sp[x][r] * q4[x][r];
+            }
         }
+        dk = row_allreduce(dk);
+        dq = row_allreduce(dq);
         const float d = bt * (vv[p] - dk);
-        *reinterpret_cast<f32x4 *>(S + (size_t)row * DK + 4 * c4) = sp + d * k4;
-        if (c4 == 0) o[tok * DV + row] = (E)(scale * (dq + d * kq));
+#pragma unroll
+        for (int x = 0; x < V4; ++x)
+            __builtin_nontemporal_store(sp[x] + d * k4[x],
+                                        reinterpret_cast<f32x4 *>(S + (size_t)row * DK + 4 * (c + 16 * x)));
+        if (c == 0) o[tok * DV + row] = (E)(scale * (dq + d * kq));
     }
 }
 
