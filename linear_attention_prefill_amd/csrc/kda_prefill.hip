@@ -653,7 +653,7 @@ template <typename E, int DK> struct ScanStage {
 };
 
 template <typename E, int DK, int DV>
-__global__ __launch_bounds__(256) void kda_scan_kernel(
+__global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     const E *__restrict__ ws, const float *__restrict__ ws_dec,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ slots,
     const float *state_in, float *state_out, E *__restrict__ o,
