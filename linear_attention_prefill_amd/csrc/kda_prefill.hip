@@ -181,10 +181,14 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
         if (cu_reg) return __builtin_amdgcn_readlane(cu_v, i);
         return __builtin_amdgcn_readfirstlane(cu_lds ? sCu[i] : cu_s[i]);
     };
-    // First chunk at or after `item` in steps of the grid that belongs to a
-    // sequence (ids between sequences' chunk ranges are skipped).
-    auto find_chunk = [&](int item) -> ChunkRef {
-        for (; item < n_items; item += stride) {
+    // Items are walked from the last one down (t-th visited item is
+    // n_items - 1 - t), so the records the state scan reads first are the
+    // ones written last and are still in the caches when it starts.  Returns
+    // the first item at or after position t, in steps of the grid, that
+    // belongs to a sequence (ids between sequences' chunk ranges are skipped).
+    auto find_chunk = [&](int t) -> ChunkRef {
+        for (; t < n_items; t += stride) {
+            const int item = n_items - 1 - t;
             const int cid = item / H;
             int lo = 0, hi = N - 1;
             while (lo < hi) {
@@ -258,7 +262,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
         E *const Rk = Rq + L::kQElems;
         E *const Ra = Rk + L::kKElems;
         E *const Ru = Ra + L::kAElems;
-        const ChunkRef nxt = find_chunk(cur.item + stride);
+        const ChunkRef nxt = find_chunk(n_items - 1 - cur.item + stride);
 
         // ---- per-row factors (log2 units); everything derived from k, q, V
         // leaves the registers ----
