@@ -181,15 +181,24 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
         if (cu_reg) return __builtin_amdgcn_readlane(cu_v, i);
         return __builtin_amdgcn_readfirstlane(cu_lds ? sCu[i] : cu_s[i]);
     };
-    // Items are walked from the last one down (t-th visited item is
-    // n_items - 1 - t), so the records the state scan reads first are the
-    // ones written last and are still in the caches when it starts.  Returns
-    // the first item at or after position t, in steps of the grid, that
-    // belongs to a sequence (ids between sequences' chunk ranges are skipped).
-    auto find_chunk = [&](int t) -> ChunkRef {
-        for (; t < n_items; t += stride) {
-            const int item = n_items - 1 - t;
-            const int cid = item / H;
+    // Items (chunk id cid, head h; item = cid H + h) are walked from the last
+    // one down in steps of the grid, so the records the state scan reads
+    // first are the ones written last and are still in the caches when it
+    // starts.  The step is kept as a quotient and remainder of H, so the walk
+    // needs no division.  find_chunk returns the first item at or below (cid,
+    // h) on this walk that belongs to a sequence (ids between sequences'
+    // chunk ranges are skipped).
+    const int step_q = stride / H, step_r = stride % H;
+    auto step_down = [&](int &cid, int &h) {
+        h -= step_r;
+        cid -= step_q;
+        if (h < 0) {
+            h += H;
+            --cid;
+        }
+    };
+    auto find_chunk = [&](int cid, int h) -> ChunkRef {
+        for (; cid >= 0; step_down(cid, h)) {
             int lo = 0, hi = N - 1;
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
@@ -199,7 +208,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
             const int len = end > start ? end - start : 0;
             const int jc = cid - (start / kChunk + lo);
             if (jc >= 0 && jc * kChunk < len)
-                return ChunkRef{item, cid, item - cid * H, start + jc * kChunk, min(kChunk, len - jc * kChunk)};
+                return ChunkRef{cid * H + h, cid, h, start + jc * kChunk, min(kChunk, len - jc * kChunk)};
         }
         return ChunkRef{-1, 0, 0, 0, 0};
     };
@@ -237,7 +246,11 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
         }
     };
 
-    ChunkRef cur = find_chunk(blockIdx.x);
+    ChunkRef cur;
+    {
+        const int item0 = n_items - 1 - (int)blockIdx.x;
+        cur = find_chunk(item0 / H, item0 % H);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) load_row(cur, r);
     load_beta(cur);
@@ -262,7 +275,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
         E *const Rk = Rq + L::kQElems;
         E *const Ra = Rk + L::kKElems;
         E *const Ru = Ra + L::kAElems;
-        const ChunkRef nxt = find_chunk(n_items - 1 - cur.item + stride);
+        int ncid = cur.cid, nh = cur.h;
+        step_down(ncid, nh);
+        const ChunkRef nxt = find_chunk(ncid, nh);
 
         // ---- per-row factors (log2 units); everything derived from k, q, V
         // leaves the registers ----
