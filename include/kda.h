@@ -67,6 +67,22 @@ typedef enum {
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
 
+/*
+ * State addressing by lines.  The state block of (slot s, head h) is the dense
+ * [d_v][d_k] fp32 block at
+ *     pool + s * state_slot_stride + h * state_head_stride     (fp32 elements)
+ * so a state pool can live inside an engine's own pages: a KDA line at the
+ * start of each page, with other per-head data (a conv window) between the
+ * heads ("kern-k3-pp-prefill" page, section "D inside vLLM": vLLM's hybrid
+ * pages hold one KDA line at the start of each page, and the kernel's line
+ * stride is the one launch parameter that changes).  A stride of 0 selects
+ * the dense [num_slots][H][d_v][d_k] layout (slot stride H d_v d_k, head
+ * stride d_v d_k).  Given strides must be multiples of 4 with
+ * state_head_stride >= d_v d_k and
+ * state_slot_stride >= (H - 1) state_head_stride + d_v d_k, so no two blocks
+ * overlap; the pool must hold (num_slots - 1) slot strides plus one line.
+ */
+
 /* Sizes of one prefill call.  T = total_rows, N = num_seqs, H = num_heads. */
 typedef struct {
     int32_t total_rows;  /* T >= 0 */
@@ -77,6 +93,8 @@ typedef struct {
     int32_t num_slots;   /* rows of the state pools (the slot index space) */
     int32_t io_dtype;    /* kda_dtype_t of q, k, v and o */
     float scale;         /* multiplies o only */
+    int64_t state_slot_stride;  /* fp32 elements between slots' lines; 0 = dense */
+    int64_t state_head_stride;  /* fp32 elements between heads of a line; 0 = dense */
 } kda_prefill_desc_t;
 
 /*
@@ -104,10 +122,14 @@ size_t kda_prefill_workspace_size(const kda_prefill_desc_t *desc);
  *     are left untouched.
  * Slots not named by any live sequence are never read or written.
  *
+ * The state pools are addressed by lines as described above (dense when the
+ * desc's strides are 0).
+ *
  * Errors (returned before any launch): KDA_ERR_NULL for NULL desc, q, k, v,
  * g, beta, cu_seqlens, or o (when T > 0), or a NULL workspace of nonzero
- * required size; KDA_ERR_SHAPE for T < 0, N < 1, H < 1, num_slots < 0, or
- * slots == NULL with a state pool given and num_slots < N; KDA_ERR_DTYPE;
+ * required size; KDA_ERR_SHAPE for T < 0, N < 1, H < 1, num_slots < 0,
+ * slots == NULL with a state pool given and num_slots < N, or state strides
+ * that break the line rules; KDA_ERR_DTYPE;
  * KDA_ERR_UNSUPPORTED; KDA_ERR_ALIGN; KDA_ERR_WORKSPACE when ws_bytes is below
  * kda_prefill_workspace_size(desc); KDA_ERR_HIP if a launch fails.
  */
@@ -136,6 +158,22 @@ kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v
                                      const kda_prefill_desc_t *desc,
                                      void *workspace, size_t ws_bytes,
                                      void *stream, void *const *events);
+
+/*
+ * kda_decode_step with the state pool addressed by lines (see "State
+ * addressing by lines" above): the block of (slot s, head h) starts at
+ * state_pool + s * state_slot_stride + h * state_head_stride; strides of 0
+ * select the dense layout.  Errors as for kda_decode_step, plus KDA_ERR_SHAPE
+ * for strides that break the rules above.
+ */
+kda_status_t kda_decode_step_lines(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta,
+                                   float *state_pool, const int32_t *slots, void *o,
+                                   int32_t num_seqs, int32_t num_heads,
+                                   int32_t d_k, int32_t d_v, int32_t num_slots,
+                                   int32_t io_dtype, float scale,
+                                   int64_t state_slot_stride, int64_t state_head_stride,
+                                   void *stream);
 
 /*
  * One decode token per sequence, state updated in place (the KDA step of the

@@ -55,6 +55,19 @@ kda_status_t check_desc(const kda_prefill_desc_t *d) {
     return KDA_OK;
 }
 
+// Resolves the state strides (fp32 elements; 0 = dense) and checks the line
+// rules of kda.h: multiples of 4 (16-byte rows), blocks of one line and lines
+// of different slots never overlap.
+bool resolve_strides(int64_t slot_stride, int64_t head_stride, int H, int dk, int dv,
+                     int64_t *ss, int64_t *hs) {
+    const int64_t block = (int64_t)dk * dv;
+    *hs = head_stride ? head_stride : block;
+    *ss = slot_stride ? slot_stride : (int64_t)H * *hs;
+    if (*hs < block || *hs % 4) return false;
+    if (*ss % 4 || *ss < (int64_t)(H - 1) * *hs + block) return false;
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,6 +97,9 @@ kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_ALIGN;
     if (ws_bytes < need) return KDA_ERR_WORKSPACE;
+    int64_t ss = 0, hs = 0;
+    if (!resolve_strides(d.state_slot_stride, d.state_head_stride, d.num_heads, d.d_k, d.d_v, &ss, &hs))
+        return KDA_ERR_SHAPE;
 
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens;
@@ -91,6 +107,8 @@ kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v
     a.workspace = workspace;
     a.T = d.total_rows; a.N = d.num_seqs; a.H = d.num_heads; a.num_slots = d.num_slots;
     a.scale = d.scale;
+    a.slot_stride = ss;
+    a.head_stride = hs;
     for (int i = 0; i < 3; ++i) a.events[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
     a.num_cus = device_cus();
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -108,10 +126,12 @@ kda_status_t kda_chunk_prefill(const void *q, const void *k, const void *v, cons
                                    desc, workspace, ws_bytes, stream, nullptr);
 }
 
-kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const float *g,
-                             const float *beta, float *state_pool, const int32_t *slots, void *o,
-                             int32_t num_seqs, int32_t num_heads, int32_t d_k, int32_t d_v,
-                             int32_t num_slots, int32_t io_dtype, float scale, void *stream) {
+kda_status_t kda_decode_step_lines(const void *q, const void *k, const void *v, const float *g,
+                                   const float *beta, float *state_pool, const int32_t *slots,
+                                   void *o, int32_t num_seqs, int32_t num_heads, int32_t d_k,
+                                   int32_t d_v, int32_t num_slots, int32_t io_dtype, float scale,
+                                   int64_t state_slot_stride, int64_t state_head_stride,
+                                   void *stream) {
     if (io_dtype != KDA_F32 && io_dtype != KDA_BF16) return KDA_ERR_DTYPE;
     if (!dims_supported(d_k, d_v)) return KDA_ERR_UNSUPPORTED;
     if (num_seqs < 1 || num_heads < 1 || num_slots < 1) return KDA_ERR_SHAPE;
@@ -120,13 +140,26 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
     const void *ptrs[] = {q, k, v, g, beta, state_pool, slots, o};
     for (const void *p : ptrs)
         if (!aligned16(p)) return KDA_ERR_ALIGN;
+    int64_t ss = 0, hs = 0;
+    if (!resolve_strides(state_slot_stride, state_head_stride, num_heads, d_k, d_v, &ss, &hs))
+        return KDA_ERR_SHAPE;
     kda::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.pool = state_pool; a.slots = slots;
     a.o = o; a.N = num_seqs; a.H = num_heads; a.num_slots = num_slots; a.scale = scale;
+    a.slot_stride = ss;
+    a.head_stride = hs;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = io_dtype == KDA_BF16 ? dispatch_decode<bf16>(a, d_k, d_v, s)
                                               : dispatch_decode<float>(a, d_k, d_v, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, float *state_pool, const int32_t *slots, void *o,
+                             int32_t num_seqs, int32_t num_heads, int32_t d_k, int32_t d_v,
+                             int32_t num_slots, int32_t io_dtype, float scale, void *stream) {
+    return kda_decode_step_lines(q, k, v, g, beta, state_pool, slots, o, num_seqs, num_heads, d_k,
+                                 d_v, num_slots, io_dtype, scale, 0, 0, stream);
 }
 
 const char *kda_status_string(kda_status_t status) {
@@ -143,6 +176,6 @@ const char *kda_status_string(kda_status_t status) {
     return "unknown status";
 }
 
-int32_t kda_version(void) { return 100; }
+int32_t kda_version(void) { return 101; }
 
 }  // extern "C"

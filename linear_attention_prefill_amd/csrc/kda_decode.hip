@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *pool,
     const int32_t *__restrict__ slots, E *__restrict__ o, int N, int H, int num_slots,
-    float scale) {
+    float scale, int64_t slot_stride, int64_t head_stride) {
     constexpr int PARTS = DV / kDecodeRows;
     constexpr int CPL = DK / 16;         // key channels per lane
     constexpr int V4 = CPL / 4;          // float4 per lane and row
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
         a4[x] = *reinterpret_cast<const f32x4 *>(g + tok * DK + ch);
     }
     const float bt = beta[tok];
-    float *S = pool + ((size_t)slot * H + h) * (size_t)DV * DK;
+    float *S = pool + slot * slot_stride + h * head_stride;
 
     f32x4 s[P][V4];
     float vv[P];
@@ -117,7 +117,8 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     const int nblocks = a.N * a.H * (DV / kDecodeRows);
     kda_decode_kernel<E, DK, DV><<<dim3(nblocks), dim3(256), 0, stream>>>(
         static_cast<const E *>(a.q), static_cast<const E *>(a.k), static_cast<const E *>(a.v),
-        a.g, a.beta, a.pool, a.slots, static_cast<E *>(a.o), a.N, a.H, a.num_slots, a.scale);
+        a.g, a.beta, a.pool, a.slots, static_cast<E *>(a.o), a.N, a.H, a.num_slots, a.scale,
+        a.slot_stride, a.head_stride);
     return hipGetLastError();
 }
 

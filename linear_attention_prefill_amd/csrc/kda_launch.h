@@ -18,6 +18,7 @@ struct PrefillArgs {
     void *workspace;
     int T, N, H, num_slots;
     float scale;
+    int64_t slot_stride, head_stride;   // state addressing, fp32 elements (resolved)
     int num_cus;            // compute units of the device (persistent grids)
     hipEvent_t events[3];   // optional: before intra, between, after scan
 };
@@ -30,6 +31,7 @@ struct DecodeArgs {
     void *o;
     int N, H, num_slots;
     float scale;
+    int64_t slot_stride, head_stride;   // state addressing, fp32 elements (resolved)
 };
 
 template <typename E, int DK, int DV>

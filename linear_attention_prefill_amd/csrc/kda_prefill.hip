@@ -676,7 +676,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     const E *__restrict__ ws, const float *__restrict__ ws_dec,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ slots,
     const float *state_in, float *state_out, E *__restrict__ o,
-    int T, int N, int H, int num_slots, float scale) {
+    int T, int N, int H, int num_slots, float scale, int64_t slot_stride, int64_t head_stride) {
     constexpr int VT = DV / kSub, KS = DK / kSlab;
     constexpr int TPW = DK / 64;                       // key tiles per wave
     using L = WsLayout<E, DK, DV>;
@@ -724,7 +724,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     // my key tiles t = wave * TPW + i, C layout: lane holds S[16t + 4g + r][j0 + i]
     f32x4 S[TPW];
     if (state_in) {
-        const float *src = state_in + (((size_t)slot * H + h) * DV + j0 + li) * DK;
+        const float *src = state_in + slot * slot_stride + h * head_stride + (size_t)(j0 + li) * DK;
 #pragma unroll
         for (int i = 0; i < TPW; ++i)
             S[i] = *reinterpret_cast<const f32x4 *>(src + (wave * TPW + i) * kSub + 4 * lg);
@@ -858,7 +858,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     }
 
     if (state_out) {
-        float *dst = state_out + (((size_t)slot * H + h) * DV + j0 + li) * DK;
+        float *dst = state_out + slot * slot_stride + h * head_stride + (size_t)(j0 + li) * DK;
 #pragma unroll
         for (int i = 0; i < TPW; ++i)
             *reinterpret_cast<f32x4 *>(dst + (wave * TPW + i) * kSub + 4 * lg) = S[i];
@@ -884,7 +884,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     const int nblocks = a.N * a.H * (DV / kSub);
     kda_scan_kernel<E, DK, DV><<<dim3(nblocks), dim3(256), 0, stream>>>(
         ws, ws_dec, a.cu_seqlens, a.slots, a.state_in, a.state_out, static_cast<E *>(a.o),
-        a.T, a.N, a.H, a.num_slots, a.scale);
+        a.T, a.N, a.H, a.num_slots, a.scale, a.slot_stride, a.head_stride);
     const hipError_t e = hipGetLastError();
     if (a.events[2]) (void)hipEventRecord(a.events[2], stream);
     return e;

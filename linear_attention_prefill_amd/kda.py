@@ -27,7 +27,8 @@ class PrefillDesc(ctypes.Structure):
     _fields_ = [("total_rows", ctypes.c_int32), ("num_seqs", ctypes.c_int32),
                 ("num_heads", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("num_slots", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("state_slot_stride", ctypes.c_int64),
+                ("state_head_stride", ctypes.c_int64)]
 
 
 class KdaError(RuntimeError):
@@ -62,6 +63,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                     i32, i32, i32, i32, i32, i32, f32, vp]
+    i64 = ctypes.c_int64
+    lib.kda_decode_step_lines.restype = ctypes.c_int
+    lib.kda_decode_step_lines.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
+                                          i32, i32, i32, i32, i32, i32, f32, i64, i64, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_version.restype = i32
@@ -109,9 +114,32 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def make_desc(T, N, H, d_k, d_v, num_slots, io_dtype, scale=1.0) -> PrefillDesc:
+def make_desc(T, N, H, d_k, d_v, num_slots, io_dtype, scale=1.0, slot_stride=0,
+              head_stride=0) -> PrefillDesc:
     return PrefillDesc(int(T), int(N), int(H), int(d_k), int(d_v), int(num_slots),
-                       int(io_dtype), float(scale))
+                       int(io_dtype), float(scale), int(slot_stride), int(head_stride))
+
+
+def line_extent(num_slots, H, d_k, d_v, slot_stride, head_stride) -> int:
+    """fp32 elements a pool addressed by lines must hold (kda.h, "State
+    addressing by lines")."""
+    hs = head_stride or d_k * d_v
+    ss = slot_stride or H * hs
+    return (num_slots - 1) * ss + (H - 1) * hs + d_k * d_v
+
+
+def _check_pool(p, name, num_slots, H, dk, dv, slot_stride, head_stride):
+    """Dense pools are [num_slots, H, d_v, d_k]; pools addressed by lines are
+    any contiguous fp32 tensor holding line_extent(...) elements."""
+    if p is None:
+        return
+    if slot_stride or head_stride:
+        _dev(p, name, torch.float32)
+        need = line_extent(num_slots, H, dk, dv, slot_stride, head_stride)
+        if p.numel() < need:
+            raise ValueError("%s holds %d fp32 elements, the lines need %d" % (name, p.numel(), need))
+    else:
+        _dev(p, name, torch.float32, (num_slots, H, dv, dk))
 
 
 def prefill_workspace_size(T, N, H, d_k, d_v, dtype=torch.bfloat16) -> int:
@@ -121,13 +149,16 @@ def prefill_workspace_size(T, N, H, d_k, d_v, dtype=torch.bfloat16) -> int:
 
 def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o=None,
                   slots=None, num_slots=None, scale=1.0, workspace=None, stream=None,
-                  events=None):
+                  events=None, state_slot_stride=0, state_head_stride=0):
     """KDA chunked prefill over packed sequences (see ``kda_chunk_prefill``).
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype); g: [T, H, d_k]
     fp32; beta: [T, H] fp32; cu_seqlens: [N+1] int32 (device); state_in /
     state_out: [num_slots, H, d_v, d_k] fp32 pools or None (may be the same
-    tensor); slots: [N] int32 or None.  events: optional three recorded
+    tensor); slots: [N] int32 or None.  With state_slot_stride /
+    state_head_stride (fp32 elements, kda.h "State addressing by lines") the
+    pools are flat fp32 buffers and num_slots must be given.  events: optional
+    three recorded
     torch.cuda.Event(enable_timing=True) objects, recorded before the
     intra-chunk kernel, between the kernels and after the scan
     (``kda_chunk_prefill_timed``).  Returns o [T, H, d_v].
@@ -144,15 +175,18 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
     _dev(cu_seqlens, "cu_seqlens", torch.int32)
     N = cu_seqlens.shape[0] - 1
     pools = [p for p in (state_in, state_out) if p is not None]
+    lines = bool(state_slot_stride or state_head_stride)
     if num_slots is None:
+        if lines and pools:
+            raise ValueError("num_slots is required for pools addressed by lines")
         num_slots = pools[0].shape[0] if pools else N
     for name, p in (("state_in", state_in), ("state_out", state_out)):
-        _dev(p, name, torch.float32, (num_slots, H, dv, dk) if p is not None else None)
+        _check_pool(p, name, num_slots, H, dk, dv, state_slot_stride, state_head_stride)
     _dev(slots, "slots", torch.int32, (N,) if slots is not None else None)
     if o is None:
         o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     _dev(o, "o", q.dtype, (T, H, dv))
-    desc = make_desc(T, N, H, dk, dv, num_slots, io, scale)
+    desc = make_desc(T, N, H, dk, dv, num_slots, io, scale, state_slot_stride, state_head_stride)
     need = int(lib.kda_prefill_workspace_size(ctypes.byref(desc)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -178,10 +212,14 @@ def _event_handle(ev) -> int:
     return h
 
 
-def decode_step(q, k, v, g, beta, state_pool, slots, o=None, scale=1.0, stream=None):
+def decode_step(q, k, v, g, beta, state_pool, slots, o=None, scale=1.0, stream=None,
+                num_slots=None, state_slot_stride=0, state_head_stride=0):
     """One token per sequence; state_pool [num_slots, H, d_v, d_k] updated in
     place (see ``kda_decode_step``).  q, k, g: [N, H, d_k]; v: [N, H, d_v];
-    beta: [N, H]; slots: [N] int32.  Returns o [N, H, d_v]."""
+    beta: [N, H]; slots: [N] int32.  With state_slot_stride /
+    state_head_stride the pool is a flat fp32 buffer addressed by lines
+    (``kda_decode_step_lines``) and num_slots must be given.  Returns o
+    [N, H, d_v]."""
     lib = load_library()
     _dev(q, "q")
     N, H, dk = q.shape
@@ -192,13 +230,18 @@ def decode_step(q, k, v, g, beta, state_pool, slots, o=None, scale=1.0, stream=N
     _dev(g, "g", torch.float32, (N, H, dk))
     _dev(beta, "beta", torch.float32, (N, H))
     _dev(state_pool, "state_pool", torch.float32)
-    num_slots = state_pool.shape[0]
-    _dev(state_pool, "state_pool", torch.float32, (num_slots, H, dv, dk))
+    lines = bool(state_slot_stride or state_head_stride)
+    if num_slots is None:
+        if lines:
+            raise ValueError("num_slots is required for a pool addressed by lines")
+        num_slots = state_pool.shape[0]
+    _check_pool(state_pool, "state_pool", num_slots, H, dk, dv, state_slot_stride, state_head_stride)
     _dev(slots, "slots", torch.int32, (N,))
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     _dev(o, "o", q.dtype, (N, H, dv))
-    _check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
-                               _ptr(slots), _ptr(o), N, H, dk, dv, num_slots, io, float(scale),
-                               _stream(stream)))
+    _check(lib.kda_decode_step_lines(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(state_pool), _ptr(slots), _ptr(o), N, H, dk, dv,
+                                     num_slots, io, float(scale), int(state_slot_stride),
+                                     int(state_head_stride), _stream(stream)))
     return o

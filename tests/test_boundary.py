@@ -33,7 +33,8 @@ def _declared_functions():
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for n in ("kda_chunk_prefill", "kda_decode_step", "kda_prefill_workspace_size",
-              "kda_status_string", "kda_version", "kda_chunk_prefill_timed"):
+              "kda_status_string", "kda_version", "kda_chunk_prefill_timed",
+              "kda_decode_step_lines"):
         assert n in names
 
 
@@ -43,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 100
+    assert lib.kda_version() == 101
     for code in range(8):
         s = lib.kda_status_string(code).decode()
         assert s and s != "unknown status"
@@ -51,9 +52,10 @@ def test_version_and_status_strings(lib):
 
 
 def _desc(**kw):
-    d = dict(T=8192, N=16, H=32, dk=128, dv=128, slots=64, io=K.KDA_BF16, scale=1.0)
+    d = dict(T=8192, N=16, H=32, dk=128, dv=128, slots=64, io=K.KDA_BF16, scale=1.0, ss=0, hs=0)
     d.update(kw)
-    return K.make_desc(d["T"], d["N"], d["H"], d["dk"], d["dv"], d["slots"], d["io"], d["scale"])
+    return K.make_desc(d["T"], d["N"], d["H"], d["dk"], d["dv"], d["slots"], d["io"], d["scale"],
+                       d["ss"], d["hs"])
 
 
 def _ws_formula(T, N, H, dk, dv, es):
@@ -106,9 +108,32 @@ def test_prefill_rejects_bad_arguments(lib):
     assert _prefill(lib, d, ws_bytes=need - 1) == 5
 
 
+def test_prefill_rejects_bad_line_strides(lib):
+    blk = 128 * 128
+    assert _prefill(lib, _desc(hs=blk - 4)) == 2                      # heads would overlap
+    assert _prefill(lib, _desc(hs=blk + 2)) == 2                      # not a multiple of 4
+    assert _prefill(lib, _desc(ss=31 * blk + blk - 4)) == 2           # lines would overlap
+    assert _prefill(lib, _desc(ss=32 * blk + 2)) == 2                 # not a multiple of 4
+    assert _prefill(lib, _desc(hs=blk + 576, ss=31 * (blk + 576) + blk - 4)) == 2
+    assert _prefill(lib, _desc(ss=-32 * blk)) == 2
+
+
 def _decode(lib, q=A, k=A, v=A, g=A, beta=A, pool=A, slots=A, o=A, N=64, H=32, dk=128, dv=128,
             ns=64, io=K.KDA_BF16):
     return lib.kda_decode_step(q, k, v, g, beta, pool, slots, o, N, H, dk, dv, ns, io, 1.0, None)
+
+
+def _decode_lines(lib, ss, hs, N=64, H=32, dk=128, dv=128, ns=64):
+    return lib.kda_decode_step_lines(A, A, A, A, A, A, A, A, N, H, dk, dv, ns, K.KDA_BF16, 1.0,
+                                     ss, hs, None)
+
+
+def test_decode_lines_rejects_bad_strides(lib):
+    blk = 128 * 128
+    assert _decode_lines(lib, 0, blk - 4) == 2
+    assert _decode_lines(lib, 0, blk + 2) == 2
+    assert _decode_lines(lib, 31 * blk + blk - 4, 0) == 2
+    assert _decode_lines(lib, 32 * blk + 6, 0) == 2
 
 
 def test_decode_rejects_bad_arguments(lib):

@@ -1,0 +1,181 @@
+"""Parity of state pools addressed by lines (kda.h, "State addressing by
+lines"; the kern-k3-pp-prefill page, section "D inside vLLM": a KDA line at
+the start of each hybrid page, the line stride being the one launch parameter
+that changes).
+
+Each slot's line starts at a page boundary; between heads sits a gap the size
+of a 3-tap bf16 conv window over q, k, v at d = 128 (3 * 3 * 128 * 2 bytes =
+576 fp32 words), and the page has room after the line.  The hybrid-page test
+takes the page's own geometry: a 884,736-byte page (221,184 fp32 words) per
+slot and 12 heads of 67,840 bytes each (the "kern" page's KDA state of
+19,537,920 bytes per sequence is 288 such blocks; one 12-head line of 814,080
+bytes fits a page).  Gaps and unnamed slots hold a sentinel that must survive
+byte for byte; states are compared with the oracle run on the same dense pool.
+"""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_prefill_amd import workloads as W
+from oracle import oracle
+from kda_testlib import TOL, announce, dev, oracle_prefill, per_sequence_errors, rel_err, torch_dtype
+import linear_attention_prefill_amd as lap
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+GAP = 576          # fp32 words between heads of a line
+PAGE_TAIL = 1000   # fp32 words after a line, before the next page
+
+
+HYBRID_PAGE = 884736 // 4      # fp32 words per page
+HYBRID_HEAD = 67840 // 4       # fp32 words per head of a line (state + conv window)
+
+
+def strides(H, dk, dv):
+    hs = dk * dv + GAP
+    ss = H * hs + PAGE_TAIL
+    return ss, hs
+
+
+def pack(pool, ss, hs, fill):
+    """Dense [S][H][d_v][d_k] pool -> flat buffer of lines, gaps = fill."""
+    S, H, dv, dk = pool.shape
+    flat = np.full(lap.line_extent(S, H, dk, dv, ss, hs), fill, dtype=np.float32)
+    for s in range(S):
+        for h in range(H):
+            o = s * ss + h * hs
+            flat[o:o + dv * dk] = pool[s, h].reshape(-1)
+    return flat
+
+
+def unpack(flat, S, H, dk, dv, ss, hs):
+    pool = np.empty((S, H, dv, dk), dtype=np.float32)
+    for s in range(S):
+        for h in range(H):
+            o = s * ss + h * hs
+            pool[s, h] = flat[o:o + dv * dk].reshape(dv, dk)
+    return pool
+
+
+def gap_mask(S, H, dk, dv, ss, hs):
+    m = np.ones(lap.line_extent(S, H, dk, dv, ss, hs), dtype=bool)
+    for s in range(S):
+        for h in range(H):
+            o = s * ss + h * hs
+            m[o:o + dv * dk] = False
+    return m
+
+
+@pytest.mark.parametrize("dk,dv,io,in_place", [(128, 128, "bf16", True), (64, 128, "f32", True),
+                                               (128, 64, "bf16", False)])
+def test_prefill_with_line_addressed_pools(dk, dv, io, in_place):
+    c = W.random_case(61 + dk + dv, [70, 0, 129, 5, 64], H=3, d_k=dk, d_v=dv, io_dtype=io,
+                      num_slots=7, slots=[5, 2, -1, 0, 6])
+    S, H = c.state_pool.shape[0], c.H
+    ss, hs = strides(H, dk, dv)
+    fill = np.float32(-7.25)
+    flat_in = pack(c.state_pool, ss, hs, fill)
+    dt = torch_dtype(io)
+    pin = dev(flat_in)
+    pout = pin if in_place else dev(np.full_like(flat_in, fill))
+    o_init = np.full((c.T, c.H, c.d_v), 3.0, dtype=np.float32)
+    o = dev(o_init, dt)
+    announce("prefill lines %s in_place=%s" % (c.name, in_place))
+    lap.chunk_prefill(dev(c.q, dt), dev(c.k, dt), dev(c.v, dt), dev(c.g), dev(c.beta),
+                      dev(c.cu_seqlens), state_in=pin, state_out=pout, o=o, slots=dev(c.slots),
+                      num_slots=S, scale=c.scale, state_slot_stride=ss, state_head_stride=hs)
+    torch.cuda.synchronize()
+    flat_out = pout.cpu().numpy()
+    o_g = o.float().cpu().numpy()
+    o_r, pool_r, _ = oracle_prefill(c, o_init=o_init)
+    pool_g = unpack(flat_out, S, H, dk, dv, ss, hs)
+    live = (c.slots >= 0) & (c.slots < S)
+    eo, es = per_sequence_errors(c, o_g, o_r, pool_g, pool_r, live=live)
+    assert eo <= TOL[io] and es <= TOL[io], (eo, es)
+    gaps = gap_mask(S, H, dk, dv, ss, hs)
+    np.testing.assert_array_equal(flat_out[gaps], np.full(gaps.sum(), fill, dtype=np.float32))
+    named = set(int(s) for s in c.slots[live])
+    ref_unnamed = c.state_pool if in_place else np.full_like(c.state_pool, fill)
+    for s in range(S):
+        if s not in named:
+            np.testing.assert_array_equal(pool_g[s], ref_unnamed[s])
+    # the padded sequence's o rows keep their sentinel
+    cu = c.cu_seqlens
+    assert np.all(o_g[cu[2]:cu[3]] == 3.0)
+
+
+@pytest.mark.parametrize("dk,dv,io", [(128, 128, "bf16"), (64, 64, "f32")])
+def test_decode_with_line_addressed_pool(dk, dv, io):
+    c = W.random_case(71 + dk, [1] * 6, H=4, d_k=dk, d_v=dv, io_dtype=io, num_slots=9,
+                      slots=[8, -1, 0, 3, 9, 5], scale=0.8)
+    S, H = c.state_pool.shape[0], c.H
+    ss, hs = strides(H, dk, dv)
+    fill = np.float32(11.5)
+    flat = dev(pack(c.state_pool, ss, hs, fill))
+    dt = torch_dtype(io)
+    o = torch.full((c.N, c.H, c.d_v), 5.0, dtype=dt, device="cuda")
+    announce("decode lines %s" % c.name)
+    lap.decode_step(dev(c.q, dt), dev(c.k, dt), dev(c.v, dt), dev(c.g), dev(c.beta), flat,
+                    dev(c.slots), o=o, scale=c.scale, num_slots=S, state_slot_stride=ss,
+                    state_head_stride=hs)
+    torch.cuda.synchronize()
+    flat_g = flat.cpu().numpy()
+    pool_g = unpack(flat_g, S, H, dk, dv, ss, hs)
+    o_g = o.float().cpu().numpy()
+    o_r, pool_r = oracle.decode_step(c.q, c.k, c.v, c.g, c.beta, c.state_pool, c.slots,
+                                     scale=c.scale, o_init=np.full((c.N, c.H, c.d_v), 5.0))
+    for n in range(c.N):
+        s = int(c.slots[n])
+        if 0 <= s < S:
+            assert rel_err(o_g[n], o_r[n]) <= TOL[io]
+            assert rel_err(pool_g[s], pool_r[s]) <= TOL[io]
+        else:
+            assert np.all(o_g[n] == 5.0)
+    gaps = gap_mask(S, H, dk, dv, ss, hs)
+    np.testing.assert_array_equal(flat_g[gaps], np.full(gaps.sum(), fill, dtype=np.float32))
+    used = set(int(s) for s in c.slots)
+    for s in range(S):
+        if s not in used:
+            np.testing.assert_array_equal(pool_g[s], c.state_pool[s])
+
+
+def test_hybrid_page_geometry():
+    """12 heads at d = 128 on 884,736-byte pages: prefill into some pages,
+    then decode from them, both addressed by lines."""
+    H, d = 12, 128
+    ss, hs = HYBRID_PAGE, HYBRID_HEAD
+    assert hs == d * d + GAP and (H - 1) * hs + d * d <= ss
+    c = W.random_case(91, [300, 64, 1, 0], H=H, d_k=d, d_v=d, io_dtype="bf16", num_slots=6,
+                      slots=[4, 0, 5, 2])
+    S = c.state_pool.shape[0]
+    fill = np.float32(-2.5)
+    pool = dev(pack(c.state_pool, ss, hs, fill))
+    announce("prefill hybrid pages %s" % c.name)
+    o = torch.zeros((c.T, H, d), dtype=torch.bfloat16, device="cuda")
+    lap.chunk_prefill(dev(c.q, torch.bfloat16), dev(c.k, torch.bfloat16), dev(c.v, torch.bfloat16),
+                      dev(c.g), dev(c.beta), dev(c.cu_seqlens), state_in=pool, state_out=pool, o=o,
+                      slots=dev(c.slots), num_slots=S, scale=c.scale, state_slot_stride=ss,
+                      state_head_stride=hs)
+    torch.cuda.synchronize()
+    o_r, pool_r, _ = oracle_prefill(c)
+    pool_g = unpack(pool.cpu().numpy(), S, H, d, d, ss, hs)
+    eo, es = per_sequence_errors(c, o.float().cpu().numpy(), o_r, pool_g, pool_r)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
+    # one decode token for the four live sequences, from the pages just written;
+    # the oracle chains its own prefill result
+    dc = W.random_case(92, [1] * 4, H=H, d_k=d, d_v=d, io_dtype="bf16", num_slots=S,
+                       slots=list(c.slots))
+    od = torch.zeros((4, H, d), dtype=torch.bfloat16, device="cuda")
+    announce("decode hybrid pages %s" % dc.name)
+    lap.decode_step(dev(dc.q, torch.bfloat16), dev(dc.k, torch.bfloat16), dev(dc.v, torch.bfloat16),
+                    dev(dc.g), dev(dc.beta), pool, dev(dc.slots), o=od, scale=dc.scale,
+                    num_slots=S, state_slot_stride=ss, state_head_stride=hs)
+    torch.cuda.synchronize()
+    flat = pool.cpu().numpy()
+    od_r, pool_r2 = oracle.decode_step(dc.q, dc.k, dc.v, dc.g, dc.beta, pool_r, dc.slots,
+                                       scale=dc.scale)
+    assert rel_err(od.float().cpu().numpy(), od_r) <= TOL["bf16"]
+    assert rel_err(unpack(flat, S, H, d, d, ss, hs), pool_r2) <= TOL["bf16"]
+    gaps = gap_mask(S, H, d, d, ss, hs)
+    np.testing.assert_array_equal(flat[gaps], np.full(gaps.sum(), fill, dtype=np.float32))
