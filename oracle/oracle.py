@@ -175,3 +175,44 @@ def decode_step(q, k, v, g, beta, state_pool, slots, scale=1.0, o_init=None, thr
     o, pool_out, _ = chunk_prefill(q, k, v, g, beta, cu, state_pool=state_pool, slots=slots,
                                    scale=scale, o_init=o_init, threads=threads)
     return o, pool_out
+
+
+def decode_tokens(q, k, v, g, beta, state_pool, slots, num_accepted=None, commit=True, scale=1.0,
+                  o_init=None, threads=None):
+    """T tokens per sequence against one state: multi-token decode, and the
+    verify and commit of speculative tokens (the prhub report on SGLang PR
+    #32890, section "关键文件": the conv-MTP decode kernel's multi-token
+    verify, and ReplaySSM's exact fold of the accepted tokens at commit).
+
+    q, k, g: [N, T, H, d_k]; v: [N, T, H, d_v]; beta: [N, T, H]; state_pool
+    [num_slots, H, d_v, d_k]; slots [N] (padded rows as in decode_step).
+    Every token's output is the recurrence's output over the sequence's
+    tokens 0..t from its slot's state, i.e. what t + 1 decode steps give.
+    With commit, the slot's state becomes the state after the first c_n
+    tokens, c_n = num_accepted[n] clamped to [0, T] (T when None); c_n = 0
+    and commit=False leave it unchanged.
+    Returns (o [N,T,H,d_v] fp64, pool_out fp64).
+    """
+    N, T, H, dk = np.shape(k)
+    dv = np.shape(v)[3]
+
+    def rows(x, d=None):
+        x = np.asarray(x)
+        return x.reshape((N * T, H) if d is None else (N * T, H, d))
+
+    cu = np.arange(0, N * T + 1, T, dtype=np.int32)
+    oi = None if o_init is None else rows(o_init, dv)
+    o, _, _ = chunk_prefill(rows(q, dk), rows(k, dk), rows(v, dv), rows(g, dk), rows(beta), cu,
+                            state_pool=state_pool, slots=slots, scale=scale, o_init=oi,
+                            threads=threads)
+    pool_out = _f64(state_pool).copy()
+    if commit:
+        c = np.full(N, T, dtype=np.int64) if num_accepted is None else \
+            np.clip(np.asarray(num_accepted, dtype=np.int64), 0, T)
+        keep = np.concatenate([n * T + np.arange(c[n]) for n in range(N)]).astype(np.int64)
+        cu_c = np.concatenate([[0], np.cumsum(c)]).astype(np.int32)
+        _, pool_out, _ = chunk_prefill(rows(q, dk)[keep], rows(k, dk)[keep], rows(v, dv)[keep],
+                                       rows(g, dk)[keep], rows(beta)[keep], cu_c,
+                                       state_pool=state_pool, slots=slots, scale=scale,
+                                       threads=threads)
+    return o.reshape(N, T, H, dv), pool_out

@@ -298,3 +298,49 @@ def test_decode_is_one_recurrence_step():
             St = St + np.outer(kk, d)
             np.testing.assert_allclose(o[n, h], St.T @ c.q[n, h], rtol=1e-12, atol=1e-13)
             np.testing.assert_allclose(pool_out[c.slots[n], h], St.T, rtol=1e-12, atol=1e-13)
+
+
+def test_decode_tokens_against_literal_products():
+    """Multi-token decode: each token's output, and the state committed after
+    the first c_n accepted tokens, against explicit matrix products; padded
+    rows and unnamed slots stay untouched; a verify (no commit) leaves the
+    pool as it was."""
+    rng = np.random.default_rng(23)
+    N, T, H, dk, dv, S = 5, 4, 2, 6, 5, 8
+    q, k, v, g, beta = _rand_inputs(rng, N * T, H, dk, dv)
+    pool = 0.3 * rng.standard_normal((S, H, dv, dk))
+    slots = np.array([6, -1, 0, 3, 8], dtype=np.int32)     # -1 and 8 are padded rows
+    acc = np.array([4, 2, 0, 1, 3], dtype=np.int32)
+    shape4 = lambda x: x.reshape((N, T) + x.shape[1:])
+    o_init = np.full((N, T, H, dv), 9.0)
+    args = [shape4(x) for x in (q, k, v, g, beta)]
+    o, pool_out = oracle.decode_tokens(*args, pool, slots, num_accepted=acc, o_init=o_init)
+    for n in range(N):
+        s = int(slots[n])
+        if not 0 <= s < S:
+            np.testing.assert_array_equal(o[n], o_init[n])
+            continue
+        r = slice(n * T, (n + 1) * T)
+        o_l, _ = _literal(q[r], k[r], v[r], g[r], beta[r], [0, T], pool[s][None])
+        np.testing.assert_allclose(o[n], o_l, rtol=1e-11, atol=1e-12)
+        c = slice(n * T, n * T + int(acc[n]))
+        _, s_l = _literal(q[c], k[c], v[c], g[c], beta[c], [0, int(acc[n])], pool[s][None])
+        np.testing.assert_allclose(pool_out[s], s_l[0], rtol=1e-11, atol=1e-12)
+    for s in (1, 2, 4, 5, 7):
+        np.testing.assert_array_equal(pool_out[s], pool[s])
+    o2, pool2 = oracle.decode_tokens(*args, pool, slots, commit=False, o_init=o_init)
+    np.testing.assert_array_equal(o2, o)
+    np.testing.assert_array_equal(pool2, pool)
+    # all tokens committed when no counts are given
+    _, pool3 = oracle.decode_tokens(*args, pool, slots)
+    _, s_all = _literal(q[:T], k[:T], v[:T], g[:T], beta[:T], [0, T], pool[6][None])
+    np.testing.assert_allclose(pool3[6], s_all[0], rtol=1e-11, atol=1e-12)
+
+
+def test_decode_tokens_single_token_is_decode_step():
+    c = W.random_case(24, [1] * 5, H=3, d_k=8, d_v=4, io_dtype="f32", num_slots=7)
+    o1, p1 = oracle.decode_step(c.q, c.k, c.v, c.g, c.beta, c.state_pool, c.slots)
+    o2, p2 = oracle.decode_tokens(c.q[:, None], c.k[:, None], c.v[:, None], c.g[:, None],
+                                  c.beta[:, None], c.state_pool, c.slots)
+    np.testing.assert_array_equal(o2[:, 0], o1)
+    np.testing.assert_array_equal(p2, p1)
