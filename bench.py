@@ -195,6 +195,48 @@ def time_decode(case, steps, warmup, copies, torch, lap):
             "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def time_decode_tokens(case, steps, warmup, copies, torch, lap, only=None):
+    """Multi-token decode: fused verify + commit of all tokens, a verify alone
+    (state only read) and a commit alone (no outputs); `only` times one."""
+    dt = torch.bfloat16
+    N, T = case.N, case.meta["tokens"]
+    r = lambda x: torch.from_numpy(x.reshape((N, T) + x.shape[1:])).to("cuda")
+    q, k, v = r(case.q).to(dt), r(case.k).to(dt), r(case.v).to(dt)
+    g, beta = r(case.g), r(case.beta)
+    slots = torch.from_numpy(case.slots).to("cuda")
+    pools = [torch.from_numpy(case.state_pool).to("cuda") for _ in range(copies)]
+    o = torch.empty((N, T, case.H, case.d_v), dtype=dt, device="cuda")
+    modes = {"verify_commit": dict(commit=True, outputs=True),
+             "verify": dict(commit=False, outputs=True),
+             "commit": dict(commit=True, outputs=False)}
+    state = case.H * case.d_k * case.d_v * 4
+    tok_in = case.H * (2 * case.d_k * 2 + case.d_v * 2 + case.d_k * 4 + 4)
+    res = {"tokens": T}
+    for name, kw in modes.items():
+        if only and name != only:
+            continue
+        def run(i):
+            lap.decode_tokens(q, k, v, g, beta, pools[i % copies], slots,
+                              o=o if kw["outputs"] else None, **kw)
+        for i in range(warmup):
+            run(i)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            run(i)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        nbytes = N * (state * (2 if kw["commit"] else 1)
+                      + T * (tok_in - (0 if kw["outputs"] else case.H * case.d_k * 2))
+                      + (T * case.H * case.d_v * 2 if kw["outputs"] else 0))
+        res[name] = {"us": ms * 1e3, "bytes": nbytes, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                     "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "tokens/s": N * T / (ms * 1e-3)}
+    return res
+
+
 def cpu_baseline(case, seconds):
     """The fp64 oracle on the same inputs, repeated until `seconds` elapse
     (a bounded sample; heads are subsampled if one call would take longer)."""
@@ -242,10 +284,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["single", "packed", "decode"], default="single",
+    ap.add_argument("--workload", choices=["single", "packed", "decode", "decode_tokens"],
+                    default="single",
                     help="single: 1 x 8192 rows (default); packed: 16 sequences in 8192 rows; "
-                         "decode: 64 sequences x 1 token (profiling the decode kernel)")
+                         "decode: 64 sequences x 1 token (profiling the decode kernel); "
+                         "decode_tokens: 64 sequences x 4 draft tokens (multi-token decode)")
     ap.add_argument("--copies", type=int, default=3, help="rotated device copies of the inputs")
+    ap.add_argument("--tokens-mode", choices=["verify_commit", "verify", "commit"], default=None,
+                    help="decode_tokens workload: time only this mode (default: all three)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
@@ -280,6 +326,23 @@ def main():
                "roofline": {"bound": "hbm", "achieved": rd["GB/s"], "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": rd["frac_hbm"], "traffic": None,
                             "kernel": "kda_decode_kernel"}}
+        print(json.dumps(out), flush=True)
+        return
+    if args.workload == "decode_tokens":
+        mc = W.decode_tokens_case()
+        rm = time_decode_tokens(mc, args.steps, args.warmup, 4, torch, lap, args.tokens_mode)
+        f = rm[args.tokens_mode or "verify_commit"]
+        out = {"metric": "KDA multi-token decode (%s): draft tokens per second on 1 MI355X"
+                         % (args.tokens_mode or "verify_commit"),
+               "value": f["tokens/s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+               "warmup": args.warmup, "ms_per_step": f["us"] * 1e-3, "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+               "config": {"workload": mc.name, "num_seqs": mc.N, "tokens": rm["tokens"],
+                          "heads": mc.H, "d_k": mc.d_k, "d_v": mc.d_v, "pools_rotated": 4},
+               "roofline": {"bound": "hbm", "achieved": f["GB/s"], "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": f["frac_hbm"], "traffic": None,
+                            "kernel": "kda_decode_tokens_kernel"},
+               "modes": rm}
         print(json.dumps(out), flush=True)
         return
 
@@ -352,6 +415,13 @@ def main():
         rd["workload"] = dc.name
         extra["decode"] = rd
         log("decode %.1f us, %.0f GB/s" % (rd["us"], rd["GB/s"]))
+        mc = W.decode_tokens_case()
+        rm = time_decode_tokens(mc, max(10, args.steps), 3, 4, torch, lap)
+        rm["workload"] = mc.name
+        extra["decode_tokens"] = rm
+        log("decode_tokens T=%d: verify+commit %.1f us (%.0f GB/s), verify %.1f us, commit %.1f us"
+            % (rm["tokens"], rm["verify_commit"]["us"], rm["verify_commit"]["GB/s"],
+               rm["verify"]["us"], rm["commit"]["us"]))
         out["extra"] = extra
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4

@@ -192,6 +192,44 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
                              int32_t d_k, int32_t d_v, int32_t num_slots,
                              int32_t io_dtype, float scale, void *stream);
 
+/*
+ * Multi-token decode and speculative verify / commit: T = num_tokens tokens
+ * per sequence against one state (the prhub report on SGLang PR #32890,
+ * section "关键文件": the conv-MTP decode kernel, which runs a multi-token
+ * verify beside the single-token step, and ReplaySSM, which keeps a small
+ * per-request window of inputs and folds the accepted tokens into the state
+ * exactly at commit instead of snapshotting states, bit-consistent with the
+ * recurrent step).
+ *   q, k, g [N T][H][d_k]; v, o [N T][H][d_v]; beta [N T][H]: row n T + t is
+ *   token t of sequence n.  state_pool, slots and the state strides are as
+ *   for kda_decode_step_lines (a slot outside [0, num_slots) is a padded
+ *   sequence: nothing of it is read or written).
+ *   o: if not NULL, o[n T + t] is token t's output after tokens 0..t, as T
+ *   consecutive kda_decode_step calls would give it.  q may be NULL only when
+ *   o is NULL.
+ *   commit = 0: the state is only read (verify).  commit != 0: the state
+ *   after the first c_n tokens is written back, c_n = num_accepted[n] clamped
+ *   to [0, T], or T when num_accepted is NULL; c_n = 0 leaves the slot
+ *   untouched.  num_accepted is [N] int32 on the device or NULL.
+ * The committed state and every output equal, bit for bit, those of c_n
+ * (respectively t + 1) consecutive kda_decode_step calls on the same tokens.
+ * So a verify call (commit = 0) followed, once the accepted counts are known,
+ * by a commit call (o = q = NULL, commit = 1, num_accepted) on the same k, v,
+ * g, beta window leaves the state that the accepted tokens alone give.
+ * Errors as for kda_decode_step_lines, plus KDA_ERR_SHAPE for num_tokens
+ * outside [1, 16] and KDA_ERR_NULL when o is NULL and commit = 0 (nothing to
+ * do) or when o is given without q.
+ */
+kda_status_t kda_decode_tokens(const void *q, const void *k, const void *v,
+                               const float *g, const float *beta,
+                               float *state_pool, const int32_t *slots, void *o,
+                               const int32_t *num_accepted,
+                               int32_t num_seqs, int32_t num_tokens, int32_t num_heads,
+                               int32_t d_k, int32_t d_v, int32_t num_slots,
+                               int32_t io_dtype, float scale, int32_t commit,
+                               int64_t state_slot_stride, int64_t state_head_stride,
+                               void *stream);
+
 /* Static description of a status code. */
 const char *kda_status_string(kda_status_t status);
 

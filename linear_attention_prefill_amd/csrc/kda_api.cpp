@@ -32,6 +32,14 @@ hipError_t dispatch_decode(const kda::DecodeArgs &a, int dk, int dv, hipStream_t
     return kda::launch_decode<E, 128, 128>(a, s);
 }
 
+template <typename E>
+hipError_t dispatch_decode_tokens(const kda::DecodeArgs &a, int dk, int dv, hipStream_t s) {
+    if (dk == 64 && dv == 64) return kda::launch_decode_tokens<E, 64, 64>(a, s);
+    if (dk == 64 && dv == 128) return kda::launch_decode_tokens<E, 64, 128>(a, s);
+    if (dk == 128 && dv == 64) return kda::launch_decode_tokens<E, 128, 64>(a, s);
+    return kda::launch_decode_tokens<E, 128, 128>(a, s);
+}
+
 // Compute units of the current device (persistent grids are sized by it).
 int device_cus() {
     int dev = 0, n = 0;
@@ -162,6 +170,42 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const 
                                  d_v, num_slots, io_dtype, scale, 0, 0, stream);
 }
 
+kda_status_t kda_decode_tokens(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, float *state_pool, const int32_t *slots,
+                               void *o, const int32_t *num_accepted, int32_t num_seqs,
+                               int32_t num_tokens, int32_t num_heads, int32_t d_k, int32_t d_v,
+                               int32_t num_slots, int32_t io_dtype, float scale, int32_t commit,
+                               int64_t state_slot_stride, int64_t state_head_stride,
+                               void *stream) {
+    if (io_dtype != KDA_F32 && io_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (!dims_supported(d_k, d_v)) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs < 1 || num_heads < 1 || num_slots < 1) return KDA_ERR_SHAPE;
+    if (num_tokens < 1 || num_tokens > kda::kMaxDecodeTokens) return KDA_ERR_SHAPE;
+    if ((long long)num_seqs * num_heads * (d_v / 64) > INT_MAX) return KDA_ERR_SHAPE;
+    if ((long long)num_seqs * num_tokens * num_heads > INT_MAX) return KDA_ERR_SHAPE;
+    if (!k || !v || !g || !beta || !state_pool || !slots) return KDA_ERR_NULL;
+    if (!o && !commit) return KDA_ERR_NULL;      // neither outputs nor a commit
+    if (o && !q) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g, beta, state_pool, slots, o, num_accepted};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    int64_t ss = 0, hs = 0;
+    if (!resolve_strides(state_slot_stride, state_head_stride, num_heads, d_k, d_v, &ss, &hs))
+        return KDA_ERR_SHAPE;
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.pool = state_pool; a.slots = slots;
+    a.o = o; a.N = num_seqs; a.H = num_heads; a.num_slots = num_slots; a.scale = scale;
+    a.slot_stride = ss;
+    a.head_stride = hs;
+    a.T = num_tokens;
+    a.accept = num_accepted;
+    a.commit = commit ? 1 : 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = io_dtype == KDA_BF16 ? dispatch_decode_tokens<bf16>(a, d_k, d_v, s)
+                                              : dispatch_decode_tokens<float>(a, d_k, d_v, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 const char *kda_status_string(kda_status_t status) {
     switch (status) {
         case KDA_OK: return "ok";
@@ -176,6 +220,6 @@ const char *kda_status_string(kda_status_t status) {
     return "unknown status";
 }
 
-int32_t kda_version(void) { return 101; }
+int32_t kda_version(void) { return 102; }
 
 }  // extern "C"

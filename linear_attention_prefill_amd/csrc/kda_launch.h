@@ -23,6 +23,9 @@ struct PrefillArgs {
     hipEvent_t events[3];   // optional: before intra, between, after scan
 };
 
+// Most tokens a multi-token decode call may carry per sequence.
+constexpr int kMaxDecodeTokens = 16;
+
 struct DecodeArgs {
     const void *q, *k, *v;
     const float *g, *beta;
@@ -32,6 +35,9 @@ struct DecodeArgs {
     int N, H, num_slots;
     float scale;
     int64_t slot_stride, head_stride;   // state addressing, fp32 elements (resolved)
+    int T = 1;                          // tokens per sequence (multi-token decode)
+    const int32_t *accept = nullptr;    // tokens to commit per sequence, or NULL = T
+    int commit = 1;                     // 0: state is only read
 };
 
 template <typename E, int DK, int DV>
@@ -39,6 +45,9 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 template <typename E, int DK, int DV>
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+template <typename E, int DK, int DV>
+hipError_t launch_decode_tokens(const DecodeArgs &a, hipStream_t stream);
 
 size_t prefill_workspace_bytes(int T, int N, int H, int dk, int dv, bool bf16);
 

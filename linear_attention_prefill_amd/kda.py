@@ -67,6 +67,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_decode_step_lines.restype = ctypes.c_int
     lib.kda_decode_step_lines.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                           i32, i32, i32, i32, i32, i32, f32, i64, i64, vp]
+    lib.kda_decode_tokens.restype = ctypes.c_int
+    lib.kda_decode_tokens.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      i32, i32, i32, i32, i32, i32, i32, f32, i32, i64, i64, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_version.restype = i32
@@ -244,4 +247,48 @@ def decode_step(q, k, v, g, beta, state_pool, slots, o=None, scale=1.0, stream=N
                                      _ptr(state_pool), _ptr(slots), _ptr(o), N, H, dk, dv,
                                      num_slots, io, float(scale), int(state_slot_stride),
                                      int(state_head_stride), _stream(stream)))
+    return o
+
+
+def decode_tokens(q, k, v, g, beta, state_pool, slots, o=None, num_accepted=None, commit=True,
+                  outputs=True, scale=1.0, stream=None, num_slots=None, state_slot_stride=0,
+                  state_head_stride=0):
+    """T tokens per sequence against one state (see ``kda_decode_tokens``).
+
+    k, g: [N, T, H, d_k]; v: [N, T, H, d_v]; beta: [N, T, H]; q: [N, T, H, d_k]
+    (may be None when outputs is False); slots: [N] int32; num_accepted: [N]
+    int32 or None.  commit=False only reads the state (verify); commit=True
+    writes back the state after num_accepted[n] tokens (all T when None).
+    outputs=False skips the outputs (a commit of a verified window).  Returns
+    o [N, T, H, d_v], or None when outputs is False."""
+    lib = load_library()
+    _dev(k, "k")
+    N, T, H, dk = k.shape
+    dv = v.shape[3]
+    io = _io_code(k.dtype)
+    _dev(v, "v", k.dtype, (N, T, H, dv))
+    _dev(g, "g", torch.float32, (N, T, H, dk))
+    _dev(beta, "beta", torch.float32, (N, T, H))
+    if outputs:
+        _dev(q, "q", k.dtype, (N, T, H, dk))
+        if o is None:
+            o = torch.empty((N, T, H, dv), dtype=k.dtype, device=k.device)
+        _dev(o, "o", k.dtype, (N, T, H, dv))
+    else:
+        if q is not None:
+            _dev(q, "q", k.dtype, (N, T, H, dk))
+        o = None
+    _dev(state_pool, "state_pool", torch.float32)
+    lines = bool(state_slot_stride or state_head_stride)
+    if num_slots is None:
+        if lines:
+            raise ValueError("num_slots is required for a pool addressed by lines")
+        num_slots = state_pool.shape[0]
+    _check_pool(state_pool, "state_pool", num_slots, H, dk, dv, state_slot_stride, state_head_stride)
+    _dev(slots, "slots", torch.int32, (N,))
+    _dev(num_accepted, "num_accepted", torch.int32, (N,) if num_accepted is not None else None)
+    _check(lib.kda_decode_tokens(_ptr(q) if outputs else None, _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(state_pool), _ptr(slots), _ptr(o), _ptr(num_accepted), N, T,
+                                 H, dk, dv, num_slots, io, float(scale), 1 if commit else 0,
+                                 int(state_slot_stride), int(state_head_stride), _stream(stream)))
     return o

@@ -234,6 +234,18 @@ def decode_case(seed=5, n=64, H=32, d=128, num_slots=64) -> Case:
                 np.arange(n + 1, dtype=np.int32), "bf16", state_pool=pool, slots=slots)
 
 
+def decode_tokens_case(seed=7, n=64, tokens=4, H=32, d=128, num_slots=64) -> Case:
+    """n sequences x `tokens` draft tokens (rows n * tokens + t), states from a
+    num_slots pool: the multi-token decode / speculative-verify shape."""
+    st = _streams(seed)
+    q, k, v, g, beta = draw_tokens(st[0], n * tokens, H, d, d, "bf16")
+    pool = draw_pool(st[1], num_slots, H, d, d)
+    slots = np.random.default_rng(st[3]).permutation(num_slots)[:n].astype(np.int32)
+    return Case("decode_tokens_N%d_T%d_H%d_d%d_bf16" % (n, tokens, H, d), q, k, v, g, beta,
+                np.arange(0, n * tokens + 1, tokens, dtype=np.int32), "bf16", state_pool=pool,
+                slots=slots, meta={"tokens": tokens})
+
+
 def random_case(seed, lengths, H=2, d_k=64, d_v=64, io_dtype="bf16", num_slots=None,
                 with_state=True, mu_g=0.0, scale=1.0, slots=None, pool_std=0.1) -> Case:
     """A small packed case for sweeps: given per-sequence lengths (zero allowed)."""

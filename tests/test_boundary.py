@@ -34,7 +34,7 @@ def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for n in ("kda_chunk_prefill", "kda_decode_step", "kda_prefill_workspace_size",
               "kda_status_string", "kda_version", "kda_chunk_prefill_timed",
-              "kda_decode_step_lines"):
+              "kda_decode_step_lines", "kda_decode_tokens"):
         assert n in names
 
 
@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 101
+    assert lib.kda_version() == 102
     for code in range(8):
         s = lib.kda_status_string(code).decode()
         assert s and s != "unknown status"
@@ -146,3 +146,24 @@ def test_decode_rejects_bad_arguments(lib):
         assert _decode(lib, **{key: None}) == 1, key
     assert _decode(lib, pool=A + 4) == 4
     assert _decode(lib, o=A + 2) == 4
+
+
+def _tokens(lib, q=A, o=A, acc=None, T=4, commit=1, N=64, H=32, dk=128, dv=128, ns=64, ss=0, hs=0,
+            pool=A, slots=A):
+    return lib.kda_decode_tokens(q, A, A, A, A, pool, slots, o, acc, N, T, H, dk, dv, ns,
+                                 K.KDA_BF16, 1.0, commit, ss, hs, None)
+
+
+def test_decode_tokens_rejects_bad_arguments(lib):
+    assert _tokens(lib, T=0) == 2
+    assert _tokens(lib, T=17) == 2
+    assert _tokens(lib, N=0) == 2
+    assert _tokens(lib, ns=0) == 2
+    assert _tokens(lib, dk=96) == 6
+    assert _tokens(lib, o=None, commit=0) == 1          # nothing to do
+    assert _tokens(lib, q=None) == 1                    # outputs need q
+    assert _tokens(lib, pool=None) == 1
+    assert _tokens(lib, slots=None) == 1
+    assert _tokens(lib, acc=A + 4) == 4
+    assert _tokens(lib, o=A + 2) == 4
+    assert _tokens(lib, hs=128 * 128 - 4) == 2
