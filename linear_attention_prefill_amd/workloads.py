@@ -246,6 +246,30 @@ def decode_tokens_case(seed=7, n=64, tokens=4, H=32, d=128, num_slots=64) -> Cas
                 slots=slots, meta={"tokens": tokens})
 
 
+CONV_TAP_SCALE = (0.1, 0.15, 0.25, 0.5)   # bound on |tap j|; the bounds sum to 1
+
+
+def draw_conv(seed, num_slots, H, d_k, d_v, io_dtype="bf16"):
+    """Synthetic short-conv parameters: taps [H, 4, 2 d_k + d_v] fp32, tap j
+    uniform in +-CONV_TAP_SCALE[j] (so a conv of unit-norm rows stays within
+    unit norm), and a window pool [num_slots, H, 3, 2 d_k + d_v] of raw
+    inputs drawn like tokens (unit-norm q and k rows, N(0, 1) v), rounded to
+    the io dtype."""
+    ss = np.random.SeedSequence([seed, 0xC0])
+    cw, cq, ck, cv = ss.spawn(4)
+    C = 2 * d_k + d_v
+    rng = np.random.default_rng(cw)
+    weight = (rng.uniform(-1.0, 1.0, (H, 4, C)) *
+              np.asarray(CONV_TAP_SCALE)[None, :, None]).astype(np.float32)
+    n = num_slots * 3
+    wq = _l2norm(np.random.default_rng(cq).standard_normal((n, H, d_k)))
+    wk = _l2norm(np.random.default_rng(ck).standard_normal((n, H, d_k)))
+    wv = np.random.default_rng(cv).standard_normal((n, H, d_v))
+    win = np.concatenate([_cast(wq, io_dtype), _cast(wk, io_dtype), _cast(wv, io_dtype)], axis=2)
+    window = win.reshape(num_slots, 3, H, C).transpose(0, 2, 1, 3).copy()
+    return weight, window
+
+
 def random_case(seed, lengths, H=2, d_k=64, d_v=64, io_dtype="bf16", num_slots=None,
                 with_state=True, mu_g=0.0, scale=1.0, slots=None, pool_std=0.1) -> Case:
     """A small packed case for sweeps: given per-sequence lengths (zero allowed)."""

@@ -216,3 +216,101 @@ def decode_tokens(q, k, v, g, beta, state_pool, slots, num_accepted=None, commit
                                        state_pool=state_pool, slots=slots, scale=scale,
                                        threads=threads)
     return o.reshape(N, T, H, dv), pool_out
+
+
+# ---------------------------------------------------------------------------
+# Short conv front end.  The KDA layers of the kern-k3-pp-prefill page run
+# "with per-sequence conv windows and states" (section "P: the packed
+# prefill") and its decode build fuses the conv into the step (section "D:
+# TP8 / EP8 / DCP8"); SGLang keeps the window as [slot][tap][q|k|v] bf16
+# (section "D inside SGLang").  The page's state size (the "kern" page,
+# section "The manifest": 19,537,920 bytes a sequence, 288 blocks of a
+# 64 KiB state plus 3 x 3 x 128 bf16) gives a window of 3 rows.  Reading: the
+# window holds a sequence's 3 most recent raw inputs, so the conv is causal,
+# per channel, of width 4; an optional SiLU follows it.
+
+CONV_WINDOW = 3
+CONV_WIDTH = CONV_WINDOW + 1
+
+
+def silu(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def conv_front(q, k, v, cu_seqlens, weight, window=None, slots=None, num_slots=None,
+               activation="none"):
+    """Causal per-channel conv of width 4 over the channels [q | k | v] of each
+    head, run per sequence from the sequence's conv window.
+
+    q, k: [T, H, d_k]; v: [T, H, d_v]; weight: [H, 4, 2 d_k + d_v], tap j
+    multiplying input x_{t-3+j}; window: [num_slots, H, 3, 2 d_k + d_v] raw
+    inputs, row i holding x_{start-3+i}, or None for zeros.  slots and
+    num_slots as in chunk_prefill; a padded sequence convolves from a zero
+    window and leaves every window untouched.  activation: "none" or "silu".
+    Returns (qc, kc, vc) in fp64 and the window pool after the call (fp64, or
+    None without a window pool): each live sequence's slot then holds its
+    last 3 raw inputs, older window rows filling in for short sequences.
+    """
+    q, k, v, w = _f64(q), _f64(k), _f64(v), _f64(weight)
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    C = 2 * dk + dv
+    if w.shape != (H, CONV_WIDTH, C):
+        raise ValueError("weight must be [H, 4, 2 d_k + d_v]")
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    if num_slots is None:
+        num_slots = N if window is None else np.shape(window)[0]
+    sl = np.arange(N) if slots is None else np.asarray(slots, dtype=np.int64)
+    live = (sl >= 0) & (sl < num_slots)
+    x = np.concatenate([q, k, v], axis=2)                      # [T, H, C]
+    y = np.zeros_like(x)
+    win = None if window is None else _f64(window).copy()
+    for n in range(N):
+        a, b = int(cu[n]), int(cu[n + 1])
+        w0 = win[sl[n]] if (win is not None and live[n]) else np.zeros((H, CONV_WINDOW, C))
+        ext = np.concatenate([w0.transpose(1, 0, 2), x[a:b]], axis=0)   # [L + 3, H, C]
+        for t in range(b - a):
+            acc = np.zeros((H, C))
+            for j in range(CONV_WIDTH):
+                acc += w[:, j, :] * ext[t + j]
+            y[a + t] = acc
+        if win is not None and live[n]:
+            win[sl[n]] = ext[-CONV_WINDOW:].transpose(1, 0, 2)
+    if activation == "silu":
+        y = silu(y)
+    elif activation != "none":
+        raise ValueError("activation must be 'none' or 'silu'")
+    return y[:, :, :dk], y[:, :, dk:2 * dk], y[:, :, 2 * dk:], win
+
+
+def chunk_prefill_conv(q, k, v, g, beta, cu_seqlens, weight, window=None, state_pool=None,
+                       slots=None, scale=1.0, o_init=None, num_slots=None, activation="none",
+                       threads=None):
+    """chunk_prefill on the conv front end's outputs (q, k, v are the raw
+    inputs).  Returns (o, pool_out, s_final, window_out)."""
+    if num_slots is None:
+        if state_pool is not None:
+            num_slots = np.shape(state_pool)[0]
+        elif window is not None:
+            num_slots = np.shape(window)[0]
+    qc, kc, vc, win = conv_front(q, k, v, cu_seqlens, weight, window, slots, num_slots,
+                                 activation)
+    o, pool_out, s_fin = chunk_prefill(qc, kc, vc, g, beta, cu_seqlens, state_pool=state_pool,
+                                       slots=slots, scale=scale, o_init=o_init,
+                                       threads=threads, num_slots=num_slots)
+    return o, pool_out, s_fin, win
+
+
+def decode_step_conv(q, k, v, g, beta, state_pool, slots, weight, window, scale=1.0,
+                     o_init=None, activation="none", threads=None):
+    """decode_step with the conv front end: one token per sequence, state and
+    window pools updated.  Returns (o, pool_out, window_out)."""
+    N = np.shape(q)[0]
+    cu = np.arange(N + 1, dtype=np.int32)
+    qc, kc, vc, win = conv_front(q, k, v, cu, weight, window, slots, np.shape(state_pool)[0],
+                                 activation)
+    o, pool_out = decode_step(qc, kc, vc, g, beta, state_pool, slots, scale=scale,
+                              o_init=o_init, threads=threads)
+    return o, pool_out, win

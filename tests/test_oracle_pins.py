@@ -344,3 +344,93 @@ def test_decode_tokens_single_token_is_decode_step():
                                   c.beta[:, None], c.state_pool, c.slots)
     np.testing.assert_array_equal(o2[:, 0], o1)
     np.testing.assert_array_equal(p2, p1)
+
+
+def _conv_inputs(rng, lengths, H, dk, dv, S):
+    T = int(sum(lengths))
+    q, k, v, g, beta = _rand_inputs(rng, T, H, dk, dv)
+    C = 2 * dk + dv
+    weight = rng.uniform(-1, 1, (H, 4, C)) * np.array([0.1, 0.15, 0.25, 0.5])[None, :, None]
+    window = rng.standard_normal((S, H, 3, C)) * 0.3
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return q, k, v, g, beta, weight, window, cu
+
+
+def test_conv_front_against_numpy_convolve():
+    """Each (sequence, head, channel) is np.convolve of [window; inputs] with
+    the reversed taps ('valid' part); SiLU is x * expit(x)."""
+    from scipy.special import expit
+    rng = np.random.default_rng(31)
+    lengths = [5, 1, 0, 2, 9]
+    H, dk, dv, S = 2, 3, 4, 7
+    q, k, v, g, beta, w, win, cu = _conv_inputs(rng, lengths, H, dk, dv, S)
+    slots = np.array([3, 0, 5, -1, 6], dtype=np.int32)
+    for act in ("none", "silu"):
+        qc, kc, vc, wout = oracle.conv_front(q, k, v, cu, w, win, slots, S, activation=act)
+        y = np.concatenate([qc, kc, vc], axis=2)
+        x = np.concatenate([q, k, v], axis=2)
+        for n in range(len(lengths)):
+            a, b = cu[n], cu[n + 1]
+            s = slots[n]
+            w0 = win[s] if 0 <= s < S else np.zeros((H, 3, 2 * dk + dv))
+            for h in range(H):
+                for c in range(2 * dk + dv):
+                    ext = np.concatenate([w0[h, :, c], x[a:b, h, c]])
+                    ref = np.convolve(ext, w[h, ::-1, c], mode="valid")[:b - a]
+                    if act == "silu":
+                        ref = ref * expit(ref)
+                    np.testing.assert_allclose(y[a:b, h, c], ref, rtol=1e-12, atol=1e-14)
+                    if 0 <= s < S:
+                        np.testing.assert_allclose(wout[s, h, :, c], ext[-3:], rtol=0, atol=0)
+        for s in (1, 2, 4):
+            np.testing.assert_array_equal(wout[s], win[s])
+
+
+def test_conv_identity_taps_reduce_to_plain_prefill():
+    """Taps (0, 0, 0, 1) with no activation: the conv passes inputs through,
+    so prefill with the conv equals prefill without it."""
+    rng = np.random.default_rng(32)
+    lengths = [6, 2, 11]
+    H, dk, dv, S = 2, 4, 3, 5
+    q, k, v, g, beta, _, win, cu = _conv_inputs(rng, lengths, H, dk, dv, S)
+    w = np.zeros((H, 4, 2 * dk + dv))
+    w[:, 3, :] = 1.0
+    pool = 0.2 * rng.standard_normal((S, H, dv, dk))
+    slots = np.array([4, 1, 2], dtype=np.int32)
+    o1, p1, _, wout = oracle.chunk_prefill_conv(q, k, v, g, beta, cu, w, win, pool, slots)
+    o2, p2, _ = oracle.chunk_prefill(q, k, v, g, beta, cu, state_pool=pool, slots=slots)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(p1, p2)
+    # sequence 1 has 2 rows: the window keeps its newest old row, then the 2 inputs
+    x = np.concatenate([q, k, v], axis=2)
+    np.testing.assert_array_equal(wout[1][:, 0], win[1][:, 2])
+    np.testing.assert_array_equal(wout[1][:, 1:].transpose(1, 0, 2), x[6:8])
+
+
+def test_conv_prefill_split_and_decode_continuity():
+    """One prefill over 13 rows equals 8 rows then 5 rows (state and window
+    carried in the pools), and equals 8 rows then 5 decode steps."""
+    rng = np.random.default_rng(33)
+    H, dk, dv, S = 2, 4, 4, 3
+    q, k, v, g, beta, w, win, _ = _conv_inputs(rng, [13], H, dk, dv, S)
+    pool = 0.2 * rng.standard_normal((S, H, dv, dk))
+    sl = np.array([2], dtype=np.int32)
+    full = oracle.chunk_prefill_conv(q, k, v, g, beta, [0, 13], w, win, pool, sl,
+                                     activation="silu")
+    r1 = slice(0, 8)
+    a = oracle.chunk_prefill_conv(q[r1], k[r1], v[r1], g[r1], beta[r1], [0, 8], w, win, pool, sl,
+                                  activation="silu")
+    r2 = slice(8, 13)
+    b = oracle.chunk_prefill_conv(q[r2], k[r2], v[r2], g[r2], beta[r2], [0, 5], w, a[3], a[1],
+                                  sl, activation="silu")
+    np.testing.assert_allclose(np.concatenate([a[0], b[0]]), full[0], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(b[1], full[1], rtol=1e-11, atol=1e-12)
+    np.testing.assert_array_equal(b[3], full[3])
+    pool_d, win_d = a[1], a[3]
+    for t in range(8, 13):
+        r = slice(t, t + 1)
+        o, pool_d, win_d = oracle.decode_step_conv(q[r], k[r], v[r], g[r], beta[r], pool_d, sl, w,
+                                                   win_d, activation="silu")
+        np.testing.assert_allclose(o[0], full[0][t], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(pool_d, full[1], rtol=1e-11, atol=1e-12)
+    np.testing.assert_array_equal(win_d, full[3])
