@@ -120,7 +120,9 @@ def to_dev(case, copies, torch):
     return sets, dt
 
 
-def time_prefill(case, steps, warmup, copies, torch, lap):
+def time_prefill(case, steps, warmup, copies, torch, lap, conv=None):
+    """conv: None, or (weight [H,4,C], window pool, activation) for the short
+    conv front end; each input copy gets its own window pool."""
     sets, dt = to_dev(case, copies, torch)
     T, H, dk, dv = case.T, case.H, case.d_k, case.d_v
     cu = torch.from_numpy(case.cu_seqlens).to("cuda")
@@ -133,15 +135,21 @@ def time_prefill(case, steps, warmup, copies, torch, lap):
                  for _ in range(copies)]
         state_in = False
     outs = [torch.empty((T, H, dv), dtype=dt, device="cuda") for _ in range(copies)]
-    ws = torch.empty(max(lap.prefill_workspace_size(T, case.N, H, dk, dv, dt), 16),
+    ws = torch.empty(max(lap.prefill_workspace_size(T, case.N, H, dk, dv, dt, conv=bool(conv)), 16),
                      dtype=torch.uint8, device="cuda")
+    ckw = [{} for _ in range(copies)]
+    if conv:
+        w = torch.from_numpy(conv[0]).to("cuda")
+        ckw = [{"conv_weight": w, "conv_window": torch.from_numpy(conv[1]).to("cuda").to(dt),
+                "conv_activation": conv[2]} for _ in range(copies)]
 
     def call(i, events=None):
         s = sets[i % copies]
         p = pools[i % copies]
         lap.chunk_prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], cu,
                           state_in=p if state_in else None, state_out=p, o=outs[i % copies],
-                          slots=slots, scale=case.scale, workspace=ws, events=events)
+                          slots=slots, scale=case.scale, workspace=ws, events=events,
+                          **ckw[i % copies])
 
     for i in range(warmup):
         call(i)
@@ -167,7 +175,7 @@ def time_prefill(case, steps, warmup, copies, torch, lap):
     }
 
 
-def time_decode(case, steps, warmup, copies, torch, lap):
+def time_decode(case, steps, warmup, copies, torch, lap, conv=None):
     dt = torch.bfloat16 if case.io_dtype == "bf16" else torch.float32
     q = torch.from_numpy(case.q).to("cuda").to(dt)
     k = torch.from_numpy(case.k).to("cuda").to(dt)
@@ -177,13 +185,18 @@ def time_decode(case, steps, warmup, copies, torch, lap):
     slots = torch.from_numpy(case.slots).to("cuda")
     pools = [torch.from_numpy(case.state_pool).to("cuda") for _ in range(copies)]
     o = torch.empty((case.N, case.H, case.d_v), dtype=dt, device="cuda")
+    ckw = [{} for _ in range(copies)]
+    if conv:
+        w = torch.from_numpy(conv[0]).to("cuda")
+        ckw = [{"conv_weight": w, "conv_window": torch.from_numpy(conv[1]).to("cuda").to(dt),
+                "conv_activation": conv[2]} for _ in range(copies)]
     for i in range(warmup):
-        lap.decode_step(q, k, v, g, beta, pools[i % copies], slots, o=o)
+        lap.decode_step(q, k, v, g, beta, pools[i % copies], slots, o=o, **ckw[i % copies])
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
-        lap.decode_step(q, k, v, g, beta, pools[i % copies], slots, o=o)
+        lap.decode_step(q, k, v, g, beta, pools[i % copies], slots, o=o, **ckw[i % copies])
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
@@ -191,6 +204,9 @@ def time_decode(case, steps, warmup, copies, torch, lap):
     es = 2 if case.io_dtype == "bf16" else 4
     nbytes = case.N * (2 * state + case.H * (2 * case.d_k * es + case.d_v * es + case.d_k * 4
                                              + 4 + case.d_v * es))
+    if conv:   # windows read and written; the taps, shared by all sequences, read once
+        C = 2 * case.d_k + case.d_v
+        nbytes += case.N * case.H * C * 2 * 3 * es + case.H * 4 * C * 4
     return {"us": ms * 1e3, "bytes": nbytes, "GB/s": nbytes / (ms * 1e-3) / 1e9,
             "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
@@ -290,6 +306,8 @@ def main():
                          "decode: 64 sequences x 1 token (profiling the decode kernel); "
                          "decode_tokens: 64 sequences x 4 draft tokens (multi-token decode)")
     ap.add_argument("--copies", type=int, default=3, help="rotated device copies of the inputs")
+    ap.add_argument("--conv", action="store_true",
+                    help="prefill workloads: run the short conv front end (SiLU) before the path")
     ap.add_argument("--tokens-mode", choices=["verify_commit", "verify", "commit"], default=None,
                     help="decode_tokens workload: time only this mode (default: all three)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -316,16 +334,20 @@ def main():
 
     if args.workload == "decode":
         dc = W.decode_case()
-        rd = time_decode(dc, args.steps, args.warmup, 4, torch, lap)
+        conv = None
+        if args.conv:
+            cw = W.draw_conv(12, dc.state_pool.shape[0], dc.H, dc.d_k, dc.d_v, dc.io_dtype)
+            conv = (cw[0], cw[1], "silu")
+        rd = time_decode(dc, args.steps, args.warmup, 4, torch, lap, conv=conv)
         out = {"metric": "KDA decode step: state read-modify-write bandwidth on 1 MI355X",
                "value": rd["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
                "warmup": args.warmup, "ms_per_step": rd["us"] * 1e-3, "higher_is_better": True,
                "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-               "config": {"workload": dc.name, "num_seqs": dc.N, "heads": dc.H, "d_k": dc.d_k,
-                          "d_v": dc.d_v, "pools_rotated": 4},
+               "config": {"workload": dc.name + ("+conv3_silu" if conv else ""), "num_seqs": dc.N,
+                          "heads": dc.H, "d_k": dc.d_k, "d_v": dc.d_v, "pools_rotated": 4},
                "roofline": {"bound": "hbm", "achieved": rd["GB/s"], "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": rd["frac_hbm"], "traffic": None,
-                            "kernel": "kda_decode_kernel"}}
+                            "kernel": "kda_decode_conv_kernel" if conv else "kda_decode_kernel"}}
         print(json.dumps(out), flush=True)
         return
     if args.workload == "decode_tokens":
@@ -354,9 +376,15 @@ def main():
     es = 2 if case.io_dtype == "bf16" else 4
     n_chunks = chunk_count(lengths)
 
-    r = time_prefill(case, args.steps, args.warmup, args.copies, torch, lap)
-    log("prefill %.1f us/step (intra %.1f us, scan %.1f us)"
-        % (r["ms_per_step"] * 1e3, r["intra_ms"] * 1e3, r["scan_ms"] * 1e3))
+    conv = None
+    if args.conv:
+        cw = W.draw_conv(11, 1 if case.state_pool is None else case.state_pool.shape[0], H, dk,
+                         dv, case.io_dtype)
+        conv = (cw[0], cw[1], "silu")
+    r = time_prefill(case, args.steps, args.warmup, args.copies, torch, lap, conv=conv)
+    log("prefill%s %.1f us/step (intra %.1f us, scan %.1f us)"
+        % (" with conv" if conv else "", r["ms_per_step"] * 1e3, r["intra_ms"] * 1e3,
+           r["scan_ms"] * 1e3))
     n_live = case.N
     ib = intra_bytes(T, H, dk, dv, es, n_chunks)
     sb = scan_bytes(T, H, dk, dv, es, n_chunks, n_live, r["state_in"], True)
@@ -388,7 +416,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": case.name, "total_rows": T, "num_seqs": case.N, "heads": H,
+        "config": {"workload": case.name + ("+conv3_silu" if conv else ""), "total_rows": T, "num_seqs": case.N, "heads": H,
                    "d_k": dk, "d_v": dv, "chunk": 64, "io_dtype": case.io_dtype,
                    "state": "fp32", "initial_state": "pool" if r["state_in"] else "zero",
                    "input_copies_rotated": args.copies},
@@ -410,11 +438,27 @@ def main():
                                "tokens/s": pc.T / (rp["ms_per_step"] * 1e-3),
                                "intra_us": rp["intra_ms"] * 1e3, "scan_us": rp["scan_ms"] * 1e3}
             log("packed %.1f us/step" % (rp["ms_per_step"] * 1e3))
+            cw = W.draw_conv(11, 1, H, dk, dv, case.io_dtype)
+            rc = time_prefill(case, max(5, args.steps // 2), 2, args.copies, torch, lap,
+                              conv=(cw[0], cw[1], "silu"))
+            conv_us = (rc["ms_per_step"] - rc["intra_ms"] - rc["scan_ms"]) * 1e3
+            extra["prefill_conv"] = {"workload": case.name + "+conv3_silu",
+                                     "us": rc["ms_per_step"] * 1e3,
+                                     "tokens/s": T / (rc["ms_per_step"] * 1e-3),
+                                     "conv_us": conv_us, "intra_us": rc["intra_ms"] * 1e3,
+                                     "scan_us": rc["scan_ms"] * 1e3}
+            log("prefill with conv %.1f us/step (conv front end %.1f us)"
+                % (rc["ms_per_step"] * 1e3, conv_us))
         dc = W.decode_case()
         rd = time_decode(dc, max(10, args.steps), 3, 4, torch, lap)
         rd["workload"] = dc.name
         extra["decode"] = rd
         log("decode %.1f us, %.0f GB/s" % (rd["us"], rd["GB/s"]))
+        cw = W.draw_conv(12, dc.state_pool.shape[0], dc.H, dc.d_k, dc.d_v, dc.io_dtype)
+        rdc = time_decode(dc, max(10, args.steps), 3, 4, torch, lap, conv=(cw[0], cw[1], "silu"))
+        rdc["workload"] = dc.name + "+conv3_silu"
+        extra["decode_conv"] = rdc
+        log("decode with conv %.1f us, %.0f GB/s" % (rdc["us"], rdc["GB/s"]))
         mc = W.decode_tokens_case()
         rm = time_decode_tokens(mc, max(10, args.steps), 3, 4, torch, lap)
         rm["workload"] = mc.name

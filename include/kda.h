@@ -83,6 +83,40 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
  * overlap; the pool must hold (num_slots - 1) slot strides plus one line.
  */
 
+/*
+ * Short conv front end.  On the prefill side of the kern-k3-pp-prefill page
+ * every sequence carries a conv window next to its recurrent state (section
+ * "P: the packed prefill"), its decode build fuses the conv into the step (section "D:
+ * TP8 / EP8 / DCP8"), and SGLang keeps the window as [slot][tap][q | k | v]
+ * bf16 (section "D inside SGLang").  The "kern" page's KDA state of
+ * 19,537,920 bytes a sequence (section "The manifest") is 288 blocks of a
+ * 64 KiB state plus 3 x 3 x 128 bf16, so the window holds 3 rows.  Reading
+ * taken here: per head, the channels x = [q | k | v] (2 d_k + d_v of them)
+ * pass through a causal per-channel conv of width 4,
+ *     y_t = w0 x_{t-3} + w1 x_{t-2} + w2 x_{t-1} + w3 x_t,
+ * whose three older inputs at a sequence's start come from its window; an
+ * optional SiLU follows; y, rounded to the io dtype, replaces q, k and v for
+ * the rest of the step.  After the call each live sequence's window holds its
+ * last three raw inputs (older window rows shift in for sequences shorter
+ * than three rows; a zero-length sequence leaves it as it was).  A padded
+ * sequence (slot out of range) convolves from zeros and touches no window.
+ */
+typedef enum { KDA_CONV_NONE = 0, KDA_CONV_LINEAR = 1, KDA_CONV_SILU = 2 } kda_conv_mode_t;
+
+typedef struct {
+    const float *weight;  /* [H][4][2 d_k + d_v] fp32: tap j multiplies x_{t-3+j} */
+    void *window;         /* raw inputs, io dtype, read and rewritten in place */
+    /* Row i (0 = oldest) of (slot s, head h), part p (0 q, 1 k, 2 v), channel c
+     * is element s*slot + h*head + i*row + p*part + c of `window`.  Zeros give
+     * the dense [num_slots][H][3][2 d_k + d_v] layout (part = d_k, row =
+     * 2 d_k + d_v, head = 3 row, slot = H head).  SGLang's tap-major
+     * [slot][tap][q | k | v] is slot = 3 row, row = H (2 d_k + d_v),
+     * part = H d_k, head = d_k (this needs d_k = d_v).  Given strides must be
+     * multiples of 4 with part >= d_k; the caller keeps the addressed rows
+     * from overlapping. */
+    int64_t slot_stride, head_stride, row_stride, part_stride;
+} kda_conv_t;
+
 /* Sizes of one prefill call.  T = total_rows, N = num_seqs, H = num_heads. */
 typedef struct {
     int32_t total_rows;  /* T >= 0 */
@@ -95,12 +129,15 @@ typedef struct {
     float scale;         /* multiplies o only */
     int64_t state_slot_stride;  /* fp32 elements between slots' lines; 0 = dense */
     int64_t state_head_stride;  /* fp32 elements between heads of a line; 0 = dense */
+    int32_t conv_mode;   /* kda_conv_mode_t; not NONE only with kda_chunk_prefill_conv */
+    int32_t reserved;    /* 0 */
 } kda_prefill_desc_t;
 
 /*
  * Bytes of device workspace kda_chunk_prefill needs for `desc` (0 if desc is
  * invalid).  The workspace holds the per-chunk operands that pass from the
- * intra-chunk kernel to the state scan; it is scratch for one call.
+ * intra-chunk kernel to the state scan, and with a conv mode the convolved
+ * q, k and v; it is scratch for one call.
  */
 size_t kda_prefill_workspace_size(const kda_prefill_desc_t *desc);
 
@@ -160,6 +197,27 @@ kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v
                                      void *stream, void *const *events);
 
 /*
+ * kda_chunk_prefill_timed with the short conv front end (desc->conv_mode not
+ * KDA_CONV_NONE; see "Short conv front end" above): q, k and v are the raw
+ * inputs, conv->window is read and then rewritten, and the rest of the step
+ * runs on the convolved values.  The conv runs first, then the window
+ * update, then the two kernels that `events` (optional, as for
+ * kda_chunk_prefill_timed) bracket.  Errors as for kda_chunk_prefill, plus
+ * KDA_ERR_NULL for a NULL conv, weight or window, and KDA_ERR_SHAPE for a
+ * conv mode out of range or window strides that break the rules above.
+ * kda_chunk_prefill and kda_chunk_prefill_timed return KDA_ERR_NULL for a
+ * desc with a conv mode.
+ */
+kda_status_t kda_chunk_prefill_conv(const void *q, const void *k, const void *v,
+                                    const float *g, const float *beta,
+                                    const int32_t *cu_seqlens,
+                                    const float *state_in, float *state_out,
+                                    void *o, const int32_t *slots,
+                                    const kda_prefill_desc_t *desc, const kda_conv_t *conv,
+                                    void *workspace, size_t ws_bytes,
+                                    void *stream, void *const *events);
+
+/*
  * kda_decode_step with the state pool addressed by lines (see "State
  * addressing by lines" above): the block of (slot s, head h) starts at
  * state_pool + s * state_slot_stride + h * state_head_stride; strides of 0
@@ -191,6 +249,23 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
                              int32_t num_seqs, int32_t num_heads,
                              int32_t d_k, int32_t d_v, int32_t num_slots,
                              int32_t io_dtype, float scale, void *stream);
+
+/*
+ * kda_decode_step_lines with the short conv front end fused in (conv_mode
+ * KDA_CONV_LINEAR or KDA_CONV_SILU; see "Short conv front end" above): q, k
+ * and v are the raw token inputs; each live sequence's window is read and
+ * shifted by one row in place.  Errors as for kda_decode_step_lines, plus
+ * KDA_ERR_NULL for a NULL conv, weight or window and KDA_ERR_SHAPE for a
+ * conv mode out of range or bad window strides.
+ */
+kda_status_t kda_decode_step_conv(const void *q, const void *k, const void *v,
+                                  const float *g, const float *beta,
+                                  float *state_pool, const int32_t *slots, void *o,
+                                  int32_t num_seqs, int32_t num_heads,
+                                  int32_t d_k, int32_t d_v, int32_t num_slots,
+                                  int32_t io_dtype, float scale,
+                                  int64_t state_slot_stride, int64_t state_head_stride,
+                                  int32_t conv_mode, const kda_conv_t *conv, void *stream);
 
 /*
  * Multi-token decode and speculative verify / commit: T = num_tokens tokens

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["kda_prefill.hip", "kda_decode.hip"]
+HIP_SOURCES = ["kda_prefill.hip", "kda_decode.hip", "kda_conv.hip"]
 CXX_SOURCES = ["kda_api.cpp"]
 
 # Packed fp32 VALU ops are disabled for all device code.

@@ -40,6 +40,23 @@ hipError_t dispatch_decode_tokens(const kda::DecodeArgs &a, int dk, int dv, hipS
     return kda::launch_decode_tokens<E, 128, 128>(a, s);
 }
 
+template <typename E>
+hipError_t dispatch_conv_front(const kda::ConvArgs &a, int dk, int dv, hipStream_t s) {
+    if (dk == 64 && dv == 64) return kda::launch_conv_front<E, 64, 64>(a, s);
+    if (dk == 64 && dv == 128) return kda::launch_conv_front<E, 64, 128>(a, s);
+    if (dk == 128 && dv == 64) return kda::launch_conv_front<E, 128, 64>(a, s);
+    return kda::launch_conv_front<E, 128, 128>(a, s);
+}
+
+template <typename E>
+hipError_t dispatch_decode_conv(const kda::DecodeArgs &a, const kda::ConvArgs &c, int dk, int dv,
+                                hipStream_t s) {
+    if (dk == 64 && dv == 64) return kda::launch_decode_conv<E, 64, 64>(a, c, s);
+    if (dk == 64 && dv == 128) return kda::launch_decode_conv<E, 64, 128>(a, c, s);
+    if (dk == 128 && dv == 64) return kda::launch_decode_conv<E, 128, 64>(a, c, s);
+    return kda::launch_decode_conv<E, 128, 128>(a, c, s);
+}
+
 // Compute units of the current device (persistent grids are sized by it).
 int device_cus() {
     int dev = 0, n = 0;
@@ -56,6 +73,7 @@ kda_status_t check_desc(const kda_prefill_desc_t *d) {
     if (!dims_supported(d->d_k, d->d_v)) return KDA_ERR_UNSUPPORTED;
     if (d->total_rows < 0 || d->num_seqs < 1 || d->num_heads < 1 || d->num_slots < 0)
         return KDA_ERR_SHAPE;
+    if (d->conv_mode < KDA_CONV_NONE || d->conv_mode > KDA_CONV_SILU) return KDA_ERR_SHAPE;
     if (d->num_heads > 65535) return KDA_ERR_SHAPE;                       // grid.y of the intra kernel
     const long long chunks = (long long)d->total_rows / 64 + d->num_seqs;
     if (chunks > INT_MAX) return KDA_ERR_SHAPE;
@@ -76,41 +94,87 @@ bool resolve_strides(int64_t slot_stride, int64_t head_stride, int H, int dk, in
     return true;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t kda_prefill_workspace_size(const kda_prefill_desc_t *desc) {
-    if (check_desc(desc) != KDA_OK) return 0;
-    return kda::prefill_workspace_bytes(desc->total_rows, desc->num_seqs, desc->num_heads,
-                                        desc->d_k, desc->d_v, desc->io_dtype == KDA_BF16);
+// Resolves the conv window strides (io elements; 0 = dense head-major) and
+// checks the rules of kda.h: multiples of 4 (8- or 16-byte rows), non-negative,
+// q and k parts of a row apart by at least d_k.
+bool resolve_conv(const kda_conv_t *c, int H, int dk, int dv, kda::ConvWin *w) {
+    const int64_t C = 2 * (int64_t)dk + dv;
+    w->ps = c->part_stride ? c->part_stride : dk;
+    w->ts = c->row_stride ? c->row_stride : C;
+    w->hs = c->head_stride ? c->head_stride : 3 * C;
+    w->ss = c->slot_stride ? c->slot_stride : (int64_t)H * w->hs;
+    const int64_t v[] = {w->ps, w->ts, w->hs, w->ss};
+    for (int64_t x : v)
+        if (x < 0 || x % 4) return false;
+    return w->ps >= dk;
 }
 
-kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v,
-                                     const float *g, const float *beta,
-                                     const int32_t *cu_seqlens, const float *state_in,
-                                     float *state_out, void *o, const int32_t *slots,
-                                     const kda_prefill_desc_t *desc, void *workspace,
-                                     size_t ws_bytes, void *stream, void *const *events) {
+// Host checks shared by the conv entry points; fills the conv arguments that
+// do not depend on the call's buffers.
+kda_status_t check_conv(int mode, const kda_conv_t *conv, int H, int dk, int dv,
+                        kda::ConvArgs *c) {
+    if (mode < KDA_CONV_LINEAR || mode > KDA_CONV_SILU) return KDA_ERR_SHAPE;
+    if (!conv || !conv->weight || !conv->window) return KDA_ERR_NULL;
+    if (!aligned16(conv->weight) || !aligned16(conv->window)) return KDA_ERR_ALIGN;
+    if (!resolve_conv(conv, H, dk, dv, &c->win)) return KDA_ERR_SHAPE;
+    c->weight = conv->weight;
+    c->window = conv->window;
+    c->silu = mode == KDA_CONV_SILU;
+    return KDA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+kda_status_t prefill_impl(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const int32_t *cu_seqlens, const float *state_in,
+                          float *state_out, void *o, const int32_t *slots,
+                          const kda_prefill_desc_t *desc, const kda_conv_t *conv, bool with_conv,
+                          void *workspace, size_t ws_bytes, void *stream, void *const *events) {
     const kda_status_t st = check_desc(desc);
     if (st != KDA_OK) return st;
     const kda_prefill_desc_t d = *desc;
+    if (!with_conv && d.conv_mode != KDA_CONV_NONE) return KDA_ERR_NULL;
+    if (with_conv && d.conv_mode == KDA_CONV_NONE) return KDA_ERR_SHAPE;
     if (!slots && (state_in || state_out) && d.num_slots < d.num_seqs) return KDA_ERR_SHAPE;
     if (!q || !k || !v || !g || !beta || !cu_seqlens) return KDA_ERR_NULL;
     if (!o && d.total_rows > 0) return KDA_ERR_NULL;
-    const size_t need = kda::prefill_workspace_bytes(d.total_rows, d.num_seqs, d.num_heads,
-                                                     d.d_k, d.d_v, d.io_dtype == KDA_BF16);
+    const bool bf = d.io_dtype == KDA_BF16;
+    const size_t rec_bytes = kda::prefill_workspace_bytes(d.total_rows, d.num_seqs, d.num_heads,
+                                                          d.d_k, d.d_v, bf);
+    const size_t need = rec_bytes + (with_conv ? kda::conv_workspace_bytes(
+                                                     d.total_rows, d.num_heads, d.d_k, d.d_v, bf)
+                                               : 0);
     if (need > 0 && !workspace) return KDA_ERR_NULL;
     const void *ptrs[] = {q, k, v, g, beta, cu_seqlens, state_in, state_out, o, slots, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    kda::ConvArgs c{};
+    if (with_conv) {
+        const kda_status_t cs = check_conv(d.conv_mode, conv, d.num_heads, d.d_k, d.d_v, &c);
+        if (cs != KDA_OK) return cs;
+        if (((long long)d.total_rows / 64 + 1) * d.num_heads > INT_MAX) return KDA_ERR_SHAPE;
+    }
     if (ws_bytes < need) return KDA_ERR_WORKSPACE;
     int64_t ss = 0, hs = 0;
     if (!resolve_strides(d.state_slot_stride, d.state_head_stride, d.num_heads, d.d_k, d.d_v, &ss, &hs))
         return KDA_ERR_SHAPE;
 
+    hipStream_t s = static_cast<hipStream_t>(stream);
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens;
+    if (with_conv) {
+        const size_t es = bf ? 2 : 4;
+        char *base = static_cast<char *>(workspace) + align256(rec_bytes);
+        const size_t nq = align256((size_t)d.total_rows * d.num_heads * d.d_k * es);
+        c.q = q; c.k = k; c.v = v;
+        c.qc = base; c.kc = base + nq; c.vc = base + 2 * nq;
+        c.cu_seqlens = cu_seqlens; c.slots = slots;
+        c.T = d.total_rows; c.N = d.num_seqs; c.H = d.num_heads; c.num_slots = d.num_slots;
+        const hipError_t e = bf ? dispatch_conv_front<bf16>(c, d.d_k, d.d_v, s)
+                                : dispatch_conv_front<float>(c, d.d_k, d.d_v, s);
+        if (e != hipSuccess) return KDA_ERR_HIP;
+        a.q = c.qc; a.k = c.kc; a.v = c.vc;
+    }
     a.state_in = state_in; a.state_out = state_out; a.o = o; a.slots = slots;
     a.workspace = workspace;
     a.T = d.total_rows; a.N = d.num_seqs; a.H = d.num_heads; a.num_slots = d.num_slots;
@@ -119,10 +183,81 @@ kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v
     a.head_stride = hs;
     for (int i = 0; i < 3; ++i) a.events[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
     a.num_cus = device_cus();
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = d.io_dtype == KDA_BF16 ? dispatch_prefill<bf16>(a, d.d_k, d.d_v, s)
-                                                : dispatch_prefill<float>(a, d.d_k, d.d_v, s);
+    const hipError_t e = bf ? dispatch_prefill<bf16>(a, d.d_k, d.d_v, s)
+                            : dispatch_prefill<float>(a, d.d_k, d.d_v, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t decode_impl(const void *q, const void *k, const void *v, const float *g,
+                         const float *beta, float *state_pool, const int32_t *slots, void *o,
+                         int32_t num_seqs, int32_t num_heads, int32_t d_k, int32_t d_v,
+                         int32_t num_slots, int32_t io_dtype, float scale,
+                         int64_t state_slot_stride, int64_t state_head_stride, int32_t conv_mode,
+                         const kda_conv_t *conv, void *stream) {
+    if (io_dtype != KDA_F32 && io_dtype != KDA_BF16) return KDA_ERR_DTYPE;
+    if (!dims_supported(d_k, d_v)) return KDA_ERR_UNSUPPORTED;
+    if (num_seqs < 1 || num_heads < 1 || num_slots < 1) return KDA_ERR_SHAPE;
+    if ((long long)num_seqs * num_heads * (d_v / 64) > INT_MAX) return KDA_ERR_SHAPE;
+    if (!q || !k || !v || !g || !beta || !state_pool || !slots || !o) return KDA_ERR_NULL;
+    const void *ptrs[] = {q, k, v, g, beta, state_pool, slots, o};
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return KDA_ERR_ALIGN;
+    kda::ConvArgs c{};
+    if (conv_mode != KDA_CONV_NONE) {
+        const kda_status_t cs = check_conv(conv_mode, conv, num_heads, d_k, d_v, &c);
+        if (cs != KDA_OK) return cs;
+    }
+    int64_t ss = 0, hs = 0;
+    if (!resolve_strides(state_slot_stride, state_head_stride, num_heads, d_k, d_v, &ss, &hs))
+        return KDA_ERR_SHAPE;
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.pool = state_pool; a.slots = slots;
+    a.o = o; a.N = num_seqs; a.H = num_heads; a.num_slots = num_slots; a.scale = scale;
+    a.slot_stride = ss;
+    a.head_stride = hs;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf = io_dtype == KDA_BF16;
+    hipError_t e;
+    if (conv_mode != KDA_CONV_NONE)
+        e = bf ? dispatch_decode_conv<bf16>(a, c, d_k, d_v, s)
+               : dispatch_decode_conv<float>(a, c, d_k, d_v, s);
+    else
+        e = bf ? dispatch_decode<bf16>(a, d_k, d_v, s) : dispatch_decode<float>(a, d_k, d_v, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_prefill_workspace_size(const kda_prefill_desc_t *desc) {
+    if (check_desc(desc) != KDA_OK) return 0;
+    const bool bf = desc->io_dtype == KDA_BF16;
+    size_t n = kda::prefill_workspace_bytes(desc->total_rows, desc->num_seqs, desc->num_heads,
+                                            desc->d_k, desc->d_v, bf);
+    if (desc->conv_mode != KDA_CONV_NONE)
+        n += kda::conv_workspace_bytes(desc->total_rows, desc->num_heads, desc->d_k, desc->d_v, bf);
+    return n;
+}
+
+kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v,
+                                     const float *g, const float *beta,
+                                     const int32_t *cu_seqlens, const float *state_in,
+                                     float *state_out, void *o, const int32_t *slots,
+                                     const kda_prefill_desc_t *desc, void *workspace,
+                                     size_t ws_bytes, void *stream, void *const *events) {
+    return prefill_impl(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, slots, desc, nullptr,
+                        false, workspace, ws_bytes, stream, events);
+}
+
+kda_status_t kda_chunk_prefill_conv(const void *q, const void *k, const void *v, const float *g,
+                                    const float *beta, const int32_t *cu_seqlens,
+                                    const float *state_in, float *state_out, void *o,
+                                    const int32_t *slots, const kda_prefill_desc_t *desc,
+                                    const kda_conv_t *conv, void *workspace, size_t ws_bytes,
+                                    void *stream, void *const *events) {
+    return prefill_impl(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, slots, desc, conv,
+                        true, workspace, ws_bytes, stream, events);
 }
 
 kda_status_t kda_chunk_prefill(const void *q, const void *k, const void *v, const float *g,
@@ -140,26 +275,21 @@ kda_status_t kda_decode_step_lines(const void *q, const void *k, const void *v, 
                                    int32_t d_v, int32_t num_slots, int32_t io_dtype, float scale,
                                    int64_t state_slot_stride, int64_t state_head_stride,
                                    void *stream) {
-    if (io_dtype != KDA_F32 && io_dtype != KDA_BF16) return KDA_ERR_DTYPE;
-    if (!dims_supported(d_k, d_v)) return KDA_ERR_UNSUPPORTED;
-    if (num_seqs < 1 || num_heads < 1 || num_slots < 1) return KDA_ERR_SHAPE;
-    if ((long long)num_seqs * num_heads * (d_v / 64) > INT_MAX) return KDA_ERR_SHAPE;
-    if (!q || !k || !v || !g || !beta || !state_pool || !slots || !o) return KDA_ERR_NULL;
-    const void *ptrs[] = {q, k, v, g, beta, state_pool, slots, o};
-    for (const void *p : ptrs)
-        if (!aligned16(p)) return KDA_ERR_ALIGN;
-    int64_t ss = 0, hs = 0;
-    if (!resolve_strides(state_slot_stride, state_head_stride, num_heads, d_k, d_v, &ss, &hs))
-        return KDA_ERR_SHAPE;
-    kda::DecodeArgs a;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.pool = state_pool; a.slots = slots;
-    a.o = o; a.N = num_seqs; a.H = num_heads; a.num_slots = num_slots; a.scale = scale;
-    a.slot_stride = ss;
-    a.head_stride = hs;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = io_dtype == KDA_BF16 ? dispatch_decode<bf16>(a, d_k, d_v, s)
-                                              : dispatch_decode<float>(a, d_k, d_v, s);
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    return decode_impl(q, k, v, g, beta, state_pool, slots, o, num_seqs, num_heads, d_k, d_v,
+                       num_slots, io_dtype, scale, state_slot_stride, state_head_stride,
+                       KDA_CONV_NONE, nullptr, stream);
+}
+
+kda_status_t kda_decode_step_conv(const void *q, const void *k, const void *v, const float *g,
+                                  const float *beta, float *state_pool, const int32_t *slots,
+                                  void *o, int32_t num_seqs, int32_t num_heads, int32_t d_k,
+                                  int32_t d_v, int32_t num_slots, int32_t io_dtype, float scale,
+                                  int64_t state_slot_stride, int64_t state_head_stride,
+                                  int32_t conv_mode, const kda_conv_t *conv, void *stream) {
+    if (conv_mode == KDA_CONV_NONE) return KDA_ERR_SHAPE;
+    return decode_impl(q, k, v, g, beta, state_pool, slots, o, num_seqs, num_heads, d_k, d_v,
+                       num_slots, io_dtype, scale, state_slot_stride, state_head_stride,
+                       conv_mode, conv, stream);
 }
 
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v, const float *g,
@@ -220,6 +350,6 @@ const char *kda_status_string(kda_status_t status) {
     return "unknown status";
 }
 
-int32_t kda_version(void) { return 102; }
+int32_t kda_version(void) { return 103; }
 
 }  // extern "C"

@@ -91,14 +91,6 @@ __device__ __forceinline__ float row_update(f32x4 (&s)[V4], const f32x4 (&a)[V4]
     return d;
 }
 
-// Raw io vectors of four elements, kept unconverted while loads are in flight.
-template <typename E> struct Raw4Of { typedef f32x4 type; };
-template <> struct Raw4Of<bf16> { typedef bf16x4 type; };
-__device__ __forceinline__ f32x4 raw_to_f32(const f32x4 &x) { return x; }
-__device__ __forceinline__ f32x4 raw_to_f32(const bf16x4 &x) {
-    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-}
-
 __device__ __forceinline__ float row_output(float d, float kq, float dq, float scale) {
 #pragma clang fp contract(off)
     return scale * __builtin_fmaf(d, kq, dq);
@@ -160,6 +152,102 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
         const int row = part * kDecodeRows + p * RPI + rr;
         float dq;
         const float d = row_update<V4>(s[p], a4, k4, q4, bt, vv[p], dq);
+#pragma unroll
+        for (int x = 0; x < V4; ++x)
+            __builtin_nontemporal_store(s[p][x], reinterpret_cast<f32x4 *>(S + (size_t)row * DK + 4 * (c + 16 * x)));
+        if (c == 0) o[tok * DV + row] = (E)row_output(d, kq, dq, scale);
+    }
+}
+
+// The decode step with the short conv fused in (the KDA_CONV build of the
+// kern-k3-pp-prefill page, section "D: TP8 / EP8 / DCP8", which reads the
+// window in SGLang's tap-major layout in its CONV_TAP_MAJOR variant, section
+// "D inside SGLang"; here any layout the window strides describe).  One
+// workgroup owns all d_v rows of a (sequence, head), so it alone reads and
+// rewrites that window: each of the 2 d_k + d_v channels is convolved once
+// (threads t and t + 256), rounded to the io dtype as the prefill pass does,
+// and staged in LDS; the window shifts by one row; then the state rows are
+// updated as in the plain step, reading k, q and v from LDS.
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(256) void kda_decode_conv_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, float *pool,
+    const int32_t *__restrict__ slots, E *__restrict__ o, int N, int H, int num_slots,
+    float scale, int64_t slot_stride, int64_t head_stride, const float *__restrict__ weight,
+    E *window, ConvWin win, int silu) {
+    constexpr int C = 2 * DK + DV;
+    constexpr int CPT = (C + 255) / 256;         // channels per thread
+    constexpr int V4 = DK / 64;
+    constexpr int RPI = 256 / 16;
+    constexpr int P = DV / RPI;                  // passes over all d_v rows
+    __shared__ float sX[C];
+    const int tid = threadIdx.x;
+    const int n = blockIdx.x / H, h = blockIdx.x % H;
+    if (n >= N) return;
+    const int slot = slots[n];
+    if (slot < 0 || slot >= num_slots) return;   // padded row: touch nothing
+    const int c = tid & 15, rr = tid >> 4;
+    const size_t tok = (size_t)n * H + h;
+
+    // token channels, window rows and taps (unconditional, clamped loads)
+    E xr[CPT], wo[CPT][kConvWindow];
+    float wt[CPT][kConvTaps];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int ch = min(tid + 256 * u, C - 1);
+        const int part = ch < DK ? 0 : (ch < 2 * DK ? 1 : 2);
+        const int pc = ch - part * DK;
+        xr[u] = part == 0 ? q[tok * DK + pc] : (part == 1 ? k[tok * DK + pc] : v[tok * DV + pc]);
+#pragma unroll
+        for (int i = 0; i < kConvWindow; ++i) wo[u][i] = window[win.at(slot, h, i, part, pc)];
+#pragma unroll
+        for (int j = 0; j < kConvTaps; ++j) wt[u][j] = weight[((size_t)h * kConvTaps + j) * C + ch];
+    }
+    f32x4 a4[V4];
+#pragma unroll
+    for (int x = 0; x < V4; ++x)
+        a4[x] = *reinterpret_cast<const f32x4 *>(g + tok * DK + 4 * (c + 16 * x));
+    const float bt = beta[tok];
+    float *S = pool + slot * slot_stride + h * head_stride;
+    f32x4 s[P][V4];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int row = p * RPI + rr;
+#pragma unroll
+        for (int x = 0; x < V4; ++x)
+            s[p][x] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)row * DK + 4 * (c + 16 * x)));
+    }
+
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int ch = tid + 256 * u;
+        if (ch < C) {
+            const int part = ch < DK ? 0 : (ch < 2 * DK ? 1 : 2);
+            const int pc = ch - part * DK;
+            sX[ch] = round_io<E>(conv_act(conv4(wt[u][0], wt[u][1], wt[u][2], wt[u][3],
+                                                (float)wo[u][0], (float)wo[u][1], (float)wo[u][2],
+                                                (float)xr[u]), silu));
+            window[win.at(slot, h, 0, part, pc)] = wo[u][1];
+            window[win.at(slot, h, 1, part, pc)] = wo[u][2];
+            window[win.at(slot, h, 2, part, pc)] = xr[u];
+        }
+    }
+    __syncthreads();
+
+    f32x4 k4[V4], q4[V4];
+#pragma unroll
+    for (int x = 0; x < V4; ++x) {
+        k4[x] = *reinterpret_cast<const f32x4 *>(&sX[DK + 4 * (c + 16 * x)]);
+        q4[x] = *reinterpret_cast<const f32x4 *>(&sX[4 * (c + 16 * x)]);
+        a4[x] = f32x4{decay_factor(a4[x][0]), decay_factor(a4[x][1]), decay_factor(a4[x][2]),
+                      decay_factor(a4[x][3])};
+    }
+    const float kq = token_kq<V4>(k4, q4);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int row = p * RPI + rr;
+        float dq;
+        const float d = row_update<V4>(s[p], a4, k4, q4, bt, sX[2 * DK + row], dq);
 #pragma unroll
         for (int x = 0; x < V4; ++x)
             __builtin_nontemporal_store(s[p][x], reinterpret_cast<f32x4 *>(S + (size_t)row * DK + 4 * (c + 16 * x)));
@@ -342,9 +430,20 @@ hipError_t launch_decode_tokens(const DecodeArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <typename E, int DK, int DV>
+hipError_t launch_decode_conv(const DecodeArgs &a, const ConvArgs &c, hipStream_t stream) {
+    kda_decode_conv_kernel<E, DK, DV><<<dim3(a.N * a.H), dim3(256), 0, stream>>>(
+        static_cast<const E *>(a.q), static_cast<const E *>(a.k), static_cast<const E *>(a.v),
+        a.g, a.beta, a.pool, a.slots, static_cast<E *>(a.o), a.N, a.H, a.num_slots, a.scale,
+        a.slot_stride, a.head_stride, c.weight, static_cast<E *>(c.window), c.win, c.silu);
+    return hipGetLastError();
+}
+
 #define KDA_INST(E, DK, DV)                                                           \
     template hipError_t launch_decode<E, DK, DV>(const DecodeArgs &, hipStream_t);    \
-    template hipError_t launch_decode_tokens<E, DK, DV>(const DecodeArgs &, hipStream_t);
+    template hipError_t launch_decode_tokens<E, DK, DV>(const DecodeArgs &, hipStream_t); \
+    template hipError_t launch_decode_conv<E, DK, DV>(const DecodeArgs &, const ConvArgs &, \
+                                                      hipStream_t);
 KDA_INST(bf16, 64, 64)
 KDA_INST(bf16, 64, 128)
 KDA_INST(bf16, 128, 64)

@@ -177,6 +177,14 @@ template <> __device__ __forceinline__ void store4<float>(float *p, const f32x4 
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw io vectors of four elements, kept unconverted while loads are in flight.
+template <typename E> struct Raw4Of { typedef f32x4 type; };
+template <> struct Raw4Of<bf16> { typedef bf16x4 type; };
+__device__ __forceinline__ f32x4 raw_to_f32(const f32x4 &x) { return x; }
+__device__ __forceinline__ f32x4 raw_to_f32(const bf16x4 &x) {
+    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+
 // Varlen bookkeeping shared by the prefill kernels.  Sequence n starts at
 // row clamp(cu[n], 0, T) and ends at clamp(cu[n+1], start, T).  Its chunks
 // take the ids floor(start / 64) + n + j, j = 0 .. ceil(len / 64) - 1; these
@@ -209,5 +217,27 @@ template <typename E, int DK, int DV> struct WsLayout {
     static constexpr int kUElems = kChunk * DV;           // u: (DV/16) tiles x 64 lanes x 16
     static constexpr int kRecElems = kWElems + kQElems + kKElems + kAElems + kUElems;
 };
+
+// Short conv front end (shared by the prefill pass and the fused decode).
+// Each head's channels [q | k | v] are convolved per sequence with 4 taps:
+// y_t = w0 x_{t-3} + w1 x_{t-2} + w2 x_{t-1} + w3 x_t, the three older inputs
+// coming from the sequence's window at its start, then an optional SiLU;
+// the result is rounded to the io dtype, as the layer before would emit it.
+constexpr int kConvWindow = 3;
+constexpr int kConvTaps = kConvWindow + 1;
+
+__device__ __forceinline__ float conv4(float w0, float w1, float w2, float w3, float xm3,
+                                       float xm2, float xm1, float x0) {
+#pragma clang fp contract(off)
+    return __builtin_fmaf(w3, x0, __builtin_fmaf(w2, xm1, __builtin_fmaf(w1, xm2, w0 * xm3)));
+}
+
+// SiLU y / (1 + e^-y) with the hardware reciprocal (about 1 ulp).
+__device__ __forceinline__ float conv_act(float y, int silu) {
+#pragma clang fp contract(off)
+    return silu ? y * __builtin_amdgcn_rcpf(1.f + fast_exp2(-y * kLog2e)) : y;
+}
+
+template <typename E> __device__ __forceinline__ float round_io(float x) { return (float)(E)x; }
 
 }  // namespace kda

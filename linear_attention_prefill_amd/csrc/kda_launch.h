@@ -40,8 +40,37 @@ struct DecodeArgs {
     int commit = 1;                     // 0: state is only read
 };
 
+// Conv window addressing: row i of (slot, head), part p (0 q, 1 k, 2 v),
+// channel c is element slot*ss + head*hs + i*ts + p*ps + c of the window
+// pool (io dtype elements).
+struct ConvWin {
+    int64_t ss, hs, ts, ps;
+    __host__ __device__ __forceinline__ int64_t at(int slot, int h, int i, int p, int c) const {
+        return (int64_t)slot * ss + (int64_t)h * hs + (int64_t)i * ts + (int64_t)p * ps + c;
+    }
+};
+
+// Short conv front end: raw q, k, v in, convolved q, k, v out (prefill).
+struct ConvArgs {
+    const void *q, *k, *v;          // raw inputs
+    void *qc, *kc, *vc;             // convolved outputs (prefill)
+    const int32_t *cu_seqlens;
+    const int32_t *slots;
+    const float *weight;            // [H][4][2 d_k + d_v]
+    void *window;
+    ConvWin win;
+    int T, N, H, num_slots;
+    int silu;
+};
+
 template <typename E, int DK, int DV>
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+template <typename E, int DK, int DV>
+hipError_t launch_conv_front(const ConvArgs &a, hipStream_t stream);
+
+template <typename E, int DK, int DV>
+hipError_t launch_decode_conv(const DecodeArgs &a, const ConvArgs &c, hipStream_t stream);
 
 template <typename E, int DK, int DV>
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
@@ -50,5 +79,8 @@ template <typename E, int DK, int DV>
 hipError_t launch_decode_tokens(const DecodeArgs &a, hipStream_t stream);
 
 size_t prefill_workspace_bytes(int T, int N, int H, int dk, int dv, bool bf16);
+
+// Workspace bytes of the convolved q, k, v (placed after the records).
+size_t conv_workspace_bytes(int T, int H, int dk, int dv, bool bf16);
 
 }  // namespace kda

@@ -897,6 +897,12 @@ size_t prefill_workspace_bytes(int T, int N, int H, int dk, int dv, bool bf16) {
     return max_chunks * (size_t)H * (rec * es + (size_t)dk * 4);
 }
 
+size_t conv_workspace_bytes(int T, int H, int dk, int dv, bool bf16) {
+    const size_t es = bf16 ? 2 : 4;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    return 256 + 2 * up((size_t)T * H * dk * es) + up((size_t)T * H * dv * es);
+}
+
 #define KDA_INST(E, DK, DV) \
     template hipError_t launch_prefill<E, DK, DV>(const PrefillArgs &, hipStream_t);
 KDA_INST(bf16, 64, 64)

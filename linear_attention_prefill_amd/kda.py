@@ -28,7 +28,17 @@ class PrefillDesc(ctypes.Structure):
                 ("num_heads", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("num_slots", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("state_slot_stride", ctypes.c_int64),
-                ("state_head_stride", ctypes.c_int64)]
+                ("state_head_stride", ctypes.c_int64), ("conv_mode", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class ConvDesc(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("window", ctypes.c_void_p),
+                ("slot_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+                ("row_stride", ctypes.c_int64), ("part_stride", ctypes.c_int64)]
+
+
+CONV_MODES = {"none": 1, "silu": 2}     # activation after the conv -> kda_conv_mode_t
 
 
 class KdaError(RuntimeError):
@@ -60,6 +70,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_chunk_prefill_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                             ctypes.POINTER(PrefillDesc), vp, sz, vp,
                                             ctypes.POINTER(ctypes.c_void_p)]
+    lib.kda_chunk_prefill_conv.restype = ctypes.c_int
+    lib.kda_chunk_prefill_conv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           ctypes.POINTER(PrefillDesc), ctypes.POINTER(ConvDesc),
+                                           vp, sz, vp, ctypes.POINTER(ctypes.c_void_p)]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                     i32, i32, i32, i32, i32, i32, f32, vp]
@@ -67,6 +81,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_decode_step_lines.restype = ctypes.c_int
     lib.kda_decode_step_lines.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                           i32, i32, i32, i32, i32, i32, f32, i64, i64, vp]
+    lib.kda_decode_step_conv.restype = ctypes.c_int
+    lib.kda_decode_step_conv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
+                                         i32, i32, i32, i32, i32, i32, f32, i64, i64, i32,
+                                         ctypes.POINTER(ConvDesc), vp]
     lib.kda_decode_tokens.restype = ctypes.c_int
     lib.kda_decode_tokens.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       i32, i32, i32, i32, i32, i32, i32, f32, i32, i64, i64, vp]
@@ -118,9 +136,30 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def make_desc(T, N, H, d_k, d_v, num_slots, io_dtype, scale=1.0, slot_stride=0,
-              head_stride=0) -> PrefillDesc:
+              head_stride=0, conv_mode=0) -> PrefillDesc:
     return PrefillDesc(int(T), int(N), int(H), int(d_k), int(d_v), int(num_slots),
-                       int(io_dtype), float(scale), int(slot_stride), int(head_stride))
+                       int(io_dtype), float(scale), int(slot_stride), int(head_stride),
+                       int(conv_mode), 0)
+
+
+def _conv_desc(weight, window, H, dk, dv, dtype, strides):
+    """Checks the conv taps and window tensors and packs a kda_conv_t."""
+    C = 2 * dk + dv
+    _dev(weight, "conv_weight", torch.float32, (H, 4, C))
+    if window is None:
+        raise ValueError("conv_window is required with conv_weight")
+    _dev(window, "conv_window", dtype)
+    ss, hs, rs, ps = (int(x) for x in strides)
+    if not any((ss, hs, rs, ps)) and tuple(window.shape[1:]) != (H, 3, C):
+        raise ValueError("a dense conv_window must be [num_slots, %d, 3, %d], got %s"
+                         % (H, C, tuple(window.shape)))
+    return ConvDesc(weight.data_ptr(), window.data_ptr(), ss, hs, rs, ps)
+
+
+def _conv_mode(activation):
+    if activation not in CONV_MODES:
+        raise ValueError("conv_activation must be 'none' or 'silu'")
+    return CONV_MODES[activation]
 
 
 def line_extent(num_slots, H, d_k, d_v, slot_stride, head_stride) -> int:
@@ -145,14 +184,15 @@ def _check_pool(p, name, num_slots, H, dk, dv, slot_stride, head_stride):
         _dev(p, name, torch.float32, (num_slots, H, dv, dk))
 
 
-def prefill_workspace_size(T, N, H, d_k, d_v, dtype=torch.bfloat16) -> int:
-    d = make_desc(T, N, H, d_k, d_v, N, _io_code(dtype))
+def prefill_workspace_size(T, N, H, d_k, d_v, dtype=torch.bfloat16, conv=False) -> int:
+    d = make_desc(T, N, H, d_k, d_v, N, _io_code(dtype), conv_mode=1 if conv else 0)
     return int(load_library().kda_prefill_workspace_size(ctypes.byref(d)))
 
 
 def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o=None,
                   slots=None, num_slots=None, scale=1.0, workspace=None, stream=None,
-                  events=None, state_slot_stride=0, state_head_stride=0):
+                  events=None, state_slot_stride=0, state_head_stride=0, conv_weight=None,
+                  conv_window=None, conv_activation="none", conv_strides=(0, 0, 0, 0)):
     """KDA chunked prefill over packed sequences (see ``kda_chunk_prefill``).
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype); g: [T, H, d_k]
@@ -160,8 +200,12 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
     state_out: [num_slots, H, d_v, d_k] fp32 pools or None (may be the same
     tensor); slots: [N] int32 or None.  With state_slot_stride /
     state_head_stride (fp32 elements, kda.h "State addressing by lines") the
-    pools are flat fp32 buffers and num_slots must be given.  events: optional
-    three recorded
+    pools are flat fp32 buffers and num_slots must be given.  With conv_weight
+    [H, 4, 2 d_k + d_v] fp32 and conv_window (io dtype; dense
+    [num_slots, H, 3, 2 d_k + d_v] or any tensor the conv_strides (slot,
+    head, row, part) address) q, k, v are raw inputs to the short conv front
+    end (``kda_chunk_prefill_conv``); the window is updated in place.
+    events: optional three recorded
     torch.cuda.Event(enable_timing=True) objects, recorded before the
     intra-chunk kernel, between the kernels and after the scan
     (``kda_chunk_prefill_timed``).  Returns o [T, H, d_v].
@@ -189,7 +233,11 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
     if o is None:
         o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     _dev(o, "o", q.dtype, (T, H, dv))
-    desc = make_desc(T, N, H, dk, dv, num_slots, io, scale, state_slot_stride, state_head_stride)
+    conv = None
+    if conv_weight is not None:
+        conv = _conv_desc(conv_weight, conv_window, H, dk, dv, q.dtype, conv_strides)
+    desc = make_desc(T, N, H, dk, dv, num_slots, io, scale, state_slot_stride, state_head_stride,
+                     _conv_mode(conv_activation) if conv is not None else 0)
     need = int(lib.kda_prefill_workspace_size(ctypes.byref(desc)))
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -197,12 +245,16 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(state_in),
             _ptr(state_out), _ptr(o), _ptr(slots), ctypes.byref(desc), _ptr(workspace),
             workspace.numel(), _stream(stream))
-    if events is None:
-        _check(lib.kda_chunk_prefill(*args))
-    else:
+    handles = None
+    if events is not None:
         if len(events) != 3:
             raise ValueError("events must hold three torch.cuda.Event objects")
         handles = (ctypes.c_void_p * 3)(*[_event_handle(e) for e in events])
+    if conv is not None:
+        _check(lib.kda_chunk_prefill_conv(*args[:11], ctypes.byref(conv), *args[11:], handles))
+    elif handles is None:
+        _check(lib.kda_chunk_prefill(*args))
+    else:
         _check(lib.kda_chunk_prefill_timed(*args, handles))
     return o
 
@@ -216,13 +268,15 @@ def _event_handle(ev) -> int:
 
 
 def decode_step(q, k, v, g, beta, state_pool, slots, o=None, scale=1.0, stream=None,
-                num_slots=None, state_slot_stride=0, state_head_stride=0):
+                num_slots=None, state_slot_stride=0, state_head_stride=0, conv_weight=None,
+                conv_window=None, conv_activation="none", conv_strides=(0, 0, 0, 0)):
     """One token per sequence; state_pool [num_slots, H, d_v, d_k] updated in
     place (see ``kda_decode_step``).  q, k, g: [N, H, d_k]; v: [N, H, d_v];
     beta: [N, H]; slots: [N] int32.  With state_slot_stride /
     state_head_stride the pool is a flat fp32 buffer addressed by lines
-    (``kda_decode_step_lines``) and num_slots must be given.  Returns o
-    [N, H, d_v]."""
+    (``kda_decode_step_lines``) and num_slots must be given.  With
+    conv_weight and conv_window (as for chunk_prefill) the short conv runs
+    fused into the step (``kda_decode_step_conv``).  Returns o [N, H, d_v]."""
     lib = load_library()
     _dev(q, "q")
     N, H, dk = q.shape
@@ -243,10 +297,15 @@ def decode_step(q, k, v, g, beta, state_pool, slots, o=None, scale=1.0, stream=N
     if o is None:
         o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     _dev(o, "o", q.dtype, (N, H, dv))
-    _check(lib.kda_decode_step_lines(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                     _ptr(state_pool), _ptr(slots), _ptr(o), N, H, dk, dv,
-                                     num_slots, io, float(scale), int(state_slot_stride),
-                                     int(state_head_stride), _stream(stream)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(slots),
+            _ptr(o), N, H, dk, dv, num_slots, io, float(scale), int(state_slot_stride),
+            int(state_head_stride))
+    if conv_weight is not None:
+        conv = _conv_desc(conv_weight, conv_window, H, dk, dv, q.dtype, conv_strides)
+        _check(lib.kda_decode_step_conv(*args, _conv_mode(conv_activation), ctypes.byref(conv),
+                                        _stream(stream)))
+    else:
+        _check(lib.kda_decode_step_lines(*args, _stream(stream)))
     return o
 
 

@@ -219,11 +219,11 @@ def decode_tokens(q, k, v, g, beta, state_pool, slots, num_accepted=None, commit
 
 
 # ---------------------------------------------------------------------------
-# Short conv front end.  The KDA layers of the kern-k3-pp-prefill page run
-# "with per-sequence conv windows and states" (section "P: the packed
-# prefill") and its decode build fuses the conv into the step (section "D:
-# TP8 / EP8 / DCP8"); SGLang keeps the window as [slot][tap][q|k|v] bf16
-# (section "D inside SGLang").  The page's state size (the "kern" page,
+# Short conv front end.  On the prefill side of the kern-k3-pp-prefill page
+# every sequence carries a conv window next to its recurrent state (section
+# "P: the packed prefill"), its decode build fuses the conv into the step
+# (section "D: TP8 / EP8 / DCP8"), and SGLang keeps the window as
+# [slot][tap][q|k|v] bf16 (section "D inside SGLang").  The page's state size (the "kern" page,
 # section "The manifest": 19,537,920 bytes a sequence, 288 blocks of a
 # 64 KiB state plus 3 x 3 x 128 bf16) gives a window of 3 rows.  Reading: the
 # window holds a sequence's 3 most recent raw inputs, so the conv is causal,

@@ -34,7 +34,8 @@ def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for n in ("kda_chunk_prefill", "kda_decode_step", "kda_prefill_workspace_size",
               "kda_status_string", "kda_version", "kda_chunk_prefill_timed",
-              "kda_decode_step_lines", "kda_decode_tokens"):
+              "kda_decode_step_lines", "kda_decode_tokens", "kda_chunk_prefill_conv",
+              "kda_decode_step_conv"):
         assert n in names
 
 
@@ -44,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 102
+    assert lib.kda_version() == 103
     for code in range(8):
         s = lib.kda_status_string(code).decode()
         assert s and s != "unknown status"
@@ -52,10 +53,11 @@ def test_version_and_status_strings(lib):
 
 
 def _desc(**kw):
-    d = dict(T=8192, N=16, H=32, dk=128, dv=128, slots=64, io=K.KDA_BF16, scale=1.0, ss=0, hs=0)
+    d = dict(T=8192, N=16, H=32, dk=128, dv=128, slots=64, io=K.KDA_BF16, scale=1.0, ss=0, hs=0,
+             conv=0)
     d.update(kw)
     return K.make_desc(d["T"], d["N"], d["H"], d["dk"], d["dv"], d["slots"], d["io"], d["scale"],
-                       d["ss"], d["hs"])
+                       d["ss"], d["hs"], d["conv"])
 
 
 def _ws_formula(T, N, H, dk, dv, es):
@@ -167,3 +169,81 @@ def test_decode_tokens_rejects_bad_arguments(lib):
     assert _tokens(lib, acc=A + 4) == 4
     assert _tokens(lib, o=A + 2) == 4
     assert _tokens(lib, hs=128 * 128 - 4) == 2
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """The ctypes mirrors of kda_prefill_desc_t and kda_conv_t have the C
+    sizes and field offsets (checked with gcc against include/kda.h)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "layout.c"
+    fields = [("kda_prefill_desc_t", n) for n, _ in K.PrefillDesc._fields_] + \
+             [("kda_conv_t", n) for n, _ in K.ConvDesc._fields_]
+    body = "".join('printf("%%s.%%s %%zu\\n", "%s", "%s", offsetof(%s, %s));\n' % (t, f, t, f)
+                   for t, f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "kda.h"\nint main(void){\n'
+                   + body + 'printf("size.desc %zu\\nsize.conv %zu\\n", sizeof(kda_prefill_desc_t),'
+                   ' sizeof(kda_conv_t));\nreturn 0;}\n')
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = dict(line.rsplit(" ", 1) for line in subprocess.check_output([str(exe)]).decode().split("\n")
+               if line)
+    for t, cls in (("kda_prefill_desc_t", K.PrefillDesc), ("kda_conv_t", K.ConvDesc)):
+        for n, _ in cls._fields_:
+            assert int(got["%s.%s" % (t, n)]) == getattr(cls, n).offset, (t, n)
+    assert int(got["size.desc"]) == ctypes.sizeof(K.PrefillDesc)
+    assert int(got["size.conv"]) == ctypes.sizeof(K.ConvDesc)
+
+
+def _conv(w=A, win=A, ss=0, hs=0, rs=0, ps=0):
+    return K.ConvDesc(w, win, ss, hs, rs, ps)
+
+
+def _prefill_conv(lib, desc, conv, ws_bytes=1 << 40):
+    return lib.kda_chunk_prefill_conv(A, A, A, A, A, A, None, None, A, None, ctypes.byref(desc),
+                                      ctypes.byref(conv) if conv is not None else None, A,
+                                      ws_bytes, None, None)
+
+
+def test_prefill_conv_rejects_bad_arguments(lib):
+    assert _prefill(lib, _desc(conv=1)) == 1                          # conv mode without conv
+    assert _prefill_conv(lib, _desc(conv=0), _conv()) == 2            # conv entry, no mode
+    assert _prefill_conv(lib, _desc(conv=3), _conv()) == 2
+    assert _prefill_conv(lib, _desc(conv=1), None) == 1
+    assert _prefill_conv(lib, _desc(conv=1), _conv(w=None)) == 1
+    assert _prefill_conv(lib, _desc(conv=2), _conv(win=None)) == 1
+    assert _prefill_conv(lib, _desc(conv=1), _conv(win=A + 8)) == 4
+    assert _prefill_conv(lib, _desc(conv=1), _conv(ps=64)) == 2       # part stride < d_k
+    assert _prefill_conv(lib, _desc(conv=1), _conv(rs=386)) == 2      # not a multiple of 4
+    assert _prefill_conv(lib, _desc(conv=1), _conv(ss=-4)) == 2
+    d = _desc(conv=2)
+    need = lib.kda_prefill_workspace_size(ctypes.byref(d))
+    assert _prefill_conv(lib, d, _conv(), ws_bytes=need - 1) == 5
+
+
+def test_conv_workspace_size(lib):
+    up = lambda x: (x + 255) // 256 * 256
+    for T, H, dk, dv, io, es in [(8192, 32, 128, 128, K.KDA_BF16, 2), (77, 3, 128, 64, K.KDA_F32, 4)]:
+        d0 = K.make_desc(T, 2, H, dk, dv, 2, io, 1.0)
+        d1 = K.make_desc(T, 2, H, dk, dv, 2, io, 1.0, conv_mode=1)
+        extra = 256 + 2 * up(T * H * dk * es) + up(T * H * dv * es)
+        assert (lib.kda_prefill_workspace_size(ctypes.byref(d1))
+                == lib.kda_prefill_workspace_size(ctypes.byref(d0)) + extra)
+
+
+def _decode_conv(lib, mode=1, conv="ok", **kw):
+    c = _conv(**kw) if conv == "ok" else conv
+    return lib.kda_decode_step_conv(A, A, A, A, A, A, A, A, 64, 32, 128, 128, 64, K.KDA_BF16, 1.0,
+                                    0, 0, mode, ctypes.byref(c) if c is not None else None, None)
+
+
+def test_decode_conv_rejects_bad_arguments(lib):
+    assert _decode_conv(lib, mode=0) == 2
+    assert _decode_conv(lib, mode=3) == 2
+    assert _decode_conv(lib, conv=None) == 1
+    assert _decode_conv(lib, w=None) == 1
+    assert _decode_conv(lib, win=A + 4) == 4
+    assert _decode_conv(lib, ps=100) == 2
+    assert _decode_conv(lib, hs=6) == 2
