@@ -1,18 +1,23 @@
 #!/usr/bin/env python3
 """KDA prefill throughput on one MI355X, with the roofline of the dominant kernel.
 
-    python bench.py [--steps K] [--warmup W] [--workload single|packed]
+    python bench.py [--steps K] [--warmup W] [--workload single|packed|decode|decode_tokens]
+                    [--conv] [--tokens-mode MODE] [--no-extra] [--no-cpu-baseline]
 
 A step is one kda_chunk_prefill call (intra-chunk kernel + state scan) over
 one 8192-row chunk, with inputs already resident in HBM.  The default
 workload is one sequence of 8192 rows, H=32, d_k=d_v=128, bf16 q/k/v/o, fp32
 g/beta/state, zero initial state.  Inputs rotate over several device copies so
 that the 256 MB last-level cache cannot serve a step from the previous one.
+About 150 ms of untimed calls run before the W warmup steps so that clocks
+have settled; then exactly K steps are timed between two events.
 
 Prints ONE JSON line.  Besides the throughput it reports:
   roofline      the dominant kernel's algorithmic bytes per launch over its
-                average duration (HIP events recorded between the kernels on
-                the launch stream, inside the timed region), against 8 TB/s;
+                average duration, from HIP events recorded on the launch
+                stream before, between and after the kernels in a second pass
+                of K steps (the events cost a few microseconds a step, so the
+                timed steps run without them), against 8 TB/s;
   cpu_baseline  the fp64 oracle timed on the host cores on the same inputs;
   kernels       both kernels' average durations and algorithmic bytes;
   path          the whole step's algorithmic bytes per token against HBM;
@@ -120,6 +125,19 @@ def to_dev(case, copies, torch):
     return sets, dt
 
 
+def prewarm(call, torch, ms=150.0):
+    """Untimed calls for about `ms` milliseconds before the warmup steps, so
+    that clocks and first-touch costs have settled when timing starts."""
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1e3 < ms and i < 5000:
+        call(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def time_prefill(case, steps, warmup, copies, torch, lap, conv=None):
     """conv: None, or (weight [H,4,C], window pool, activation) for the short
     conv front end; each input copy gets its own window pool."""
@@ -151,20 +169,30 @@ def time_prefill(case, steps, warmup, copies, torch, lap, conv=None):
                           slots=slots, scale=case.scale, workspace=ws, events=events,
                           **ckw[i % copies])
 
+    prewarm(call, torch)
     for i in range(warmup):
         call(i)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for trio in evs:          # torch creates the underlying hipEvents on first record
-        for e in trio:
-            e.record()
+    # the timed steps: plain calls, bracketed by two events
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(steps):
-        call(i, evs[i])
+        call(i)
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
+    # per-kernel durations: the same steps again with events recorded on the
+    # launch stream before, between and after the two kernels (events between
+    # kernels cost a few microseconds a step, so they stay out of the timed
+    # steps above)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for trio in evs:          # torch creates the underlying hipEvents on first record
+        for e in trio:
+            e.record()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        call(i, evs[i])
+    torch.cuda.synchronize()
     intra = [e[0].elapsed_time(e[1]) for e in evs]
     scan = [e[1].elapsed_time(e[2]) for e in evs]
     return {
@@ -190,6 +218,8 @@ def time_decode(case, steps, warmup, copies, torch, lap, conv=None):
         w = torch.from_numpy(conv[0]).to("cuda")
         ckw = [{"conv_weight": w, "conv_window": torch.from_numpy(conv[1]).to("cuda").to(dt),
                 "conv_activation": conv[2]} for _ in range(copies)]
+    prewarm(lambda i: lap.decode_step(q, k, v, g, beta, pools[i % copies], slots, o=o,
+                                      **ckw[i % copies]), torch)
     for i in range(warmup):
         lap.decode_step(q, k, v, g, beta, pools[i % copies], slots, o=o, **ckw[i % copies])
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -234,6 +264,7 @@ def time_decode_tokens(case, steps, warmup, copies, torch, lap, only=None):
         def run(i):
             lap.decode_tokens(q, k, v, g, beta, pools[i % copies], slots,
                               o=o if kw["outputs"] else None, **kw)
+        prewarm(run, torch)
         for i in range(warmup):
             run(i)
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
