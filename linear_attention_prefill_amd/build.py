@@ -8,6 +8,7 @@ Compiles every HIP source under csrc/ plus the C ABI into
 from __future__ import annotations
 
 import argparse
+import hashlib
 import os
 import shutil
 import subprocess
@@ -27,6 +28,22 @@ CXX_SOURCES = ["kda_api.cpp"]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",
           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
+
+
+HASH_FILE = LIB + ".srchash"
+
+
+def source_hash() -> str:
+    """sha256 over the library's sources (csrc/ and include/), in name order."""
+    h = hashlib.sha256()
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC))
+             if f.endswith((".hip", ".h", ".cpp"))]
+    files += [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))]
+    for path in files:
+        h.update(os.path.relpath(path, ROOT).encode())
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def _hipcc() -> str:
@@ -74,6 +91,8 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
             *[obj for _, obj, _ in jobs]]
     subprocess.check_call(link)
     os.replace(tmp, LIB)
+    with open(HASH_FILE, "w") as fh:          # which sources this library was built from
+        fh.write(source_hash() + "\n")
     return LIB
 
 

@@ -48,7 +48,7 @@ template <typename E, int DK, int DV>
 constexpr int conv_threads() { return kConvGroups * (2 * DK + DV) / Io16<E>::kN; }
 
 template <typename E, int DK, int DV, int SILU>
-__global__ __launch_bounds__(conv_threads<E, DK, DV>()) void kda_conv_kernel(
+__global__ __launch_bounds__((conv_threads<E, DK, DV>())) void kda_conv_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     E *__restrict__ qc, E *__restrict__ kc, E *__restrict__ vc,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ slots,

@@ -30,6 +30,18 @@ def _declared_functions():
     return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
 
 
+def test_library_matches_sources():
+    """libkda.so was built from the sources in the tree (the build records a
+    hash of csrc/ and include/ next to it); a stale library would make every
+    other test check old code."""
+    from linear_attention_prefill_amd import build
+    if not os.path.exists(build.HASH_FILE):
+        build.build()
+    with open(build.HASH_FILE) as fh:
+        built = fh.read().strip()
+    assert built == build.source_hash(), "libkda.so is stale: run python -m linear_attention_prefill_amd.build"
+
+
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for n in ("kda_chunk_prefill", "kda_decode_step", "kda_prefill_workspace_size",
