@@ -41,8 +41,10 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "KDA prefill tokens/s on 1 MI355X (8192-row packed chunk) + % MFMA/HBM roof"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# sources of the two prefill kernels whose HBM traffic profiles/traffic.json
+# holds: the stored traffic is reported only while their hash matches
 KERNEL_SOURCES = [os.path.join(ROOT, "linear_attention_prefill_amd", "csrc", f)
-                  for f in ("kda_prefill.hip", "kda_device.h", "kda_decode.hip")]
+                  for f in ("kda_prefill.hip", "kda_device.h")]
 
 
 def log(msg):

@@ -197,7 +197,7 @@ kda_status_t decode_impl(const void *q, const void *k, const void *v, const floa
     if (io_dtype != KDA_F32 && io_dtype != KDA_BF16) return KDA_ERR_DTYPE;
     if (!dims_supported(d_k, d_v)) return KDA_ERR_UNSUPPORTED;
     if (num_seqs < 1 || num_heads < 1 || num_slots < 1) return KDA_ERR_SHAPE;
-    if ((long long)num_seqs * num_heads * (d_v / 64) > INT_MAX) return KDA_ERR_SHAPE;
+    if ((long long)num_seqs * num_heads * (d_v / 16) > INT_MAX) return KDA_ERR_SHAPE;   // grid of the step
     if (!q || !k || !v || !g || !beta || !state_pool || !slots || !o) return KDA_ERR_NULL;
     const void *ptrs[] = {q, k, v, g, beta, state_pool, slots, o};
     for (const void *p : ptrs)

@@ -15,12 +15,16 @@
 //   d_j = beta (v_j - s'.k)                  delta-rule correction
 //   S[:, j] = s' + d_j k                     write back in place
 //   o_j = scale (s'.q + d_j (k.q))           = scale S_new[:, j].q
-// Rows are independent, so a workgroup of 256 threads covers 64 rows of one
-// (sequence, head); a row is spread over the 16 lanes of a DPP row, each lane
-// holding d_k / 16 key channels, and the dot products are summed across those
-// lanes with four row rotations.  Every lane issues all of its row loads
-// before any arithmetic, so each workgroup keeps 64 rows (16-32 KiB) in
-// flight.
+// Rows are independent, so a workgroup of 256 threads covers a slice of the
+// rows of one (sequence, head); a row is spread over the 16 lanes of a DPP
+// row, each lane holding d_k / 16 key channels, and the dot products are
+// summed across those lanes with four row rotations.  Every lane issues all
+// of its row loads before any arithmetic.  The single-token step gives each
+// workgroup 16 rows (one pass of its 256 threads, 4-8 KiB of state): many
+// small workgroups keep more of HBM busy than fewer large ones (measured, 64
+// sequences at H = 32, d = 128: 16 rows 45 us, 32 rows 46 us, 64 rows 47 us,
+// 128 rows 49 us).  The multi-token kernel keeps 64 rows, since each of its
+// workgroups stages every token's k, q and decay once.
 //
 // Both kernels do a token's arithmetic through the same helpers, with every
 // multiply-add written out and contraction switched off, so T tokens in one
@@ -30,7 +34,8 @@
 
 namespace kda {
 
-constexpr int kDecodeRows = 64;
+constexpr int kDecodeRows = 64;    // state rows per workgroup, multi-token kernel
+constexpr int kStepRows = 16;      // state rows per workgroup, single-token step (one pass)
 
 // Sum over the 16 lanes of a DPP row, left in every lane (row_ror 8, 4, 2, 1).
 __device__ __forceinline__ float row_allreduce(float x) {
@@ -102,11 +107,11 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     const float *__restrict__ g, const float *__restrict__ beta, float *pool,
     const int32_t *__restrict__ slots, E *__restrict__ o, int N, int H, int num_slots,
     float scale, int64_t slot_stride, int64_t head_stride) {
-    constexpr int PARTS = DV / kDecodeRows;
+    constexpr int PARTS = DV / kStepRows;
     constexpr int CPL = DK / 16;         // key channels per lane
     constexpr int V4 = CPL / 4;          // float4 per lane and row
     constexpr int RPI = 256 / 16;        // rows covered by one pass of the workgroup
-    constexpr int P = kDecodeRows / RPI; // passes
+    constexpr int P = kStepRows / RPI;   // passes
     const int tid = threadIdx.x;
     const int part = blockIdx.x % PARTS;
     const int nh = blockIdx.x / PARTS;
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     float vv[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        const int row = part * kDecodeRows + p * RPI + rr;
+        const int row = part * kStepRows + p * RPI + rr;
 #pragma unroll
         for (int x = 0; x < V4; ++x)
             s[p][x] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)row * DK + 4 * (c + 16 * x)));
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(
     const float kq = token_kq<V4>(k4, q4);
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        const int row = part * kDecodeRows + p * RPI + rr;
+        const int row = part * kStepRows + p * RPI + rr;
         float dq;
         const float d = row_update<V4>(s[p], a4, k4, q4, bt, vv[p], dq);
 #pragma unroll
@@ -405,7 +410,7 @@ __global__ __launch_bounds__(256) void kda_decode_tokens_kernel(
 
 template <typename E, int DK, int DV>
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
-    const int nblocks = a.N * a.H * (DV / kDecodeRows);
+    const int nblocks = a.N * a.H * (DV / kStepRows);
     kda_decode_kernel<E, DK, DV><<<dim3(nblocks), dim3(256), 0, stream>>>(
         static_cast<const E *>(a.q), static_cast<const E *>(a.k), static_cast<const E *>(a.v),
         a.g, a.beta, a.pool, a.slots, static_cast<E *>(a.o), a.N, a.H, a.num_slots, a.scale,
