@@ -865,6 +865,219 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     }
 }
 
+// kda_scan_pair_kernel: the state scan for calls with many (sequence, head)
+// pairs, where the scan is bound by how many bytes each CU pulls from L2
+// rather than by its chain of chunks.  One workgroup of 8 waves covers 32
+// columns of d_v: waves 0..3 update columns 0..15 of the pair and waves 4..7
+// columns 16..31, exactly as the 4 waves of kda_scan_kernel do.  The chunk
+// operands both halves need (w, Q e^Gam, K~^T and A_qk, 14 fragments per
+// wave row) are loaded from the record once: each half loads 7 of them into
+// its rolling register stages and publishes them through LDS (double
+// buffered by chunk parity, written before the first barrier of a step), so
+// the workgroup moves half the L2 bytes per column of two single-slice
+// workgroups.  bf16 only (fp32 fragments would not fit two LDS buffers).
+template <typename E, int DK> struct PairStage {
+    static constexpr int KS = DK / kSlab;
+    static constexpr int TPW = DK / 64;
+    static constexpr int F = 2 * KS + 2 * TPW + 2;     // fragments per wave row
+    static constexpr int F2 = F / 2;                   // loaded by each half
+    Frag<E> f[F2];
+    typename Raw4<E>::type u;
+    float d;
+};
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(512, 1) void kda_scan_pair_kernel(
+    const E *__restrict__ ws, const float *__restrict__ ws_dec,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ slots,
+    const float *state_in, float *state_out, E *__restrict__ o,
+    int T, int N, int H, int num_slots, float scale, int64_t slot_stride, int64_t head_stride) {
+    static_assert(sizeof(E) == 2, "bf16 only");
+    constexpr int VT = DV / kSub, KS = DK / kSlab;
+    constexpr int TPW = DK / 64;
+    using L = WsLayout<E, DK, DV>;
+    using Stage = PairStage<E, DK>;
+    constexpr int F = Stage::F, F2 = Stage::F2;
+    // shared operands [parity][fragment index][wave row][lane][8]; fragment
+    // index: w slabs 0..KS-1, Q e^Gam slabs KS..2KS-1, K~^T (tile i, slab s)
+    // at 2KS + 2i + s, A_qk halves at F-2, F-1
+    __shared__ __align__(16) E sOp[2 * F * 4 * 512];
+    __shared__ __align__(16) E sSb2[2][KS * 64 * 8];
+    __shared__ __align__(16) E sUb2[2][2 * 64 * 8];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3;
+    const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);
+    const int li = lane & 15, lg = lane >> 4;
+    E *const sSb = sSb2[grp];
+    E *const sUb = sUb2[grp];
+    // Work order as in kda_scan_kernel, over pairs of 16-column slices.
+    constexpr int VP2 = VT / 2;
+    const int B = gridDim.x, b = blockIdx.x;
+    const int NP = N * H;
+    int q, jp;
+    if (NP % 8 == 0) {
+        const int k = b >> 3;
+        jp = k % VP2;
+        q = (k / VP2) * 8 + (b & 7);
+    } else {
+        jp = b % VP2;
+        q = b / VP2;
+    }
+    if (q >= NP || b >= B) return;
+    const int jt = 2 * jp + grp;
+    const int h = q % H;
+    int n = q / H;
+    if (N <= 64) {
+        const int lane_len = lane < N ? seq_span(cu, lane, T).len : -1;
+        int rank = 0;
+        for (int m = 0; m < N; ++m) {
+            const int lm = __shfl(lane_len, m);
+            rank += (lm > lane_len || (lm == lane_len && m < lane)) ? 1 : 0;
+        }
+        const unsigned long long hit = __ballot(lane < N && rank == n);
+        n = hit ? __ffsll((long long)hit) - 1 : n;
+    }
+    const int slot = slots ? slots[n] : n;
+    if (slots && (slot < 0 || slot >= num_slots)) return;   // padded sequence
+    const SeqSpan sp = seq_span(cu, n, T);
+    const int j0 = jt * kSub;
+
+    f32x4 S[TPW];
+    if (state_in) {
+        const float *src = state_in + slot * slot_stride + h * head_stride + (size_t)(j0 + li) * DK;
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+            S[i] = *reinterpret_cast<const f32x4 *>(src + (wave * TPW + i) * kSub + 4 * lg);
+    } else {
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float x = S[i][r];
+            asm volatile("" : "+v"(x));
+            S[i][r] = x;
+        }
+    }
+
+    // Record offsets (elements) of this half's fragments for this wave row:
+    // fixed for the whole scan, so refills are unconditional and branch-free.
+    auto frag_off = [&](int idx) -> int {
+        if (idx < KS) return (wave * KS + idx) * 512;
+        if (idx < 2 * KS) return L::kWElems + (wave * KS + idx - KS) * 512;
+        if (idx < 2 * KS + 2 * TPW) {
+            const int i = (idx - 2 * KS) >> 1, s = (idx - 2 * KS) & 1;
+            return L::kWElems + L::kQElems + ((wave * TPW + i) * 2 + s) * 512;
+        }
+        return L::kWElems + L::kQElems + L::kKElems + tri_frag(wave, idx - (F - 2)) * 512;
+    };
+    int offs[F2];
+#pragma unroll
+    for (int j = 0; j < F2; ++j) offs[j] = frag_off(grp * F2 + j);
+    const int u_off = L::kWElems + L::kQElems + L::kKElems + L::kAElems + jt * (64 * 16) + lane * 16 + 4 * wave;
+
+    auto rec_of = [&](int cc) { return (size_t)(sp.first_chunk + cc) * H + h; };
+    auto load_stage = [&](Stage &X, int cc) {
+        const size_t rec = rec_of(cc);
+        const E *R = ws + rec * L::kRecElems;
+#pragma unroll
+        for (int j = 0; j < F2; ++j) X.f[j] = load_frag<E>(R + offs[j], lane);
+        X.u = *reinterpret_cast<const typename Raw4<E>::type *>(R + u_off);
+        X.d = ws_dec[rec * DK + wave * (TPW * kSub) + (lane & (TPW * kSub - 1))];
+    };
+    auto op = [&](int par, int idx) -> E * { return sOp + ((par * F + idx) * 4 + wave) * 512; };
+
+    const int nch = (sp.len + kChunk - 1) / kChunk;
+    auto step = [&](Stage &X, int cc, bool refill) {
+        const int nx = cc + 3 < nch ? cc + 3 : nch - 1;
+        const int par = cc & 1;
+        // publish my state tiles and my half of this chunk's operands
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            const int t = wave * TPW + i;
+            store4<E>(sSb + ((t >> 1) * 64 + lane) * 8 + (t & 1) * 4, S[i]);
+        }
+#pragma unroll
+        for (int j = 0; j < F2; ++j) store_frag<E>(op(par, grp * F2 + j), lane, X.f[j]);
+        __syncthreads();
+        Frag<E> Sb[KS], wf[KS], qf[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            Sb[s] = load_frag<E>(sSb + s * 512, lane);
+            wf[s] = load_frag<E>(op(par, s), lane);
+        }
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+        for (int s = 0; s < KS; s += 2) {
+            mma(a0, wf[s], Sb[s]);
+            mma(a1, wf[s + 1], Sb[s + 1]);
+        }
+        const f32x4 un = to_f32<E>(X.u) - (a0 + a1);
+        const float dd = X.d;
+        if (refill) load_stage(X, nx);
+        store4<E>(sUb + ((wave >> 1) * 64 + lane) * 8 + (wave & 1) * 4, un);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qf[s] = load_frag<E>(op(par, KS + s), lane);
+        f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
+#pragma unroll
+        for (int s = 0; s < KS; s += 2) {
+            mma(o0, Sb[s], qf[s]);
+            mma(o1, Sb[s + 1], qf[s + 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[i][r] *= __shfl(dd, i * kSub + 4 * lg + r);
+        Frag<E> kf[TPW][2], af[2];
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            kf[i][0] = load_frag<E>(op(par, 2 * KS + 2 * i), lane);
+            kf[i][1] = load_frag<E>(op(par, 2 * KS + 2 * i + 1), lane);
+        }
+        af[0] = load_frag<E>(op(par, F - 2), lane);
+        af[1] = load_frag<E>(op(par, F - 1), lane);
+        __syncthreads();
+        Frag<E> ub[2];
+        ub[0] = load_frag<E>(sUb, lane);
+        ub[1] = load_frag<E>(sUb + 512, lane);
+        mma(o0, ub[0], af[0]);
+        if (wave >= 2) mma(o1, ub[1], af[1]);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) {
+            mma(S[i], kf[i][0], ub[0]);
+            mma(S[i], kf[i][1], ub[1]);
+        }
+        const int row = wave * kSub + li;
+        if (row < sp.len - cc * kChunk)
+            store4<E>(o + ((size_t)(sp.start + cc * kChunk + row) * H + h) * DV + j0 + 4 * lg,
+                      (o0 + o1) * scale);
+    };
+
+    if (nch > 0) {
+        Stage A, Bs, Cs;
+        load_stage(A, 0);
+        load_stage(Bs, nch > 1 ? 1 : 0);
+        load_stage(Cs, nch > 2 ? 2 : nch - 1);
+        int cc = 0;
+        for (; cc + 2 < nch; cc += 3) {
+            step(A, cc, true);
+            step(Bs, cc + 1, true);
+            step(Cs, cc + 2, true);
+        }
+        if (cc < nch) step(A, cc, false);
+        if (cc + 1 < nch) step(Bs, cc + 1, false);
+    }
+
+    if (state_out) {
+        float *dst = state_out + slot * slot_stride + h * head_stride + (size_t)(j0 + li) * DK;
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+            *reinterpret_cast<f32x4 *>(dst + (wave * TPW + i) * kSub + 4 * lg) = S[i];
+    }
+}
+
 template <typename E, int DK, int DV>
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     using L = WsLayout<E, DK, DV>;
@@ -881,8 +1094,21 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
             a.g, a.beta, a.cu_seqlens, a.T, a.N, a.H, ws, ws_dec);
     }
     if (a.events[1]) (void)hipEventRecord(a.events[1], stream);
-    const int nblocks = a.N * a.H * (DV / kSub);
-    kda_scan_kernel<E, DK, DV><<<dim3(nblocks), dim3(256), 0, stream>>>(
+    // Many (sequence, head) pairs: the scan is bound by L2 bytes per CU, so
+    // pairs of slices share their operands; few pairs: it is bound by its
+    // chain of chunks, and single-slice workgroups spread it over more CUs.
+    const long long slices = (long long)a.N * a.H * (DV / kSub);
+    if constexpr (sizeof(E) == 2) {
+        if (slices > 2LL * a.num_cus) {
+            kda_scan_pair_kernel<E, DK, DV><<<dim3((int)(slices / 2)), dim3(512), 0, stream>>>(
+                ws, ws_dec, a.cu_seqlens, a.slots, a.state_in, a.state_out, static_cast<E *>(a.o),
+                a.T, a.N, a.H, a.num_slots, a.scale, a.slot_stride, a.head_stride);
+            const hipError_t e = hipGetLastError();
+            if (a.events[2]) (void)hipEventRecord(a.events[2], stream);
+            return e;
+        }
+    }
+    kda_scan_kernel<E, DK, DV><<<dim3((int)slices), dim3(256), 0, stream>>>(
         ws, ws_dec, a.cu_seqlens, a.slots, a.state_in, a.state_out, static_cast<E *>(a.o),
         a.T, a.N, a.H, a.num_slots, a.scale, a.slot_stride, a.head_stride);
     const hipError_t e = hipGetLastError();
