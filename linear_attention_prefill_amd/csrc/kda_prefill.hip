@@ -872,10 +872,12 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
 // columns 16..31, exactly as the 4 waves of kda_scan_kernel do.  The chunk
 // operands both halves need (w, Q e^Gam, K~^T and A_qk, 14 fragments per
 // wave row) are loaded from the record once: each half loads 7 of them into
-// its rolling register stages and publishes them through LDS (double
-// buffered by chunk parity, written before the first barrier of a step), so
-// the workgroup moves half the L2 bytes per column of two single-slice
-// workgroups.  bf16 only (fp32 fragments would not fit two LDS buffers).
+// its rolling register stages and publishes them through LDS, double
+// buffered by chunk parity.  A chunk's operands are written right after the
+// first barrier of the step before it (the buffer of that parity has been
+// read by then), so no LDS write sits between a step's barriers and its
+// products.  The workgroup moves half the L2 bytes per column of two
+// single-slice workgroups.  bf16 only (fp32 fragments would not fit two LDS buffers).
 template <typename E, int DK> struct PairStage {
     static constexpr int KS = DK / kSlab;
     static constexpr int TPW = DK / 64;
@@ -990,18 +992,23 @@ __global__ __launch_bounds__(512, 1) void kda_scan_pair_kernel(
     auto op = [&](int par, int idx) -> E * { return sOp + ((par * F + idx) * 4 + wave) * 512; };
 
     const int nch = (sp.len + kChunk - 1) / kChunk;
-    auto step = [&](Stage &X, int cc, bool refill) {
+    auto publish = [&](const Stage &X, int cc) {
+#pragma unroll
+        for (int j = 0; j < F2; ++j) store_frag<E>(op(cc & 1, grp * F2 + j), lane, X.f[j]);
+    };
+    auto step = [&](Stage &X, const Stage &Xn, int cc, bool refill) {
         const int nx = cc + 3 < nch ? cc + 3 : nch - 1;
         const int par = cc & 1;
-        // publish my state tiles and my half of this chunk's operands
+        // publish my state tiles (this chunk's operands went out a step ago)
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int t = wave * TPW + i;
             store4<E>(sSb + ((t >> 1) * 64 + lane) * 8 + (t & 1) * 4, S[i]);
         }
-#pragma unroll
-        for (int j = 0; j < F2; ++j) store_frag<E>(op(par, grp * F2 + j), lane, X.f[j]);
         __syncthreads();
+        // the other parity's buffer was last read before this barrier:
+        // publish the next chunk's operands into it now
+        if (cc + 1 < nch) publish(Xn, cc + 1);
         Frag<E> Sb[KS], wf[KS], qf[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -1060,14 +1067,15 @@ __global__ __launch_bounds__(512, 1) void kda_scan_pair_kernel(
         load_stage(A, 0);
         load_stage(Bs, nch > 1 ? 1 : 0);
         load_stage(Cs, nch > 2 ? 2 : nch - 1);
+        publish(A, 0);
         int cc = 0;
         for (; cc + 2 < nch; cc += 3) {
-            step(A, cc, true);
-            step(Bs, cc + 1, true);
-            step(Cs, cc + 2, true);
+            step(A, Bs, cc, true);
+            step(Bs, Cs, cc + 1, true);
+            step(Cs, A, cc + 2, true);
         }
-        if (cc < nch) step(A, cc, false);
-        if (cc + 1 < nch) step(Bs, cc + 1, false);
+        if (cc < nch) step(A, Bs, cc, false);
+        if (cc + 1 < nch) step(Bs, Cs, cc + 1, false);
     }
 
     if (state_out) {
