@@ -29,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -53,10 +54,14 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the prefill kernels' code, comments and blank lines removed
+    (editing a comment leaves the kernels, and their traffic, unchanged)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 

@@ -38,7 +38,10 @@
 // exchange.  Wave w owns chunk rows 16w..16w+15 and a quarter of the key
 // channels, swaps the rounded copies of its S and U tiles with the other
 // waves through LDS, and keeps the operands of the next chunks in flight in
-// registers.
+// registers.  kda_scan_pair_kernel: the same scan for bf16 calls with more
+// than two slices per CU, where L2 bytes per CU rather than the chain of
+// chunks set the time; one 8-wave workgroup covers two slices and loads the
+// shared chunk operands once, passing them between its halves through LDS.
 #include "kda_device.h"
 #include "kda_launch.h"
 
