@@ -9,9 +9,9 @@
 //
 // kda_conv_kernel writes the convolved q, k, v (io dtype) for the intra-chunk
 // kernel to read in place of the raw inputs.  A workgroup covers 64 rows of
-// one head, heads varying fastest across the grid: 8 groups of 8 rows times
+// one head, heads varying fastest across the grid: 4 groups of 16 rows times
 // (2 d_k + d_v) / 8 channel octets (quads for fp32), one thread each.  A
-// thread loads its 8 rows and the 3 before them up front (indices clamped, so
+// thread loads its 16 rows and the 3 before them up front (indices clamped, so
 // no load is conditional) and rolls the taps along the rows when all of them
 // lie in one sequence; the few groups that touch a
 // sequence start or end go row by row, reading the window where the three
@@ -25,8 +25,8 @@
 
 namespace kda {
 
-constexpr int kConvRows = 8;        // rows per thread
-constexpr int kConvGroups = 8;      // row groups per 64-row block
+constexpr int kConvRows = 16;       // rows per thread
+constexpr int kConvGroups = 4;      // row groups per 64-row block
 
 // 16 bytes of io values: every load and store of the conv pass moves whole
 // 16-byte pieces per lane (narrower bf16 stores reach L2 as partial lines).
