@@ -74,7 +74,7 @@ kda_status_t check_desc(const kda_prefill_desc_t *d) {
     if (d->total_rows < 0 || d->num_seqs < 1 || d->num_heads < 1 || d->num_slots < 0)
         return KDA_ERR_SHAPE;
     if (d->conv_mode < KDA_CONV_NONE || d->conv_mode > KDA_CONV_SILU) return KDA_ERR_SHAPE;
-    if (d->num_heads > 65535) return KDA_ERR_SHAPE;                       // grid.y of the intra kernel
+    if (d->num_heads > 65535) return KDA_ERR_SHAPE;                       // grid.y of the window kernel
     const long long chunks = (long long)d->total_rows / 64 + d->num_seqs;
     if (chunks > INT_MAX) return KDA_ERR_SHAPE;
     if ((long long)d->num_seqs * d->num_heads * (d->d_v / 16) > INT_MAX) return KDA_ERR_SHAPE;

@@ -142,7 +142,19 @@ def make_desc(T, N, H, d_k, d_v, num_slots, io_dtype, scale=1.0, slot_stride=0,
                        int(conv_mode), 0)
 
 
-def _conv_desc(weight, window, H, dk, dv, dtype, strides):
+def conv_extent(num_slots, H, d_k, d_v, strides) -> int:
+    """Elements a conv window pool must hold for the given (slot, head, row,
+    part) strides, zeros meaning the dense layout (kda.h, kda_conv_t)."""
+    C = 2 * d_k + d_v
+    ss, hs, rs, ps = (int(x) for x in strides)
+    ps = ps or d_k
+    rs = rs or C
+    hs = hs or 3 * C
+    ss = ss or H * hs
+    return (num_slots - 1) * ss + (H - 1) * hs + 2 * rs + max(ps + d_k, 2 * ps + d_v)
+
+
+def _conv_desc(weight, window, H, dk, dv, dtype, strides, num_slots):
     """Checks the conv taps and window tensors and packs a kda_conv_t."""
     C = 2 * dk + dv
     _dev(weight, "conv_weight", torch.float32, (H, 4, C))
@@ -150,9 +162,13 @@ def _conv_desc(weight, window, H, dk, dv, dtype, strides):
         raise ValueError("conv_window is required with conv_weight")
     _dev(window, "conv_window", dtype)
     ss, hs, rs, ps = (int(x) for x in strides)
-    if not any((ss, hs, rs, ps)) and tuple(window.shape[1:]) != (H, 3, C):
-        raise ValueError("a dense conv_window must be [num_slots, %d, 3, %d], got %s"
-                         % (H, C, tuple(window.shape)))
+    if not any((ss, hs, rs, ps)):
+        if window.dim() != 4 or tuple(window.shape[1:]) != (H, 3, C) or window.shape[0] < num_slots:
+            raise ValueError("a dense conv_window must be [>= %d, %d, 3, %d], got %s"
+                             % (num_slots, H, C, tuple(window.shape)))
+    elif window.numel() < conv_extent(num_slots, H, dk, dv, strides):
+        raise ValueError("conv_window holds %d elements, the strides need %d"
+                         % (window.numel(), conv_extent(num_slots, H, dk, dv, strides)))
     return ConvDesc(weight.data_ptr(), window.data_ptr(), ss, hs, rs, ps)
 
 
@@ -235,7 +251,7 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
     _dev(o, "o", q.dtype, (T, H, dv))
     conv = None
     if conv_weight is not None:
-        conv = _conv_desc(conv_weight, conv_window, H, dk, dv, q.dtype, conv_strides)
+        conv = _conv_desc(conv_weight, conv_window, H, dk, dv, q.dtype, conv_strides, num_slots)
     desc = make_desc(T, N, H, dk, dv, num_slots, io, scale, state_slot_stride, state_head_stride,
                      _conv_mode(conv_activation) if conv is not None else 0)
     need = int(lib.kda_prefill_workspace_size(ctypes.byref(desc)))
@@ -301,7 +317,7 @@ def decode_step(q, k, v, g, beta, state_pool, slots, o=None, scale=1.0, stream=N
             _ptr(o), N, H, dk, dv, num_slots, io, float(scale), int(state_slot_stride),
             int(state_head_stride))
     if conv_weight is not None:
-        conv = _conv_desc(conv_weight, conv_window, H, dk, dv, q.dtype, conv_strides)
+        conv = _conv_desc(conv_weight, conv_window, H, dk, dv, q.dtype, conv_strides, num_slots)
         _check(lib.kda_decode_step_conv(*args, _conv_mode(conv_activation), ctypes.byref(conv),
                                         _stream(stream)))
     else:

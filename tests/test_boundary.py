@@ -259,3 +259,17 @@ def test_decode_conv_rejects_bad_arguments(lib):
     assert _decode_conv(lib, win=A + 4) == 4
     assert _decode_conv(lib, ps=100) == 2
     assert _decode_conv(lib, hs=6) == 2
+
+
+def test_conv_extent_matches_the_layouts():
+    """Dense, tap-major and hybrid-page windows need exactly the elements
+    their tensors hold (the binding refuses smaller ones)."""
+    for S, H, dk, dv in [(6, 4, 128, 128), (3, 2, 64, 128), (1, 32, 128, 64)]:
+        C = 2 * dk + dv
+        assert K.conv_extent(S, H, dk, dv, (0, 0, 0, 0)) == S * H * 3 * C
+    S, H, d = 5, 4, 128
+    C = 3 * d
+    assert K.conv_extent(S, H, d, d, (3 * H * C, d, H * C, H * d)) == S * 3 * H * C
+    # a window right after each head's 64 KiB state in 884,736-byte pages
+    ss, hs = 2 * (884736 // 4), 2 * (67840 // 4)
+    assert K.conv_extent(4, 12, d, d, (ss, hs, C, d)) == 3 * ss + 11 * hs + 3 * C
