@@ -274,3 +274,40 @@ def test_many_pairs_shared_operand_scan(dk, dv):
     o_g, _, _, _, _ = _check_case(c)
     cu = c.cu_seqlens
     assert np.all(o_g[cu[5]:cu[6]] == 3.0)           # the padded sequence keeps its rows
+
+
+def test_malformed_device_data_stays_in_bounds():
+    """Non-monotone cu_seqlens and duplicate slots give unspecified results
+    (kda.h), but the kernels clamp them: nothing outside the buffers is
+    touched.  o and the pool sit inside guard regions that must come back
+    unchanged, and slots no sequence names keep their bytes."""
+    T, H, d, S = 500, 2, 64, 5
+    c = W.random_case(501, [T], H=H, d_k=d, d_v=d, io_dtype="bf16", num_slots=S)
+    cu = np.array([0, 300, 100, 500, 480], dtype=np.int32)       # not monotone
+    slots = np.array([1, 1, 7, 2], dtype=np.int32)                # duplicate and out of range
+    dt = torch.bfloat16
+    guard = 4096
+    o_buf = torch.full((guard + T * H * d + guard,), 9.0, dtype=dt, device="cuda")
+    p_buf = torch.full((guard + S * H * d * d + guard,), -3.0, dtype=torch.float32, device="cuda")
+    o = o_buf[guard:guard + T * H * d].view(T, H, d)
+    pool = p_buf[guard:guard + S * H * d * d].view(S, H, d, d)
+    pool.copy_(dev(c.state_pool))
+    weight, window = W.draw_conv(502, S, H, d, d, "bf16")
+    w_buf = torch.full((guard + window.size + guard,), 5.0, dtype=dt, device="cuda")
+    win = w_buf[guard:guard + window.size].view(window.shape)
+    win.copy_(dev(window, dt))
+    announce("malformed cu_seqlens and slots")
+    for conv in (False, True):
+        kw = dict(conv_weight=dev(weight), conv_window=win, conv_activation="silu") if conv else {}
+        lap.chunk_prefill(dev(c.q, dt), dev(c.k, dt), dev(c.v, dt), dev(c.g), dev(c.beta),
+                          dev(cu), state_in=pool, state_out=pool, o=o, slots=dev(slots),
+                          num_slots=S, **kw)
+        torch.cuda.synchronize()
+    for buf, val in ((o_buf, 9.0), (p_buf, -3.0), (w_buf, 5.0)):
+        assert torch.all(buf[:guard] == val) and torch.all(buf[-guard:] == val)
+    p = pool.cpu().numpy()
+    for s in (0, 3, 4):                                            # named by no sequence
+        np.testing.assert_array_equal(p[s], c.state_pool[s])
+    wn = win.float().cpu().numpy()
+    for s in (0, 3, 4):
+        np.testing.assert_array_equal(wn[s], window[s])
