@@ -311,3 +311,20 @@ def test_malformed_device_data_stays_in_bounds():
     wn = win.float().cpu().numpy()
     for s in (0, 3, 4):
         np.testing.assert_array_equal(wn[s], window[s])
+
+
+@pytest.mark.parametrize("n,io", [(100, "bf16"), (300, "f32"), (300, "bf16")])
+def test_many_sequences(n, io):
+    """Sequence bounds beyond the register path of the intra kernel: 100
+    sequences (bounds in LDS) and 300 (scalar loads), short and ragged, with
+    empty ones and padded slots."""
+    rng = np.random.default_rng(600 + n)
+    lengths = [int(x) for x in rng.integers(0, 41, size=n)]
+    slots = [int(s) for s in rng.permutation(n + 10)[:n]]
+    slots[3] = -1
+    c = W.random_case(610 + n, lengths, H=2, d_k=64, d_v=64, io_dtype=io, num_slots=n + 10,
+                      slots=slots)
+    announce("many sequences %s" % c.name)
+    o_g, _, _, _, _ = _check_case(c)
+    cu = c.cu_seqlens
+    assert np.all(o_g[cu[3]:cu[4]] == 3.0)
