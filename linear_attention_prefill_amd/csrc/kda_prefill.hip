@@ -56,6 +56,7 @@ namespace kda {
 constexpr float kDiagSpanLimit = 64.f;
 constexpr int kIntraThreads = 512;     // 8 waves: two per SIMD
 constexpr int kCuCache = 256;          // sequence bounds kept in LDS when N < this
+constexpr int kScanWarmAhead = 2;      // chunks between a scan stage's record and the one it warms
 
 // LDS of the intra-chunk kernel.  For bf16, K e^Gam, Q e^Gam and V are staged
 // as row-major tiles and read back as fragments; for fp32 (twice the bytes)
@@ -672,7 +673,47 @@ template <typename E, int DK> struct ScanStage {
     Frag<E> wf[KS], qf[KS], af[2], kf[TPW][2];
     typename Raw4<E>::type u;                  // raw: converted where it is used
     float d;                                   // e^{Gam_C} of key row 16 TPW wave + (lane % (16 TPW))
+    int pf;                                    // L2 warm-up word (first stage of the rotation only)
 };
+
+// Work order of the scan kernels.  Sequences are taken longest first (for up
+// to 64 sequences; every wave ranks them the same way), then head by head;
+// (sequence, head) pairs are dealt round robin to the 8 XCDs (workgroups go
+// to XCD b % 8), so each XCD gets an equal share of every sequence, while the
+// JT column groups of one pair stay on one XCD and share its L2.
+struct ScanWork {
+    int n, h, j;        // sequence (by rank), head, column group
+    bool valid;
+};
+__device__ __forceinline__ ScanWork scan_work(int b, int B, int N, int H, int JT, const int32_t *cu,
+                                              int T, int lane) {
+    const int NP = N * H;
+    int q, j;
+    if (NP % 8 == 0) {
+        const int k = b >> 3;
+        j = k % JT;
+        q = (k / JT) * 8 + (b & 7);
+    } else {
+        j = b % JT;
+        q = b / JT;
+    }
+    ScanWork w{0, 0, j, q < NP && b < B};
+    if (!w.valid) return w;
+    w.h = q % H;
+    int n = q / H;
+    if (N <= 64) {
+        const int lane_len = lane < N ? seq_span(cu, lane, T).len : -1;
+        int rank = 0;
+        for (int m = 0; m < N; ++m) {
+            const int lm = __shfl(lane_len, m);
+            rank += (lm > lane_len || (lm == lane_len && m < lane)) ? 1 : 0;
+        }
+        const unsigned long long hit = __ballot(lane < N && rank == n);
+        n = hit ? __ffsll((long long)hit) - 1 : n;
+    }
+    w.n = n;
+    return w;
+}
 
 template <typename E, int DK, int DV>
 __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
@@ -690,35 +731,9 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
-    // Work order.  Sequences are taken longest first (for up to 64 sequences;
-    // every wave ranks them the same way), then head by head; (sequence,
-    // head) pairs are dealt round robin to the 8 XCDs (workgroups go to XCD
-    // b % 8), so each XCD gets an equal share of every sequence, while the
-    // d_v slices of one pair stay on one XCD and share its L2.
-    const int B = gridDim.x, b = blockIdx.x;
-    const int NP = N * H;
-    int q, jt;
-    if (NP % 8 == 0) {
-        const int k = b >> 3;
-        jt = k % VT;
-        q = (k / VT) * 8 + (b & 7);
-    } else {
-        jt = b % VT;
-        q = b / VT;
-    }
-    if (q >= NP || b >= B) return;
-    const int h = q % H;
-    int n = q / H;                                      // rank of the sequence
-    if (N <= 64) {
-        const int lane_len = lane < N ? seq_span(cu, lane, T).len : -1;
-        int rank = 0;
-        for (int m = 0; m < N; ++m) {
-            const int lm = __shfl(lane_len, m);
-            rank += (lm > lane_len || (lm == lane_len && m < lane)) ? 1 : 0;
-        }
-        const unsigned long long hit = __ballot(lane < N && rank == n);
-        n = hit ? __ffsll((long long)hit) - 1 : n;
-    }
+    const ScanWork wk = scan_work(blockIdx.x, gridDim.x, N, H, VT, cu, T, lane);
+    if (!wk.valid) return;
+    const int h = wk.h, n = wk.n, jt = wk.j;
     const int slot = slots ? slots[n] : n;
     if (slots && (slot < 0 || slot >= num_slots)) return;   // padded sequence
     const SeqSpan sp = seq_span(cu, n, T);
@@ -751,8 +766,24 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     // chunk three ahead as soon as its last use in the current step has been
     // issued, so loads trickle out between the matrix-core products instead
     // of queueing behind them in one burst.
+    const int nch = (sp.len + kChunk - 1) / kChunk;
     auto rec_of = [&](int cc) { return (size_t)(sp.first_chunk + cc) * H + h; };
-    auto load_w = [&](Stage &X, int cc) {
+    // L2 warm-up.  All slices of a head ask for the same record lines at
+    // about the same time, so without it most operand loads wait on an L2
+    // miss still in flight.  Whenever the first stage of the rotation is
+    // refilled with chunk c, the waves of the head's slices touch the
+    // 128-byte lines of the records of chunks c + kScanWarmAhead .. + 2 (one
+    // word per lane and line, the lines dealt over every lane of those
+    // waves), so the operand loads mostly hit in L2.  The word is consumed
+    // when the stage is, three steps later, so nothing waits for it.
+    constexpr int kRecLines = (int)((L::kRecElems * sizeof(E) + 127) / 128);
+    const int pf_slot = min(lane * (VT * 4) + jt * 4 + wave, 3 * kRecLines - 1);
+    const int pf_rec = pf_slot / kRecLines, pf_line = pf_slot % kRecLines;
+    auto load_w = [&](Stage &X, int cc, bool warm) {
+        if (warm) {
+            const int cw = min(cc + kScanWarmAhead + pf_rec, nch - 1);
+            X.pf = reinterpret_cast<const int *>(ws + rec_of(cw) * L::kRecElems)[pf_line * 32];
+        }
         const E *Rw = ws + rec_of(cc) * L::kRecElems;
 #pragma unroll
         for (int s = 0; s < KS; ++s) X.wf[s] = load_frag<E>(Rw + (wave * KS + s) * 512, lane);
@@ -779,18 +810,17 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
         // this wave's 16 TPW decay factors, one per lane (lanes repeat them)
         X.d = ws_dec[rec * DK + wave * (TPW * kSub) + (lane & (TPW * kSub - 1))];
     };
-    auto load_stage = [&](Stage &X, int cc) {
-        load_w(X, cc);
+    auto load_stage = [&](Stage &X, int cc, bool warm) {
+        load_w(X, cc, warm);
         load_k(X, cc);
         load_q(X, cc);
     };
 
-    const int nch = (sp.len + kChunk - 1) / kChunk;
     // Refills are unconditional (clamped to the last chunk) inside the main
     // loop: a conditional load would leave a stage register holding either
     // the old or the new value, and the copy that merges them waits for
     // every load in flight.
-    auto step = [&](Stage &X, int cc, bool refill) {
+    auto step = [&](Stage &X, int cc, bool refill, bool warm) {
         const int nx = cc + 3 < nch ? cc + 3 : nch - 1;
         // publish my state tiles (rounded to E) and read every slab
 #pragma unroll
@@ -799,6 +829,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
             store4<E>(sSb + ((t >> 1) * 64 + lane) * 8 + (t & 1) * 4, S[i]);
         }
         __syncthreads();
+        if (warm) asm volatile("" ::"v"(X.pf));   // the warm-up word, loaded three steps ago
         Frag<E> Sb[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) Sb[s] = load_frag<E>(sSb + s * 512, lane);
@@ -810,7 +841,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
             mma(a1, X.wf[s + 1], Sb[s + 1]);
         }
         const f32x4 un = to_f32<E>(X.u) - (a0 + a1);
-        if (refill) load_w(X, nx);
+        if (refill) load_w(X, nx, warm);
         store4<E>(sUb + ((wave >> 1) * 64 + lane) * 8 + (wave & 1) * 4, un);
         // Q~ S part of the output does not need U: issue it before the barrier
         f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
@@ -847,17 +878,17 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
 
     if (nch > 0) {
         Stage A, Bs, Cs;
-        load_stage(A, 0);
-        load_stage(Bs, nch > 1 ? 1 : 0);
-        load_stage(Cs, nch > 2 ? 2 : nch - 1);
+        load_stage(A, 0, true);
+        load_stage(Bs, nch > 1 ? 1 : 0, false);
+        load_stage(Cs, nch > 2 ? 2 : nch - 1, false);
         int cc = 0;
         for (; cc + 2 < nch; cc += 3) {
-            step(A, cc, true);
-            step(Bs, cc + 1, true);
-            step(Cs, cc + 2, true);
+            step(A, cc, true, true);
+            step(Bs, cc + 1, true, false);
+            step(Cs, cc + 2, true, false);
         }
-        if (cc < nch) step(A, cc, false);
-        if (cc + 1 < nch) step(Bs, cc + 1, false);
+        if (cc < nch) step(A, cc, false, true);
+        if (cc + 1 < nch) step(Bs, cc + 1, false, false);
     }
 
     if (state_out) {
@@ -915,33 +946,11 @@ __global__ __launch_bounds__(512, 1) void kda_scan_pair_kernel(
     const int li = lane & 15, lg = lane >> 4;
     E *const sSb = sSb2[grp];
     E *const sUb = sUb2[grp];
-    // Work order as in kda_scan_kernel, over pairs of 16-column slices.
-    constexpr int VP2 = VT / 2;
-    const int B = gridDim.x, b = blockIdx.x;
-    const int NP = N * H;
-    int q, jp;
-    if (NP % 8 == 0) {
-        const int k = b >> 3;
-        jp = k % VP2;
-        q = (k / VP2) * 8 + (b & 7);
-    } else {
-        jp = b % VP2;
-        q = b / VP2;
-    }
-    if (q >= NP || b >= B) return;
-    const int jt = 2 * jp + grp;
-    const int h = q % H;
-    int n = q / H;
-    if (N <= 64) {
-        const int lane_len = lane < N ? seq_span(cu, lane, T).len : -1;
-        int rank = 0;
-        for (int m = 0; m < N; ++m) {
-            const int lm = __shfl(lane_len, m);
-            rank += (lm > lane_len || (lm == lane_len && m < lane)) ? 1 : 0;
-        }
-        const unsigned long long hit = __ballot(lane < N && rank == n);
-        n = hit ? __ffsll((long long)hit) - 1 : n;
-    }
+    // work order over pairs of 16-column slices
+    const ScanWork wk = scan_work(blockIdx.x, gridDim.x, N, H, VT / 2, cu, T, lane);
+    if (!wk.valid) return;
+    const int jt = 2 * wk.j + grp;
+    const int h = wk.h, n = wk.n;
     const int slot = slots ? slots[n] : n;
     if (slots && (slot < 0 || slot >= num_slots)) return;   // padded sequence
     const SeqSpan sp = seq_span(cu, n, T);
