@@ -735,7 +735,8 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     __shared__ __align__(16) E sSb[KS * 64 * 8];
     __shared__ __align__(16) E sUb[2 * 64 * 8];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, lg = lane >> 4;
     const ScanWork wk = scan_work(blockIdx.x, gridDim.x, N, H, VT, cu, T, lane);
     if (!wk.valid) return;
@@ -778,13 +779,13 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     // about the same time, so without it most operand loads wait on an L2
     // miss still in flight.  Whenever the first stage of the rotation is
     // refilled with chunk c, the waves of the head's slices touch the
-    // 128-byte lines of the records of chunks c + kScanWarmAhead .. + 2 (one
-    // word per lane and line, the lines dealt over every lane of those
-    // waves), so the operand loads mostly hit in L2.  The word is consumed
-    // when the stage is, three steps later, so nothing waits for it.
+    // 128-byte lines of the records of chunks c + kScanWarmAhead .. + 2: the
+    // VT * 4 waves take the three records in turn, 64 lines a wave and one
+    // word a lane, so the operand loads mostly hit in L2.  The word is
+    // consumed when the stage is, three steps later, so nothing waits for it.
     constexpr int kRecLines = (int)((L::kRecElems * sizeof(E) + 127) / 128);
-    const int pf_slot = min(lane * (VT * 4) + jt * 4 + wave, 3 * kRecLines - 1);
-    const int pf_rec = pf_slot / kRecLines, pf_line = pf_slot % kRecLines;
+    const int pf_wave = jt * 4 + wave;                 // uniform
+    const int pf_rec = pf_wave % 3, pf_line = min((pf_wave / 3) * 64 + lane, kRecLines - 1);
     auto load_w = [&](Stage &X, int cc, bool warm) {
         if (warm) {
             const int cw = min(cc + kScanWarmAhead + pf_rec, nch - 1);
