@@ -58,27 +58,29 @@ constexpr int kIntraThreads = 512;     // 8 waves: two per SIMD
 constexpr int kCuCache = 256;          // sequence bounds kept in LDS when N < this
 constexpr int kScanWarmAhead = 2;      // chunks between a scan stage's record and the one it warms
 
-// LDS of the intra-chunk kernel.  For bf16, K e^Gam, Q e^Gam and V are staged
-// as row-major tiles and read back as fragments; for fp32 (twice the bytes)
-// K e^Gam and Q e^Gam are rebuilt from k P, q P and e^{Gam_s}, and V is read
-// from global memory in fragment order.
+// LDS of the intra-chunk kernel.  For bf16, V is staged as a row-major tile
+// and read back as fragments; for fp32 (twice the bytes) it is read from
+// global memory in fragment order.  K e^Gam and Q e^Gam are not staged: they
+// are rebuilt from k P, q P and e^{Gam_s} where they are used (Q e^Gam by
+// waves that would otherwise wait on the first inverse level, K e^Gam as the
+// w product's operand), which keeps their products and stores out of the
+// VALU-bound factor phase and 34 KB out of LDS.
 template <typename E, int DK, int DV> struct IntraLds {
-    static constexpr bool kStage = sizeof(E) == 2;  // K e^Gam and V staged in LDS
-    // Pitches.  A k P / q P / K e^Gam / Q e^Gam row of d_k + 4 elements
+    static constexpr bool kStage = sizeof(E) == 2;  // V staged in LDS
+    // Pitches.  A k P / q P row of d_k + 4 elements
     // (4 mod 8) spreads the factor phase's row writes and the fragment reads
     // over the LDS banks: against d_k + 8 (bf16) it stalls a third fewer
     // cycles on bank conflicts and the kernel runs 9% faster; against d_k
     // (fp32) 7% faster.  Those rows are only accessed in 8-byte (bf16) or
     // 16-byte (fp32) runs.  V rows keep d_v + 8, since V is staged with
     // 16-byte row stores.
-    static constexpr int KPP = DK + 4;              // pitch of k P, q P, K e^Gam, Q e^Gam (E)
+    static constexpr int KPP = DK + 4;              // pitch of k P, q P (E)
     static constexpr int KQP = DK + 4;              // pitch of k Qf (fp32)
     static constexpr int VP = DV + (sizeof(E) == 2 ? 8 : 0);   // pitch of V (E)
     static constexpr int AP = 68;                   // pitch of A_kk -> Tm (fp32)
     static constexpr int T2P = 36;                  // pitch of Tm[32:64, 0:32] (fp32)
     static constexpr int DP = 16;                   // pitch of the diagonal A_kk blocks (fp32)
     static constexpr int T2D_BYTES = 32 * T2P * 4 > 4 * kSub * DP * 4 ? 32 * T2P * 4 : 4 * kSub * DP * 4;
-    static constexpr int X_ELEMS = kStage ? kChunk * KPP : 8;   // also the size of Q e^Gam
     static constexpr int V_ELEMS = kStage ? kChunk * VP : 8;
 };
 
@@ -152,8 +154,6 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
 
     __shared__ __align__(16) E sKP[kChunk * KPP];      // k P
     __shared__ __align__(16) E sQP[kChunk * KPP];      // q P
-    __shared__ __align__(16) E sX[LD::X_ELEMS];        // K e^Gam
-    __shared__ __align__(16) E sQh[LD::X_ELEMS];       // Q e^Gam
     __shared__ __align__(16) E sV[LD::V_ELEMS];        // V
     __shared__ __align__(16) float sKQ[kChunk * KQP];  // k Qf (fp32)
     __shared__ __align__(16) float sA[kChunk * AP];    // A_kk -> Tm
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
                 const int row = 4 * r4 + r;
                 const f32x4 gam = ex + gl[r];
                 const f32x4 kf = to_f32<E>(kr[r]), qf = to_f32<E>(qr[r]);
-                f32x4 kp, qp, kq, qh, xh;
+                f32x4 kp, qp, kq;
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     const float P = fast_exp2(gam[x] - Gs[x]);
@@ -338,15 +338,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
                     kp[x] = kf[x] * P;
                     qp[x] = qf[x] * P;
                     kq[x] = kf[x] * Qf;
-                    qh[x] = qp[x] * ebs[x];
-                    xh[x] = kp[x] * ebs[x];
                 }
                 store4<E>(sKP + row * KPP + ch0, kp);
                 store4<E>(sQP + row * KPP + ch0, qp);
-                if constexpr (LD::kStage) {
-                    store4<E>(sX + row * KPP + ch0, xh);
-                    store4<E>(sQh + row * KPP + ch0, qh);
-                }
                 *reinterpret_cast<f32x4 *>(sKQ + row * KQP + ch0) = kq;
             }
             // F_IJ = e^{Gam_s(I) - Gam_e(J)}, pair I (I + 1) / 2 + J = r, on lanes r < 10
@@ -510,20 +504,16 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
 
         // ---- off-diagonal blocks of Tm on fp32 matrix cores ----
         // level 1 (waves 0, 1), in place: Tm_10 = -Tm_11 (A_10 Tm_00), Tm_32 = -Tm_33 (A_32 Tm_22).
-        // Meanwhile waves 2..7 write Q e^Gam in the scan's fragment order:
-        // fragment (m, s) holds row 16m + i, channels 32s + kk(g, e).
+        // Meanwhile waves 2..7 write Q e^Gam = (q P) e^{Gam_s} in the scan's
+        // fragment order: fragment (m, s) holds row 16m + i, channels
+        // 32s + kk(g, e).
         if (wave >= 2) {
             for (int f = wave - 2; f < 4 * KS; f += 6) {
                 const int row = (f / KS) * kSub + li, c0 = (f % KS) * kSlab + 4 * lg;
-                Frag<E> fr;
-                if constexpr (LD::kStage) {
-                    fr = frag_from_runs<E>(sQh + row * KPP + c0, sQh + row * KPP + c0 + 16);
-                } else {
-                    fr = frag_from_runs<E>(sQP + row * KPP + c0, sQP + row * KPP + c0 + 16);
-                    const float *eb = sBs + (f / KS) * DK + c0;
+                Frag<E> fr = frag_from_runs<E>(sQP + row * KPP + c0, sQP + row * KPP + c0 + 16);
+                const float *eb = sBs + (f / KS) * DK + c0;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) fr.set(e, fr.get(e) * eb[(e & 3) + 16 * (e >> 2)]);
-                }
+                for (int e = 0; e < 8; ++e) fr.set(e, fr.get(e) * eb[(e & 3) + 16 * (e >> 2)]);
                 store_frag<E>(Rq + f * 512, lane, fr);
             }
         }
@@ -640,14 +630,10 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
                 for (int s = 0; s < 2; ++s) {
                     if (s > smax) continue;
                     const int n0 = (2 * wslab + nn) * kSub;
-                    if constexpr (LD::kStage) {
-                        xf[nn][s] = frag_cols<E>(sX, KPP, s * kSlab, n0, lane);
-                    } else {
-                        xf[nn][s] = frag_cols<E>(sKP, KPP, s * kSlab, n0, lane);
+                    xf[nn][s] = frag_cols<E>(sKP, KPP, s * kSlab, n0, lane);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            xf[nn][s].set(e, xf[nn][s].get(e) * sBs[(2 * s + (e >> 2)) * DK + n0 + li]);
-                    }
+                    for (int e = 0; e < 8; ++e)
+                        xf[nn][s].set(e, xf[nn][s].get(e) * sBs[(2 * s + (e >> 2)) * DK + n0 + li]);
                 }
 #pragma unroll
             for (int mi = 0; mi < MPW; ++mi) {
