@@ -175,37 +175,63 @@ def test_packed_varlen_prefill_full():
 
 @pytest.mark.timeout(900)
 def test_long_context_continuation():
-    """262144 tokens as 32 consecutive 8192-row calls, state carried in a
-    one-slot pool; slow decay.  The oracle checks sampled (head, value
-    column) pairs over the whole sequence (value columns evolve
-    independently), on the final state and on the last call's o."""
+    """262144 tokens, run twice: as 32 consecutive 8192-row calls with the
+    state carried in a one-slot pool, and as one 262144-row call (4096 chunks
+    in one scan chain, element offsets past 2^31).  Slow decay.  The oracle
+    checks sampled (head, value column) pairs over the whole sequence (value
+    columns evolve independently), on the final state and on the last 8192
+    rows of o."""
     heads = [0, 13, 31]
     cols = [0, 37, 64, 127]
     H, d, n_calls = 32, 128, W.LONG_CONTEXT_CALLS
-    pool = torch.zeros((1, H, d, d), dtype=torch.float32, device="cuda")
+    L = 8192
+    T = n_calls * L
+    Q = torch.empty((T, H, d), dtype=torch.bfloat16, device="cuda")
+    K = torch.empty_like(Q)
+    V = torch.empty_like(Q)
+    G = torch.empty((T, H, d), dtype=torch.float32, device="cuda")
+    B = torch.empty((T, H), dtype=torch.float32, device="cuda")
     qs, ks, vs, gs, bs = [], [], [], [], []
-    o_last = None
     for c_idx in range(n_calls):
         c = W.long_context_call(c_idx)
-        announce("prefill %s (carried state)" % c.name)
-        o = lap.chunk_prefill(dev(c.q, torch.bfloat16), dev(c.k, torch.bfloat16),
-                              dev(c.v, torch.bfloat16), dev(c.g), dev(c.beta),
-                              dev(c.cu_seqlens), state_in=pool, state_out=pool,
-                              slots=dev(c.slots))
-        torch.cuda.synchronize()
-        if c_idx == n_calls - 1:
-            o_last = o.float().cpu().numpy()
+        rows = slice(c_idx * L, (c_idx + 1) * L)
+        Q[rows] = dev(c.q, torch.bfloat16)
+        K[rows] = dev(c.k, torch.bfloat16)
+        V[rows] = dev(c.v, torch.bfloat16)
+        G[rows] = dev(c.g)
+        B[rows] = dev(c.beta)
         qs.append(c.q[:, heads]); ks.append(c.k[:, heads]); gs.append(c.g[:, heads])
         vs.append(c.v[:, heads][:, :, cols]); bs.append(c.beta[:, heads])
+    cu_call = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+    slot0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pool = torch.zeros((1, H, d, d), dtype=torch.float32, device="cuda")
+    o_chain = None
+    for c_idx in range(n_calls):
+        rows = slice(c_idx * L, (c_idx + 1) * L)
+        announce("prefill long_context call %d (carried state)" % c_idx)
+        o_chain = lap.chunk_prefill(Q[rows], K[rows], V[rows], G[rows], B[rows], cu_call,
+                                    state_in=pool, state_out=pool, slots=slot0)
+        torch.cuda.synchronize()
+    announce("prefill long_context as one %d-row call" % T)
+    pool1 = torch.full((1, H, d, d), 7.0, dtype=torch.float32, device="cuda")
+    o_one = lap.chunk_prefill(Q, K, V, G, B, torch.tensor([0, T], dtype=torch.int32, device="cuda"),
+                              state_out=pool1)
+    torch.cuda.synchronize()
+    o_chain = o_chain.float().cpu().numpy()
+    o_one = o_one[-L:].float().cpu().numpy()
+    # Chunks fall on the same rows either way and the pool carries the fp32
+    # state unchanged, so the two runs agree bit for bit.
+    np.testing.assert_array_equal(o_chain, o_one)
+    np.testing.assert_array_equal(pool.cpu().numpy(), pool1.cpu().numpy())
     q, k, v, g, b = (np.concatenate(x) for x in (qs, ks, vs, gs, bs))
-    T = q.shape[0]
     announce("oracle over %d tokens, heads %s, columns %s" % (T, heads, cols))
     o_r, s_r = oracle.recurrence(q, k, v, g, b, [0, T])
-    s_g = pool.cpu().numpy()[0][heads][:, cols, :]
-    es = rel_err(s_g, s_r[0])
-    eo = rel_err(o_last[:, heads][:, :, cols], o_r[-8192:])
-    announce("  final-state err %.3e  last-call o err %.3e" % (es, eo))
-    assert es <= TOL["bf16"] and eo <= TOL["bf16"]
+    for name, st, ol in (("32 calls", pool, o_chain), ("one call", pool1, o_one)):
+        s_g = st.cpu().numpy()[0][heads][:, cols, :]
+        es = rel_err(s_g, s_r[0])
+        eo = rel_err(ol[:, heads][:, :, cols], o_r[-L:])
+        announce("  %s: final-state err %.3e  last-8192-row o err %.3e" % (name, es, eo))
+        assert es <= TOL["bf16"] and eo <= TOL["bf16"]
 
 
 def _check_decode(c, tol):
