@@ -265,6 +265,14 @@ def test_decode_full():
     _check_decode(W.decode_case(), TOL["bf16"])
 
 
+def test_decode_many_sequences():
+    """1000 sequences x 1 token in a 1024-slot pool (2 GiB of state, slot
+    offsets past 2^31 bytes), every 40th padded: 256,000 workgroups."""
+    c = W.decode_case(seed=56, n=1000, num_slots=1024)
+    c.slots[::40] = -1
+    _check_decode(c, TOL["bf16"])
+
+
 @pytest.mark.parametrize("dk,dv,io", [(64, 64, "f32"), (128, 64, "f32"), (64, 128, "bf16"),
                                       (128, 128, "f32")])
 def test_decode_small_with_padding(dk, dv, io):
