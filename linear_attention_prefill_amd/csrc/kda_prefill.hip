@@ -67,13 +67,12 @@ constexpr int kScanWarmAhead = 2;      // chunks between a scan stage's record a
 // VALU-bound factor phase and 34 KB out of LDS.
 template <typename E, int DK, int DV> struct IntraLds {
     static constexpr bool kStage = sizeof(E) == 2;  // V staged in LDS
-    // Pitches.  A k P / q P row of d_k + 4 elements
-    // (4 mod 8) spreads the factor phase's row writes and the fragment reads
-    // over the LDS banks: against d_k + 8 (bf16) it stalls a third fewer
-    // cycles on bank conflicts and the kernel runs 9% faster; against d_k
-    // (fp32) 7% faster.  Those rows are only accessed in 8-byte (bf16) or
-    // 16-byte (fp32) runs.  V rows keep d_v + 8, since V is staged with
-    // 16-byte row stores.
+    // Pitches.  A k P / q P row of d_k + 4 elements (4 mod 8) spreads the
+    // factor phase's row writes and the fragment reads over the LDS banks:
+    // against d_k + 8 (bf16) it stalls a third fewer cycles on bank
+    // conflicts and the kernel runs 9% faster; against d_k (fp32) 7% faster.
+    // Those rows are only accessed in 8-byte (bf16) or 16-byte (fp32) runs.
+    // V rows keep d_v + 8, since V is staged with 16-byte row stores.
     static constexpr int KPP = DK + 4;              // pitch of k P, q P (E)
     static constexpr int KQP = DK + 4;              // pitch of k Qf (fp32)
     static constexpr int VP = DV + (sizeof(E) == 2 ? 8 : 0);   // pitch of V (E)
