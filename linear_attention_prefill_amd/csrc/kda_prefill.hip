@@ -33,15 +33,14 @@
 // scans give the block prefixes), A blocks and the four diagonal inverses in
 // parallel, the off-diagonal inverse blocks in two levels on fp32 matrix
 // cores, then w and u; workspace fragments are written in the scan's order.
-// kda_scan_kernel: one workgroup of 4 waves per (sequence, head, 16-column
-// slice of d_v); the d_v columns of S evolve independently, so slices need no
-// exchange.  Wave w owns chunk rows 16w..16w+15 and a quarter of the key
-// channels, swaps the rounded copies of its S and U tiles with the other
-// waves through LDS, and keeps the operands of the next chunks in flight in
-// registers.  kda_scan_pair_kernel: the same scan for bf16 calls with more
-// than two slices per CU, where L2 bytes per CU rather than the chain of
-// chunks set the time; one 8-wave workgroup covers two slices and loads the
-// shared chunk operands once, passing them between its halves through LDS.
+// kda_scan_kernel: one workgroup of 4 waves per (sequence, head, group of NS
+// 16-column slices of d_v); the d_v columns of S evolve independently, so
+// slices need no exchange.  Wave w owns chunk rows 16w..16w+15 and a quarter
+// of the key channels, swaps the rounded copies of its S and U tiles with the
+// other waves through LDS, and keeps the operands of the next chunks in
+// flight in registers, applying each to all NS slices.  NS = 1 while there
+// are at most as many slices as CUs; NS = 2 (bf16) beyond that, where the
+// L2 bytes each CU takes in, not the chain of chunks, set the time.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -658,11 +657,11 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
 // ---------------------------------------------------------------------------
 
 // Operands of one chunk for one wave (row tile m = wave, TPW key tiles).
-template <typename E, int DK> struct ScanStage {
+template <typename E, int DK, int NS> struct ScanStage {
     static constexpr int KS = DK / kSlab;
     static constexpr int TPW = DK / 64;
     Frag<E> wf[KS], qf[KS], af[2], kf[TPW][2];
-    typename Raw4<E>::type u;                  // raw: converted where it is used
+    typename Raw4<E>::type u[NS];              // per slice; raw: converted where it is used
     float d;                                   // e^{Gam_C} of key row 16 TPW wave + (lane % (16 TPW))
     int pf;                                    // L2 warm-up word (first stage of the rotation only)
 };
@@ -706,7 +705,7 @@ __device__ __forceinline__ ScanWork scan_work(int b, int B, int N, int H, int JT
     return w;
 }
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, int NS>
 __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     const E *__restrict__ ws, const float *__restrict__ ws_dec,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ slots,
@@ -715,44 +714,56 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     constexpr int VT = DV / kSub, KS = DK / kSlab;
     constexpr int TPW = DK / 64;                       // key tiles per wave
     using L = WsLayout<E, DK, DV>;
-    using Stage = ScanStage<E, DK>;
-    // rounded copies of the state slabs and of U, [slab][lane][8]
-    __shared__ __align__(16) E sSb[KS * 64 * 8];
-    __shared__ __align__(16) E sUb[2 * 64 * 8];
+    using Stage = ScanStage<E, DK, NS>;
+    // Register stages of chunk operands in flight: three for one slice; two
+    // for two slices, whose second S, u and output tiles would otherwise
+    // push the kernel past one workgroup per SIMD pair.  The L2 warm-up rides
+    // on the three-stage rotation only.
+    constexpr int STAGES = NS == 1 ? 3 : 2;
+    constexpr bool kWarm = STAGES == 3;
+    // rounded copies of the state slabs and of U, [slice][slab][lane][8]
+    __shared__ __align__(16) E sSb[NS * KS * 64 * 8];
+    __shared__ __align__(16) E sUb[NS * 2 * 64 * 8];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int li = lane & 15, lg = lane >> 4;
-    const ScanWork wk = scan_work(blockIdx.x, gridDim.x, N, H, VT, cu, T, lane);
+    const ScanWork wk = scan_work(blockIdx.x, gridDim.x, N, H, VT / NS, cu, T, lane);
     if (!wk.valid) return;
-    const int h = wk.h, n = wk.n, jt = wk.j;
+    const int h = wk.h, n = wk.n, jt = wk.j;           // jt: group of NS slices
     const int slot = slots ? slots[n] : n;
     if (slots && (slot < 0 || slot >= num_slots)) return;   // padded sequence
     const SeqSpan sp = seq_span(cu, n, T);
-    const int j0 = jt * kSub;
+    const int j0 = jt * NS * kSub;                     // first column; slice ns at j0 + 16 ns
 
-    // my key tiles t = wave * TPW + i, C layout: lane holds S[16t + 4g + r][j0 + i]
-    f32x4 S[TPW];
-    if (state_in) {
-        const float *src = state_in + slot * slot_stride + h * head_stride + (size_t)(j0 + li) * DK;
+    // my key tiles t = wave * TPW + i of slice ns, C layout: lane holds
+    // S[16t + 4g + r][j0 + 16 ns + i]
+    f32x4 S[NS][TPW];
 #pragma unroll
-        for (int i = 0; i < TPW; ++i)
-            S[i] = *reinterpret_cast<const f32x4 *>(src + (wave * TPW + i) * kSub + 4 * lg);
-    } else {
+    for (int ns = 0; ns < NS; ++ns) {
+        if (state_in) {
+            const float *src = state_in + slot * slot_stride + h * head_stride + (size_t)(j0 + ns * kSub + li) * DK;
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < TPW; ++i)
+                S[ns][i] = *reinterpret_cast<const f32x4 *>(src + (wave * TPW + i) * kSub + 4 * lg);
+        } else {
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) S[ns][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
     // Settle the state load here: otherwise the wait inserted for it at the
     // top of the chunk loop would also drain every prefetched chunk.
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
+    for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float x = S[i][r];
-            asm volatile("" : "+v"(x));
-            S[i][r] = x;
+        for (int i = 0; i < TPW; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float x = S[ns][i][r];
+                asm volatile("" : "+v"(x));
+                S[ns][i][r] = x;
+            }
         }
-    }
 
     // Record of chunk cc, by part; each part of a stage is refilled with the
     // chunk three ahead as soon as its last use in the current step has been
@@ -765,7 +776,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     // miss still in flight.  Whenever the first stage of the rotation is
     // refilled with chunk c, the waves of the head's slices touch the
     // 128-byte lines of the records of chunks c + kScanWarmAhead .. + 2: the
-    // VT * 4 waves take the three records in turn, 64 lines a wave and one
+    // VT / NS * 4 waves take the three records in turn, 64 lines a wave and one
     // word a lane, so the operand loads mostly hit in L2.  The word is
     // consumed when the stage is, three steps later, so nothing waits for it.
     constexpr int kRecLines = (int)((L::kRecElems * sizeof(E) + 127) / 128);
@@ -780,7 +791,10 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
 #pragma unroll
         for (int s = 0; s < KS; ++s) X.wf[s] = load_frag<E>(Rw + (wave * KS + s) * 512, lane);
         const E *Ru = Rw + L::kWElems + L::kQElems + L::kKElems + L::kAElems;
-        X.u = *reinterpret_cast<const typename Raw4<E>::type *>(Ru + jt * (64 * 16) + lane * 16 + 4 * wave);
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns)
+            X.u[ns] = *reinterpret_cast<const typename Raw4<E>::type *>(
+                Ru + (jt * NS + ns) * (64 * 16) + lane * 16 + 4 * wave);
     };
     auto load_q = [&](Stage &X, int cc) {
         const E *Rq = ws + rec_of(cc) * L::kRecElems + L::kWElems;
@@ -813,280 +827,112 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     // the old or the new value, and the copy that merges them waits for
     // every load in flight.
     auto step = [&](Stage &X, int cc, bool refill, bool warm) {
-        const int nx = cc + 3 < nch ? cc + 3 : nch - 1;
+        const int nx = cc + STAGES < nch ? cc + STAGES : nch - 1;
         // publish my state tiles (rounded to E) and read every slab
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int t = wave * TPW + i;
-            store4<E>(sSb + ((t >> 1) * 64 + lane) * 8 + (t & 1) * 4, S[i]);
-        }
+        for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int t = wave * TPW + i;
+                store4<E>(sSb + ns * (KS * 512) + ((t >> 1) * 64 + lane) * 8 + (t & 1) * 4, S[ns][i]);
+            }
         __syncthreads();
         if (warm) asm volatile("" ::"v"(X.pf));   // the warm-up word, loaded three steps ago
-        Frag<E> Sb[KS];
+        // per slice: my tile of U = u - w S (two independent accumulation
+        // chains), and the Q~ S part of the output, which does not need U
+        f32x4 un[NS], o0[NS], o1[NS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) Sb[s] = load_frag<E>(sSb + s * 512, lane);
-        // my tile of U = u - w S (two independent accumulation chains)
-        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+        for (int ns = 0; ns < NS; ++ns) {
+            Frag<E> Sb[KS];
 #pragma unroll
-        for (int s = 0; s < KS; s += 2) {
-            mma(a0, X.wf[s], Sb[s]);
-            mma(a1, X.wf[s + 1], Sb[s + 1]);
+            for (int s = 0; s < KS; ++s) Sb[s] = load_frag<E>(sSb + ns * (KS * 512) + s * 512, lane);
+            f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+#pragma unroll
+            for (int s = 0; s < KS; s += 2) {
+                mma(a0, X.wf[s], Sb[s]);
+                mma(a1, X.wf[s + 1], Sb[s + 1]);
+            }
+            un[ns] = to_f32<E>(X.u[ns]) - (a0 + a1);
+            o0[ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+            o1[ns] = o0[ns];
+#pragma unroll
+            for (int s = 0; s < KS; s += 2) {
+                mma(o0[ns], Sb[s], X.qf[s]);
+                mma(o1[ns], Sb[s + 1], X.qf[s + 1]);
+            }
         }
-        const f32x4 un = to_f32<E>(X.u) - (a0 + a1);
         if (refill) load_w(X, nx, warm);
-        store4<E>(sUb + ((wave >> 1) * 64 + lane) * 8 + (wave & 1) * 4, un);
-        // Q~ S part of the output does not need U: issue it before the barrier
-        f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
 #pragma unroll
-        for (int s = 0; s < KS; s += 2) {
-            mma(o0, Sb[s], X.qf[s]);
-            mma(o1, Sb[s + 1], X.qf[s + 1]);
-        }
+        for (int ns = 0; ns < NS; ++ns)
+            store4<E>(sUb + ns * 1024 + ((wave >> 1) * 64 + lane) * 8 + (wave & 1) * 4, un[ns]);
         if (refill) load_q(X, nx);
 #pragma unroll
-        for (int i = 0; i < TPW; ++i)
+        for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S[i][r] *= __shfl(X.d, i * kSub + 4 * lg + r);
+            for (int i = 0; i < TPW; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[ns][i][r] *= __shfl(X.d, i * kSub + 4 * lg + r);
         __syncthreads();
-        Frag<E> ub[2];
-        ub[0] = load_frag<E>(sUb, lane);
-        ub[1] = load_frag<E>(sUb + 512, lane);
-        // my tile of O = Q~ S + A_qk U, transposed: lane holds row 16 wave + i,
-        // columns j0 + 4g + r
-        mma(o0, ub[0], X.af[0]);
-        if (wave >= 2) mma(o1, ub[1], X.af[1]);
-        // my key tiles of S = diag(e^{Gam_C}) S + K~^T U
+        const int row = wave * kSub + li;
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            mma(S[i], X.kf[i][0], ub[0]);
-            mma(S[i], X.kf[i][1], ub[1]);
+        for (int ns = 0; ns < NS; ++ns) {
+            Frag<E> ub[2];
+            ub[0] = load_frag<E>(sUb + ns * 1024, lane);
+            ub[1] = load_frag<E>(sUb + ns * 1024 + 512, lane);
+            // my tile of O = Q~ S + A_qk U, transposed: lane holds row
+            // 16 wave + i, columns j0 + 16 ns + 4g + r
+            mma(o0[ns], ub[0], X.af[0]);
+            if (wave >= 2) mma(o1[ns], ub[1], X.af[1]);
+            // my key tiles of S = diag(e^{Gam_C}) S + K~^T U
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                mma(S[ns][i], X.kf[i][0], ub[0]);
+                mma(S[ns][i], X.kf[i][1], ub[1]);
+            }
         }
         if (refill) load_k(X, nx);
-        const int row = wave * kSub + li;
-        if (row < sp.len - cc * kChunk)
-            store4<E>(o + ((size_t)(sp.start + cc * kChunk + row) * H + h) * DV + j0 + 4 * lg,
-                      (o0 + o1) * scale);
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns)
+            if (row < sp.len - cc * kChunk)
+                store4<E>(o + ((size_t)(sp.start + cc * kChunk + row) * H + h) * DV + j0 + ns * kSub + 4 * lg,
+                          (o0[ns] + o1[ns]) * scale);
     };
 
     if (nch > 0) {
-        Stage A, Bs, Cs;
-        load_stage(A, 0, true);
-        load_stage(Bs, nch > 1 ? 1 : 0, false);
-        load_stage(Cs, nch > 2 ? 2 : nch - 1, false);
-        int cc = 0;
-        for (; cc + 2 < nch; cc += 3) {
-            step(A, cc, true, true);
-            step(Bs, cc + 1, true, false);
-            step(Cs, cc + 2, true, false);
+        if constexpr (STAGES == 3) {
+            Stage A, Bs, Cs;
+            load_stage(A, 0, kWarm);
+            load_stage(Bs, nch > 1 ? 1 : 0, false);
+            load_stage(Cs, nch > 2 ? 2 : nch - 1, false);
+            int cc = 0;
+            for (; cc + 2 < nch; cc += 3) {
+                step(A, cc, true, kWarm);
+                step(Bs, cc + 1, true, false);
+                step(Cs, cc + 2, true, false);
+            }
+            if (cc < nch) step(A, cc, false, kWarm);
+            if (cc + 1 < nch) step(Bs, cc + 1, false, false);
+        } else {
+            Stage A, Bs;
+            load_stage(A, 0, false);
+            load_stage(Bs, nch > 1 ? 1 : 0, false);
+            int cc = 0;
+            for (; cc + 1 < nch; cc += 2) {
+                step(A, cc, true, false);
+                step(Bs, cc + 1, true, false);
+            }
+            if (cc < nch) step(A, cc, false, false);
         }
-        if (cc < nch) step(A, cc, false, true);
-        if (cc + 1 < nch) step(Bs, cc + 1, false, false);
     }
 
     if (state_out) {
-        float *dst = state_out + slot * slot_stride + h * head_stride + (size_t)(j0 + li) * DK;
 #pragma unroll
-        for (int i = 0; i < TPW; ++i)
-            *reinterpret_cast<f32x4 *>(dst + (wave * TPW + i) * kSub + 4 * lg) = S[i];
-    }
-}
-
-// kda_scan_pair_kernel: the state scan for calls with many (sequence, head)
-// pairs, where the scan is bound by how many bytes each CU pulls from L2
-// rather than by its chain of chunks.  One workgroup of 8 waves covers 32
-// columns of d_v: waves 0..3 update columns 0..15 of the pair and waves 4..7
-// columns 16..31, exactly as the 4 waves of kda_scan_kernel do.  The chunk
-// operands both halves need (w, Q e^Gam, K~^T and A_qk, 14 fragments per
-// wave row) are loaded from the record once: each half loads 7 of them into
-// its rolling register stages and publishes them through LDS, double
-// buffered by chunk parity.  A chunk's operands are written right after the
-// first barrier of the step before it (the buffer of that parity has been
-// read by then), so no LDS write sits between a step's barriers and its
-// products.  The workgroup moves half the L2 bytes per column of two
-// single-slice workgroups.  bf16 only (fp32 fragments would not fit two LDS buffers).
-template <typename E, int DK> struct PairStage {
-    static constexpr int KS = DK / kSlab;
-    static constexpr int TPW = DK / 64;
-    static constexpr int F = 2 * KS + 2 * TPW + 2;     // fragments per wave row
-    static constexpr int F2 = F / 2;                   // loaded by each half
-    Frag<E> f[F2];
-    typename Raw4<E>::type u;
-    float d;
-};
-
-template <typename E, int DK, int DV>
-__global__ __launch_bounds__(512, 1) void kda_scan_pair_kernel(
-    const E *__restrict__ ws, const float *__restrict__ ws_dec,
-    const int32_t *__restrict__ cu, const int32_t *__restrict__ slots,
-    const float *state_in, float *state_out, E *__restrict__ o,
-    int T, int N, int H, int num_slots, float scale, int64_t slot_stride, int64_t head_stride) {
-    static_assert(sizeof(E) == 2, "bf16 only");
-    constexpr int VT = DV / kSub, KS = DK / kSlab;
-    constexpr int TPW = DK / 64;
-    using L = WsLayout<E, DK, DV>;
-    using Stage = PairStage<E, DK>;
-    constexpr int F = Stage::F, F2 = Stage::F2;
-    // shared operands [parity][fragment index][wave row][lane][8]; fragment
-    // index: w slabs 0..KS-1, Q e^Gam slabs KS..2KS-1, K~^T (tile i, slab s)
-    // at 2KS + 2i + s, A_qk halves at F-2, F-1
-    __shared__ __align__(16) E sOp[2 * F * 4 * 512];
-    __shared__ __align__(16) E sSb2[2][KS * 64 * 8];
-    __shared__ __align__(16) E sUb2[2][2 * 64 * 8];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = (tid >> 6) & 3;
-    const int grp = __builtin_amdgcn_readfirstlane(tid >> 8);
-    const int li = lane & 15, lg = lane >> 4;
-    E *const sSb = sSb2[grp];
-    E *const sUb = sUb2[grp];
-    // work order over pairs of 16-column slices
-    const ScanWork wk = scan_work(blockIdx.x, gridDim.x, N, H, VT / 2, cu, T, lane);
-    if (!wk.valid) return;
-    const int jt = 2 * wk.j + grp;
-    const int h = wk.h, n = wk.n;
-    const int slot = slots ? slots[n] : n;
-    if (slots && (slot < 0 || slot >= num_slots)) return;   // padded sequence
-    const SeqSpan sp = seq_span(cu, n, T);
-    const int j0 = jt * kSub;
-
-    f32x4 S[TPW];
-    if (state_in) {
-        const float *src = state_in + slot * slot_stride + h * head_stride + (size_t)(j0 + li) * DK;
+        for (int ns = 0; ns < NS; ++ns) {
+            float *dst = state_out + slot * slot_stride + h * head_stride + (size_t)(j0 + ns * kSub + li) * DK;
 #pragma unroll
-        for (int i = 0; i < TPW; ++i)
-            S[i] = *reinterpret_cast<const f32x4 *>(src + (wave * TPW + i) * kSub + 4 * lg);
-    } else {
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float x = S[i][r];
-            asm volatile("" : "+v"(x));
-            S[i][r] = x;
+            for (int i = 0; i < TPW; ++i)
+                *reinterpret_cast<f32x4 *>(dst + (wave * TPW + i) * kSub + 4 * lg) = S[ns][i];
         }
-    }
-
-    // Record offsets (elements) of this half's fragments for this wave row:
-    // fixed for the whole scan, so refills are unconditional and branch-free.
-    auto frag_off = [&](int idx) -> int {
-        if (idx < KS) return (wave * KS + idx) * 512;
-        if (idx < 2 * KS) return L::kWElems + (wave * KS + idx - KS) * 512;
-        if (idx < 2 * KS + 2 * TPW) {
-            const int i = (idx - 2 * KS) >> 1, s = (idx - 2 * KS) & 1;
-            return L::kWElems + L::kQElems + ((wave * TPW + i) * 2 + s) * 512;
-        }
-        return L::kWElems + L::kQElems + L::kKElems + tri_frag(wave, idx - (F - 2)) * 512;
-    };
-    int offs[F2];
-#pragma unroll
-    for (int j = 0; j < F2; ++j) offs[j] = frag_off(grp * F2 + j);
-    const int u_off = L::kWElems + L::kQElems + L::kKElems + L::kAElems + jt * (64 * 16) + lane * 16 + 4 * wave;
-
-    auto rec_of = [&](int cc) { return (size_t)(sp.first_chunk + cc) * H + h; };
-    auto load_stage = [&](Stage &X, int cc) {
-        const size_t rec = rec_of(cc);
-        const E *R = ws + rec * L::kRecElems;
-#pragma unroll
-        for (int j = 0; j < F2; ++j) X.f[j] = load_frag<E>(R + offs[j], lane);
-        X.u = *reinterpret_cast<const typename Raw4<E>::type *>(R + u_off);
-        X.d = ws_dec[rec * DK + wave * (TPW * kSub) + (lane & (TPW * kSub - 1))];
-    };
-    auto op = [&](int par, int idx) -> E * { return sOp + ((par * F + idx) * 4 + wave) * 512; };
-
-    const int nch = (sp.len + kChunk - 1) / kChunk;
-    auto publish = [&](const Stage &X, int cc) {
-#pragma unroll
-        for (int j = 0; j < F2; ++j) store_frag<E>(op(cc & 1, grp * F2 + j), lane, X.f[j]);
-    };
-    auto step = [&](Stage &X, const Stage &Xn, int cc, bool refill) {
-        const int nx = cc + 3 < nch ? cc + 3 : nch - 1;
-        const int par = cc & 1;
-        // publish my state tiles (this chunk's operands went out a step ago)
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            const int t = wave * TPW + i;
-            store4<E>(sSb + ((t >> 1) * 64 + lane) * 8 + (t & 1) * 4, S[i]);
-        }
-        __syncthreads();
-        // the other parity's buffer was last read before this barrier:
-        // publish the next chunk's operands into it now
-        if (cc + 1 < nch) publish(Xn, cc + 1);
-        Frag<E> Sb[KS], wf[KS], qf[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            Sb[s] = load_frag<E>(sSb + s * 512, lane);
-            wf[s] = load_frag<E>(op(par, s), lane);
-        }
-        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-#pragma unroll
-        for (int s = 0; s < KS; s += 2) {
-            mma(a0, wf[s], Sb[s]);
-            mma(a1, wf[s + 1], Sb[s + 1]);
-        }
-        const f32x4 un = to_f32<E>(X.u) - (a0 + a1);
-        const float dd = X.d;
-        if (refill) load_stage(X, nx);
-        store4<E>(sUb + ((wave >> 1) * 64 + lane) * 8 + (wave & 1) * 4, un);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) qf[s] = load_frag<E>(op(par, KS + s), lane);
-        f32x4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
-#pragma unroll
-        for (int s = 0; s < KS; s += 2) {
-            mma(o0, Sb[s], qf[s]);
-            mma(o1, Sb[s + 1], qf[s + 1]);
-        }
-#pragma unroll
-        for (int i = 0; i < TPW; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) S[i][r] *= __shfl(dd, i * kSub + 4 * lg + r);
-        Frag<E> kf[TPW][2], af[2];
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            kf[i][0] = load_frag<E>(op(par, 2 * KS + 2 * i), lane);
-            kf[i][1] = load_frag<E>(op(par, 2 * KS + 2 * i + 1), lane);
-        }
-        af[0] = load_frag<E>(op(par, F - 2), lane);
-        af[1] = load_frag<E>(op(par, F - 1), lane);
-        __syncthreads();
-        Frag<E> ub[2];
-        ub[0] = load_frag<E>(sUb, lane);
-        ub[1] = load_frag<E>(sUb + 512, lane);
-        mma(o0, ub[0], af[0]);
-        if (wave >= 2) mma(o1, ub[1], af[1]);
-#pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-            mma(S[i], kf[i][0], ub[0]);
-            mma(S[i], kf[i][1], ub[1]);
-        }
-        const int row = wave * kSub + li;
-        if (row < sp.len - cc * kChunk)
-            store4<E>(o + ((size_t)(sp.start + cc * kChunk + row) * H + h) * DV + j0 + 4 * lg,
-                      (o0 + o1) * scale);
-    };
-
-    if (nch > 0) {
-        Stage A, Bs, Cs;
-        load_stage(A, 0);
-        load_stage(Bs, nch > 1 ? 1 : 0);
-        load_stage(Cs, nch > 2 ? 2 : nch - 1);
-        publish(A, 0);
-        int cc = 0;
-        for (; cc + 2 < nch; cc += 3) {
-            step(A, Bs, cc, true);
-            step(Bs, Cs, cc + 1, true);
-            step(Cs, A, cc + 2, true);
-        }
-        if (cc < nch) step(A, Bs, cc, false);
-        if (cc + 1 < nch) step(Bs, Cs, cc + 1, false);
-    }
-
-    if (state_out) {
-        float *dst = state_out + slot * slot_stride + h * head_stride + (size_t)(j0 + li) * DK;
-#pragma unroll
-        for (int i = 0; i < TPW; ++i)
-            *reinterpret_cast<f32x4 *>(dst + (wave * TPW + i) * kSub + 4 * lg) = S[i];
     }
 }
 
@@ -1106,13 +952,14 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
             a.g, a.beta, a.cu_seqlens, a.T, a.N, a.H, ws, ws_dec);
     }
     if (a.events[1]) (void)hipEventRecord(a.events[1], stream);
-    // Many (sequence, head) pairs: the scan is bound by L2 bytes per CU, so
-    // pairs of slices share their operands; few pairs: it is bound by its
-    // chain of chunks, and single-slice workgroups spread it over more CUs.
+    // Up to one 16-column slice per CU, one workgroup per slice spreads the
+    // chains over the most CUs.  Beyond that (bf16), a workgroup takes two
+    // slices: each chunk's operands come in once for both, two workgroups
+    // still fit on a CU, and the scan moves half the L2 bytes per column.
     const long long slices = (long long)a.N * a.H * (DV / kSub);
     if constexpr (sizeof(E) == 2) {
-        if (slices > 2LL * a.num_cus) {
-            kda_scan_pair_kernel<E, DK, DV><<<dim3((int)(slices / 2)), dim3(512), 0, stream>>>(
+        if (slices > a.num_cus) {
+            kda_scan_kernel<E, DK, DV, 2><<<dim3((int)(slices / 2)), dim3(256), 0, stream>>>(
                 ws, ws_dec, a.cu_seqlens, a.slots, a.state_in, a.state_out, static_cast<E *>(a.o),
                 a.T, a.N, a.H, a.num_slots, a.scale, a.slot_stride, a.head_stride);
             const hipError_t e = hipGetLastError();
@@ -1120,7 +967,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
             return e;
         }
     }
-    kda_scan_kernel<E, DK, DV><<<dim3((int)slices), dim3(256), 0, stream>>>(
+    kda_scan_kernel<E, DK, DV, 1><<<dim3((int)slices), dim3(256), 0, stream>>>(
         ws, ws_dec, a.cu_seqlens, a.slots, a.state_in, a.state_out, static_cast<E *>(a.o),
         a.T, a.N, a.H, a.num_slots, a.scale, a.slot_stride, a.head_stride);
     const hipError_t e = hipGetLastError();

@@ -71,10 +71,13 @@ def _kernels():
 
 def test_every_kernel_is_present():
     names = " ".join(k["name"] for k in _kernels())
-    for kern in ("kda_intra_kernel", "kda_scan_kernel", "kda_scan_pair_kernel", "kda_decode_kernel",
+    for kern in ("kda_intra_kernel", "kda_scan_kernel", "kda_decode_kernel",
                  "kda_decode_tokens_kernel", "kda_decode_conv_kernel", "kda_conv_kernel",
                  "kda_conv_window_kernel"):
         assert kern in names, kern
+    # the scan with one and with two 16-column slices per workgroup (bf16)
+    assert "kda_scan_kernelIDF16bLi128ELi128ELi1E" in names
+    assert "kda_scan_kernelIDF16bLi128ELi128ELi2E" in names
 
 
 def test_no_kernel_uses_scratch():

@@ -292,10 +292,10 @@ def test_decay_range_paths(mu_g, io):
 
 
 @pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
-def test_many_pairs_shared_operand_scan(dk, dv):
-    """Enough (sequence, head, 16-column slice) triples to exceed two per CU,
-    so bf16 calls take the scan whose 8-wave workgroups share the chunk
-    operands of two slices through LDS; ragged and empty sequences, padded
+def test_many_pairs_two_slice_scan(dk, dv):
+    """Enough (sequence, head, 16-column slice) triples to exceed one per CU
+    (here more than two), so bf16 calls take the scan whose workgroups apply
+    each chunk's operands to two slices; ragged and empty sequences, padded
     slots and in-place pools included."""
     rng = np.random.default_rng(17 + dk + dv)
     lengths = [int(x) for x in rng.choice([0, 1, 2, 63, 64, 65, 129, 200], size=48)]
@@ -304,7 +304,7 @@ def test_many_pairs_shared_operand_scan(dk, dv):
     c = W.random_case(400 + dk + dv, lengths, H=4, d_k=dk, d_v=dv, io_dtype="bf16",
                       num_slots=60, slots=slots)
     assert c.N * c.H * (dv // 16) > 2 * 256
-    announce("shared-operand scan %s" % c.name)
+    announce("two-slice scan %s" % c.name)
     o_g, _, _, _, _ = _check_case(c)
     cu = c.cu_seqlens
     assert np.all(o_g[cu[5]:cu[6]] == 3.0)           # the padded sequence keeps its rows
