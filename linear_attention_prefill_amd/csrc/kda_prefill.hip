@@ -38,9 +38,12 @@
 // slices need no exchange.  Wave w owns chunk rows 16w..16w+15 and a quarter
 // of the key channels, swaps the rounded copies of its S and U tiles with the
 // other waves through LDS, and keeps the operands of the next chunks in
-// flight in registers, applying each to all NS slices.  NS = 1 while there
-// are at most as many slices as CUs; NS = 2 (bf16) beyond that, where the
-// L2 bytes each CU takes in, not the chain of chunks, set the time.
+// flight in registers, applying each to all NS slices.  The scan is bound by
+// the record bytes each CU takes in, which a workgroup takes in once for its
+// NS slices: each call uses the largest NS of 1, 2 or 4 (bf16 for NS > 1)
+// that still leaves every CU a workgroup.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -716,9 +719,9 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     using L = WsLayout<E, DK, DV>;
     using Stage = ScanStage<E, DK, NS>;
     // Register stages of chunk operands in flight: three for one slice; two
-    // for two slices, whose second S, u and output tiles would otherwise
-    // push the kernel past one workgroup per SIMD pair.  The L2 warm-up rides
-    // on the three-stage rotation only.
+    // for two or four slices, whose extra S, u and output tiles would
+    // otherwise push the kernel past two workgroups per CU.  The L2 warm-up
+    // rides on the three-stage rotation only.
     constexpr int STAGES = NS == 1 ? 3 : 2;
     constexpr bool kWarm = STAGES == 3;
     // rounded copies of the state slabs and of U, [slice][slab][lane][8]
@@ -952,27 +955,25 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
             a.g, a.beta, a.cu_seqlens, a.T, a.N, a.H, ws, ws_dec);
     }
     if (a.events[1]) (void)hipEventRecord(a.events[1], stream);
-    // Up to one 16-column slice per CU, one workgroup per slice spreads the
-    // chains over the most CUs.  Beyond that (bf16), a workgroup takes two
-    // slices: each chunk's operands come in once for both, two workgroups
-    // still fit on a CU, and the scan moves half the L2 bytes per column.
+    // The scan is bound by the record bytes each CU takes in, and a workgroup
+    // of NS 16-column slices takes them in once for all NS.  So each call
+    // gets the largest NS (1, 2 or 4; bf16 for NS > 1) that still leaves at
+    // least one workgroup per CU.
     const long long slices = (long long)a.N * a.H * (DV / kSub);
+    auto scan = [&](auto ns) -> hipError_t {
+        constexpr int NS = decltype(ns)::value;
+        kda_scan_kernel<E, DK, DV, NS><<<dim3((int)(slices / NS)), dim3(256), 0, stream>>>(
+            ws, ws_dec, a.cu_seqlens, a.slots, a.state_in, a.state_out, static_cast<E *>(a.o),
+            a.T, a.N, a.H, a.num_slots, a.scale, a.slot_stride, a.head_stride);
+        const hipError_t e = hipGetLastError();
+        if (a.events[2]) (void)hipEventRecord(a.events[2], stream);
+        return e;
+    };
     if constexpr (sizeof(E) == 2) {
-        if (slices > a.num_cus) {
-            kda_scan_kernel<E, DK, DV, 2><<<dim3((int)(slices / 2)), dim3(256), 0, stream>>>(
-                ws, ws_dec, a.cu_seqlens, a.slots, a.state_in, a.state_out, static_cast<E *>(a.o),
-                a.T, a.N, a.H, a.num_slots, a.scale, a.slot_stride, a.head_stride);
-            const hipError_t e = hipGetLastError();
-            if (a.events[2]) (void)hipEventRecord(a.events[2], stream);
-            return e;
-        }
+        if (slices >= 4LL * a.num_cus) return scan(std::integral_constant<int, 4>{});
+        if (slices >= 2LL * a.num_cus) return scan(std::integral_constant<int, 2>{});
     }
-    kda_scan_kernel<E, DK, DV, 1><<<dim3((int)slices), dim3(256), 0, stream>>>(
-        ws, ws_dec, a.cu_seqlens, a.slots, a.state_in, a.state_out, static_cast<E *>(a.o),
-        a.T, a.N, a.H, a.num_slots, a.scale, a.slot_stride, a.head_stride);
-    const hipError_t e = hipGetLastError();
-    if (a.events[2]) (void)hipEventRecord(a.events[2], stream);
-    return e;
+    return scan(std::integral_constant<int, 1>{});
 }
 
 size_t prefill_workspace_bytes(int T, int N, int H, int dk, int dv, bool bf16) {

@@ -291,20 +291,22 @@ def test_decay_range_paths(mu_g, io):
     _check_case(c)
 
 
-@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64)])
-def test_many_pairs_two_slice_scan(dk, dv):
-    """Enough (sequence, head, 16-column slice) triples to exceed one per CU
-    (here more than two), so bf16 calls take the scan whose workgroups apply
-    each chunk's operands to two slices; ragged and empty sequences, padded
-    slots and in-place pools included."""
-    rng = np.random.default_rng(17 + dk + dv)
+@pytest.mark.parametrize("dk,dv,H,ns", [(128, 128, 4, 4), (128, 128, 2, 2), (64, 64, 4, 2),
+                                        (128, 64, 4, 2), (64, 64, 8, 4)])
+def test_many_pairs_multi_slice_scan(dk, dv, H, ns):
+    """Enough (sequence, head, 16-column slice) triples for bf16 calls to take
+    the scan whose workgroups apply each chunk's operands to ns = 2 or 4
+    slices (at least ns slices per CU on a 256-CU part); ragged and empty
+    sequences, padded slots and in-place pools included."""
+    rng = np.random.default_rng(17 + dk + dv + H)
     lengths = [int(x) for x in rng.choice([0, 1, 2, 63, 64, 65, 129, 200], size=48)]
     slots = [int(s) for s in rng.permutation(60)[:48]]
     slots[5] = -1
-    c = W.random_case(400 + dk + dv, lengths, H=4, d_k=dk, d_v=dv, io_dtype="bf16",
+    c = W.random_case(400 + dk + dv + H, lengths, H=H, d_k=dk, d_v=dv, io_dtype="bf16",
                       num_slots=60, slots=slots)
-    assert c.N * c.H * (dv // 16) > 2 * 256
-    announce("two-slice scan %s" % c.name)
+    n_slices = c.N * c.H * (dv // 16)
+    assert ns * 256 <= n_slices < (2 * ns if ns < 4 else 10 ** 9) * 256
+    announce("%d-slice scan %s" % (ns, c.name))
     o_g, _, _, _, _ = _check_case(c)
     cu = c.cu_seqlens
     assert np.all(o_g[cu[5]:cu[6]] == 3.0)           # the padded sequence keeps its rows
