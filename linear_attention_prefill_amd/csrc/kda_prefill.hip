@@ -465,16 +465,37 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
             if (!(I & 1)) put_aqk(I, I + 1, f32x4{0.f, 0.f, 0.f, 0.f});
             float *D = sD + I * kSub * DP;
             *reinterpret_cast<f32x4 *>(D + li * DP + 4 * lg) = vk;
-            // the block was written by this wave only; LDS accesses of a wave
-            // complete in order
-            const int jj = li;
+            // Column jj = li of (I + D)^-1 by forward substitution: row ii
+            // sums its terms in the order mm = 0, 1, ..., each as soon as
+            // entry mm is final, and takes the sum off the unit vector's
+            // entry.  The block was written by this wave only; LDS accesses
+            // of a wave complete in order.
             float tcol[kSub];
+            if constexpr (sizeof(E) == 2) {
+                // The unit vector comes from an opaque bit per item.  Selects
+                // on ii < jj and ii == jj would be hoisted out of the item
+                // loop as 32 lane masks, spilled to vector-register lanes and
+                // read back on the chain: 1.06x slower for the kernel.
+                unsigned unit = 1u << li;
+                asm volatile("" : "+v"(unit));
 #pragma unroll
-            for (int ii = 0; ii < kSub; ++ii) {
-                float s = 0.f;
+                for (int ii = 0; ii < kSub; ++ii) {
+                    float acc = 0.f;
 #pragma unroll
-                for (int mm = 0; mm < ii; ++mm) s = fmaf(D[ii * DP + mm], tcol[mm], s);
-                tcol[ii] = ii < jj ? 0.f : (ii == jj ? 1.f : -s);
+                    for (int mm = 0; mm < ii; ++mm) acc = fmaf(D[ii * DP + mm], tcol[mm], acc);
+                    tcol[ii] = (float)__builtin_amdgcn_ubfe(unit, ii, 1) - acc;
+                }
+            } else {
+                // fp32: its raw inputs take twice the registers, which leaves
+                // no room for the 16 unit entries; the masks are used instead.
+                const int jj = li;
+#pragma unroll
+                for (int ii = 0; ii < kSub; ++ii) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int mm = 0; mm < ii; ++mm) acc = fmaf(D[ii * DP + mm], tcol[mm], acc);
+                    tcol[ii] = ii < jj ? 0.f : (ii == jj ? 1.f : -acc);
+                }
             }
             if (lg == 0) {
 #pragma unroll
