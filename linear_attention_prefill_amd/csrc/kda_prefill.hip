@@ -79,9 +79,7 @@ template <typename E, int DK, int DV> struct IntraLds {
     static constexpr int KQP = DK + 4;              // pitch of k Qf (fp32)
     static constexpr int VP = DV + (sizeof(E) == 2 ? 8 : 0);   // pitch of V (E)
     static constexpr int AP = 68;                   // pitch of A_kk -> Tm (fp32)
-    static constexpr int T2P = 36;                  // pitch of Tm[32:64, 0:32] (fp32)
     static constexpr int DP = 16;                   // pitch of the diagonal A_kk blocks (fp32)
-    static constexpr int T2D_BYTES = 32 * T2P * 4 > 4 * kSub * DP * 4 ? 32 * T2P * 4 : 4 * kSub * DP * 4;
     static constexpr int V_ELEMS = kStage ? kChunk * VP : 8;
 };
 
@@ -142,7 +140,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
     using L = WsLayout<E, DK, DV>;
     using R4 = typename Raw4<E>::type;
     constexpr int NTH = kIntraThreads;
-    constexpr int KPP = LD::KPP, KQP = LD::KQP, VP = LD::VP, AP = LD::AP, T2P = LD::T2P, DP = LD::DP;
+    constexpr int KPP = LD::KPP, KQP = LD::KQP, VP = LD::VP, AP = LD::AP, DP = LD::DP;
     constexpr int KS = DK / kSlab;                     // d_k slabs
     constexpr int VT = DV / kSub;                      // d_v tiles
     constexpr int C4 = DK / 4;                         // 4-channel columns
@@ -158,7 +156,8 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
     __shared__ __align__(16) E sV[LD::V_ELEMS];        // V
     __shared__ __align__(16) float sKQ[kChunk * KQP];  // k Qf (fp32)
     __shared__ __align__(16) float sA[kChunk * AP];    // A_kk -> Tm
-    __shared__ __align__(16) char sT2D[LD::T2D_BYTES];  // diagonal A_kk blocks; later Tm[32:64, 0:32]
+    __shared__ __align__(16) float sD[4 * kSub * DP];  // diagonal A_kk blocks
+    __shared__ __align__(16) E sTb[6 * 512];           // Tm diag(beta) fragments, index tri_frag(m, s)
     __shared__ __align__(16) float sBs[4 * DK];        // e^{Gam} at each block's first row
     __shared__ __align__(16) float sCe[4 * DK];        // e^{Gam_C - Gam} at each block's last row
     __shared__ __align__(16) float sF[10 * DK];        // F_IJ, J <= I, index I(I+1)/2 + J
@@ -166,8 +165,6 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
     __shared__ int sExact[4 * C4];                     // per block and 4-channel column
     __shared__ int sCu[kCuCache];
 
-    float *const sT2 = reinterpret_cast<float *>(sT2D);
-    float *const sD = reinterpret_cast<float *>(sT2D);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
     // factor phase: lane (r, c) of wave w < FW (r = lane % 16, c = lane / 16)
@@ -184,6 +181,15 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
     const int cu_v = (cu_reg && lane <= N) ? cu[lane] : 0;
     if (!cu_reg && cu_lds)
         for (int i = tid; i <= N; i += NTH) sCu[i] = cu[i];
+    // Tm diag(beta) fragments (m, s), s <= m / 2: lane (i, g) holds row
+    // 16 m + i, columns 32 s + kk(g, e), as the w and u products take them.
+    // Their right halves for even m are the zero blocks (0, 1) and (2, 3),
+    // written once here; every other half is rewritten per item where its
+    // block of Tm becomes final.
+    if (tid < 128) {
+        const int m = 2 * (tid >> 6);                  // fragments (0, 0) and (2, 1)
+        store4<E>(sTb + tri_frag(m, m >> 1) * 512 + lane * 8 + 4, f32x4{0.f, 0.f, 0.f, 0.f});
+    }
     __syncthreads();
     // (scalar loads for the uncached case: no vector-memory wait in the loop)
     const int32_t __attribute__((address_space(4))) *cu_s =
@@ -546,18 +552,30 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
             for (int ks = 0; ks < 4; ++ks)
                 P = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(I * kSub + li) * AP + J * kSub + lg + 4 * ks],
                                                          sA[(J * kSub + lg + 4 * ks) * AP + J * kSub + li], P, 0, 0, 0);
-            // P in C layout is the B operand with contraction index 4g + r
+            // P in C layout is the A operand of P^T with contraction index
+            // 4g + r, so (Tm_II P)^T = P^T Tm_II^T leaves lane (i, g) holding
+            // row i, columns 4g .. 4g + 3 of Tm_IJ: one 16-byte row store, and
+            // the left half of Tm diag(beta) fragment (I, J / 2)
             f32x4 Tt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                Tt = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(I * kSub + li) * AP + I * kSub + 4 * lg + r], P[r], Tt, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sA[(I * kSub + 4 * lg + r) * AP + J * kSub + li] = -Tt[r];
+                Tt = __builtin_amdgcn_mfma_f32_16x16x4f32(P[r], sA[(I * kSub + li) * AP + I * kSub + 4 * lg + r], Tt, 0, 0, 0);
+            Tt = -Tt;
+            *reinterpret_cast<f32x4 *>(sA + (I * kSub + li) * AP + J * kSub + 4 * lg) = Tt;
+            store4<E>(sTb + tri_frag(I, J >> 1) * 512 + lane * 8 + 4 * (J & 1),
+                      Tt * *reinterpret_cast<const f32x4 *>(sBeta + J * kSub + 4 * lg));
+        }
+        if (wave >= 4) {
+            // the diagonal half of Tm diag(beta) fragment (I, I / 2), I = wave - 4
+            const int I = wave - 4;
+            store4<E>(sTb + tri_frag(I, I >> 1) * 512 + lane * 8 + 4 * (I & 1),
+                      *reinterpret_cast<const f32x4 *>(sA + (I * kSub + li) * AP + I * kSub + 4 * lg) *
+                          *reinterpret_cast<const f32x4 *>(sBeta + I * kSub + 4 * lg));
         }
         load_row(nxt, 2);
         __syncthreads();
-        // level 2 (waves 0..3, output tile (ti, tj)) into sT2:
-        // Tm[32:64, 0:32] = -Tm_hi (A[32:64, 0:32] Tm_lo).
+        // level 2 (waves 0..3, output tile (ti, tj)), straight into the Tm
+        // diag(beta) fragments (2 + ti, 0): Tm[32:64, 0:32] = -Tm_hi (A[32:64, 0:32] Tm_lo).
         // Meanwhile waves 4..7 write K e^{Gam_C - Gam}, transposed, in the
         // scan's order: fragment (t, s) holds key channels 16t + i over chunk
         // rows 32s + kk(g, e).
@@ -586,30 +604,25 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
                         sA[(32 + kt * kSub + li) * AP + lg + 4 * ks],
                         sA[(lg + 4 * ks) * AP + tj * kSub + li], Qt[kt], 0, 0, 0);
             }
+            // transposed as in level 1: lane (i, g) receives row i, columns
+            // 4g .. 4g + 3 of the tile
             f32x4 Tt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     Tt = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                        sA[(32 + ti * kSub + li) * AP + 32 + kt * kSub + 4 * lg + r], Qt[kt][r], Tt, 0, 0, 0);
+                        Qt[kt][r], sA[(32 + ti * kSub + li) * AP + 32 + kt * kSub + 4 * lg + r], Tt, 0, 0, 0);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sT2[(ti * kSub + 4 * lg + r) * T2P + tj * kSub + li] = -Tt[r];
+            store4<E>(sTb + tri_frag(2 + ti, 0) * 512 + lane * 8 + 4 * tj,
+                      -Tt * *reinterpret_cast<const f32x4 *>(sBeta + tj * kSub + 4 * lg));
         }
         load_row(nxt, 3);
         __syncthreads();
 
         // ---- w and u on the matrix cores, with diag(beta) folded into Tm ----
         // fragment (m, s) of Tm diag(beta): row 16 m + i, columns 32 s + kk(g, e)
-        auto tm_frag = [&](int m, int s) {
-            const int row = m * kSub + li, c0 = s * kSlab + 4 * lg;
-            const float *src = (m >= 2 && s == 0) ? sT2 + (row - 32) * T2P + c0 : sA + row * AP + c0;
-            const f32x4 a = *reinterpret_cast<const f32x4 *>(src) * *reinterpret_cast<const f32x4 *>(sBeta + c0);
-            const f32x4 b = *reinterpret_cast<const f32x4 *>(src + 16) *
-                            *reinterpret_cast<const f32x4 *>(sBeta + c0 + 16);
-            return frag_from_tiles<E>(a, b);
-        };
+        auto tm_frag = [&](int m, int s) { return load_frag<E>(sTb + tri_frag(m, s) * 512, lane); };
         // w: wave owns d_k slab `wslab` of row tiles wm0 .. wm0 + MPW - 1;
         // u: wave owns value tile `wave` (if any)
         const int wslab = wave % KS, wm0 = (wave / KS) * MPW;
