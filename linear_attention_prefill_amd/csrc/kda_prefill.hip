@@ -69,6 +69,11 @@ constexpr int kScanWarmAhead = 2;      // chunks between a scan stage's record a
 // VALU-bound factor phase and 34 KB out of LDS.
 template <typename E, int DK, int DV> struct IntraLds {
     static constexpr bool kStage = sizeof(E) == 2;  // V staged in LDS
+    // bf16: k P, V and e^{Gam_s} (all the w and u products read from the row
+    // factors) in two buffers, alternating by item, so that the next item's
+    // factor phase needs no barrier after this item's w and u.  fp32 has no
+    // room for the second k P.
+    static constexpr int NB = sizeof(E) == 2 ? 2 : 1;
     // Pitches.  A k P / q P row of d_k + 4 elements (4 mod 8) spreads the
     // factor phase's row writes and the fragment reads over the LDS banks:
     // against d_k + 8 (bf16) it stalls a third fewer cycles on bank
@@ -151,14 +156,14 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
     constexpr int MPW = KS / 2;                        // w row tiles per wave
     static_assert(FW <= NTH / 64 && VT <= 8, "thread mapping");
 
-    __shared__ __align__(16) E sKP[kChunk * KPP];      // k P
+    __shared__ __align__(16) E sKPb[LD::NB * kChunk * KPP];  // k P
     __shared__ __align__(16) E sQP[kChunk * KPP];      // q P
-    __shared__ __align__(16) E sV[LD::V_ELEMS];        // V
+    __shared__ __align__(16) E sVb[LD::NB * LD::V_ELEMS];   // V
     __shared__ __align__(16) float sKQ[kChunk * KQP];  // k Qf (fp32)
     __shared__ __align__(16) float sA[kChunk * AP];    // A_kk -> Tm
     __shared__ __align__(16) float sD[4 * kSub * DP];  // diagonal A_kk blocks
     __shared__ __align__(16) E sTb[6 * 512];           // Tm diag(beta) fragments, index tri_frag(m, s)
-    __shared__ __align__(16) float sBs[4 * DK];        // e^{Gam} at each block's first row
+    __shared__ __align__(16) float sBsb[LD::NB * 4 * DK];   // e^{Gam} at each block's first row
     __shared__ __align__(16) float sCe[4 * DK];        // e^{Gam_C - Gam} at each block's last row
     __shared__ __align__(16) float sF[10 * DK];        // F_IJ, J <= I, index I(I+1)/2 + J
     __shared__ __align__(16) float sBeta[kChunk];
@@ -284,7 +289,11 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
     for (int p = 0; p < VPT; ++p) settle(xv[p]);
     settle(bt);
 
+    int buf = 0;
     while (cur.item >= 0) {
+        E *const sKP = sKPb + buf * (kChunk * KPP);
+        E *const sV = sVb + buf * LD::V_ELEMS;
+        float *const sBs = sBsb + buf * (4 * DK);
         const int C = cur.C;
         const size_t rec = (size_t)cur.item;           // = cid * H + h
         E *const Rw = ws + rec * L::kRecElems;
@@ -684,7 +693,12 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
                 store_frag<E>(Rw + (m * KS + wslab) * 512, lane, frag_from_tiles<E>(acc0, acc1));
             }
         }
-        __syncthreads();   // LDS is rewritten by the next chunk
+        // Single-buffered, LDS is rewritten by the next chunk.  Double-
+        // buffered, the next chunk's factor phase writes only buffers that
+        // w and u no longer read, and its first barrier orders everything
+        // after it behind this chunk's w and u.
+        if constexpr (LD::NB == 1) __syncthreads();
+        buf ^= LD::NB - 1;
         cur = nxt;
     }
 }
