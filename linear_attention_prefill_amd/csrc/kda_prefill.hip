@@ -32,7 +32,10 @@
 // computed.  Per item: row factors (lanes hold four consecutive rows, DPP row
 // scans give the block prefixes), A blocks and the four diagonal inverses in
 // parallel, the off-diagonal inverse blocks in two levels on fp32 matrix
-// cores, then w and u; workspace fragments are written in the scan's order.
+// cores (which also leave Tm diag(beta) in LDS as bf16 fragments), then w and
+// u; workspace fragments are written in the scan's order.  For bf16 the row
+// factors that w and u read are double-buffered, so a wave that finishes
+// them starts the next item's row factors without waiting for the others.
 // kda_scan_kernel: one workgroup of 4 waves per (sequence, head, group of NS
 // 16-column slices of d_v); the d_v columns of S evolve independently, so
 // slices need no exchange.  Wave w owns chunk rows 16w..16w+15 and a quarter
