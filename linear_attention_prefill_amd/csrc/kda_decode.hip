@@ -23,8 +23,10 @@
 // workgroup 16 rows (one pass of its 256 threads, 4-8 KiB of state): many
 // small workgroups keep more of HBM busy than fewer large ones (measured, 64
 // sequences at H = 32, d = 128: 16 rows 45 us, 32 rows 46 us, 64 rows 47 us,
-// 128 rows 49 us).  The multi-token kernel keeps 64 rows, since each of its
-// workgroups stages every token's k, q and decay once.
+// 128 rows 49 us).  The multi-token kernel gives each workgroup 32 rows,
+// since each of its workgroups stages every token's k, q and decay once
+// (64 sequences x 4 tokens, verify and commit in one call: 64 rows 51.4 us,
+// 32 rows 49.5 us, 16 rows 55.3 us; a verify alone is 1 us slower at 32).
 //
 // Both kernels do a token's arithmetic through the same helpers, with every
 // multiply-add written out and contraction switched off, so T tokens in one
@@ -34,7 +36,7 @@
 
 namespace kda {
 
-constexpr int kDecodeRows = 64;    // state rows per workgroup, multi-token kernel
+constexpr int kDecodeRows = 32;    // state rows per workgroup, multi-token kernel
 constexpr int kStepRows = 16;      // state rows per workgroup, single-token step (one pass)
 
 // Sum over the 16 lanes of a DPP row, left in every lane (row_ror 8, 4, 2, 1).
