@@ -11,10 +11,23 @@ from oracle import oracle
 TOL = {"bf16": 2e-2, "f32": 1e-4}
 
 
+# pytest's capture manager, set by conftest.py when running under pytest.
+CAPTURE = None
+
+
 def announce(msg: str):
-    """Name the case before a GPU step (unbuffered, bypasses capture)."""
-    sys.__stderr__.write("[gpu-case] %s\n" % msg)
-    sys.__stderr__.flush()
+    """Name the case before a GPU step.  pytest captures at the file
+    descriptor level, so the line is written with capture suspended: it
+    reaches the terminal (or the log a run is redirected to) at once, and
+    survives a process that dies in the GPU step that follows."""
+    line = "[gpu-case] %s\n" % msg
+    if CAPTURE is not None:
+        with CAPTURE.global_and_fixture_disabled():
+            sys.stderr.write(line)
+            sys.stderr.flush()
+    else:
+        sys.__stderr__.write(line)
+        sys.__stderr__.flush()
 
 
 def torch_dtype(io):

@@ -31,6 +31,7 @@ def _check_case(case, tol=None, **kw):
                                      else case.N)
         live = (case.slots >= 0) & (case.slots < ns)
     eo, es = per_sequence_errors(case, o_g, o_r, pool_g, pool_r, live=live)
+    announce("  max relative error: o %.3g, state %.3g (tolerance %.3g)" % (eo, es, tol))
     assert eo <= tol, "o error %.3g > %.3g" % (eo, tol)
     assert es <= tol, "state error %.3g > %.3g" % (es, tol)
     return o_g, pool_g, o_r, pool_r, live
