@@ -162,8 +162,12 @@ size_t kda_prefill_workspace_size(const kda_prefill_desc_t *desc);
  * The state pools are addressed by lines as described above (dense when the
  * desc's strides are 0).
  *
- * Errors (returned before any launch): KDA_ERR_NULL for NULL desc, q, k, v,
- * g, beta, cu_seqlens, or o (when T > 0), or a NULL workspace of nonzero
+ * With T = 0 (every sequence empty) no row is read or written: q, k, v, g,
+ * beta and o may be NULL, and each live sequence's final state is its initial
+ * state.
+ *
+ * Errors (returned before any launch): KDA_ERR_NULL for NULL desc or
+ * cu_seqlens, for NULL q, k, v, g, beta or o when T > 0, or a NULL workspace of nonzero
  * required size; KDA_ERR_SHAPE for T < 0, N < 1, H < 1, num_slots < 0,
  * slots == NULL with a state pool given and num_slots < N, or state strides
  * that break the line rules; KDA_ERR_DTYPE;

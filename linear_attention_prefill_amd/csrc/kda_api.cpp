@@ -136,8 +136,9 @@ kda_status_t prefill_impl(const void *q, const void *k, const void *v, const flo
     if (!with_conv && d.conv_mode != KDA_CONV_NONE) return KDA_ERR_NULL;
     if (with_conv && d.conv_mode == KDA_CONV_NONE) return KDA_ERR_SHAPE;
     if (!slots && (state_in || state_out) && d.num_slots < d.num_seqs) return KDA_ERR_SHAPE;
-    if (!q || !k || !v || !g || !beta || !cu_seqlens) return KDA_ERR_NULL;
-    if (!o && d.total_rows > 0) return KDA_ERR_NULL;
+    // with no rows, no row input or output is touched
+    if (!cu_seqlens) return KDA_ERR_NULL;
+    if (d.total_rows > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
     const bool bf = d.io_dtype == KDA_BF16;
     const size_t rec_bytes = kda::prefill_workspace_bytes(d.total_rows, d.num_seqs, d.num_heads,
                                                           d.d_k, d.d_v, bf);

@@ -113,6 +113,7 @@ def test_prefill_rejects_bad_arguments(lib):
     for key in ("q", "k", "v", "g", "beta", "cu"):
         assert _prefill(lib, _desc(), **{key: None}) == 1, key
     assert _prefill(lib, _desc(), o=None) == 1
+    assert _prefill(lib, _desc(T=0), cu=None) == 1                    # cu_seqlens even with no rows
     assert _prefill(lib, _desc(), ws=None) == 1
     assert _prefill(lib, _desc(), q=A + 8) == 4                       # misaligned
     assert _prefill(lib, _desc(), sin=A + 4) == 4

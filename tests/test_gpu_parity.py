@@ -107,6 +107,34 @@ def test_padded_sequences_touch_nothing():
         np.testing.assert_array_equal(pool_g[s], c.state_pool[s])
 
 
+def test_zero_rows_pass_states_through():
+    """T = 0 with three sequences, all empty: no rows and no outputs; each
+    sequence's final state is its initial state (the recurrence over no
+    tokens), copied to its slot of a separate output pool bit for bit, and the
+    slots no sequence names keep their contents."""
+    H, d, num_slots = 2, 64, 5
+    for io in ("bf16", "f32"):
+        announce("prefill T=0 N=3 H=%d d=%d %s" % (H, d, io))
+        dt = torch_dtype(io)
+        # zero-row views of one-row buffers: non-null, aligned pointers
+        q, k, v = (torch.zeros((1, H, d), dtype=dt, device="cuda")[:0] for _ in range(3))
+        g = torch.zeros((1, H, d), dtype=torch.float32, device="cuda")[:0]
+        beta = torch.zeros((1, H), dtype=torch.float32, device="cuda")[:0]
+        cu = torch.zeros(4, dtype=torch.int32, device="cuda")
+        rng = np.random.default_rng(31)
+        s_in = dev((0.02 * rng.standard_normal((num_slots, H, d, d))).astype(np.float32))
+        s_out = torch.full_like(s_in, 7.0)
+        slots = torch.tensor([4, 0, 2], dtype=torch.int32, device="cuda")
+        o = lap.chunk_prefill(q, k, v, g, beta, cu, state_in=s_in, state_out=s_out, slots=slots,
+                              num_slots=num_slots)
+        torch.cuda.synchronize()
+        assert o.shape[0] == 0
+        for s in (4, 0, 2):
+            assert torch.equal(s_out[s], s_in[s])
+        for s in (1, 3):
+            assert torch.all(s_out[s] == 7.0)
+
+
 def test_identity_slots():
     c = W.random_case(24, [33, 100], H=2, d_k=64, d_v=64, io_dtype="bf16", num_slots=2)
     c.slots = None
