@@ -111,7 +111,8 @@ def test_zero_rows_pass_states_through():
     """T = 0 with three sequences, all empty: no rows and no outputs; each
     sequence's final state is its initial state (the recurrence over no
     tokens), copied to its slot of a separate output pool bit for bit, and the
-    slots no sequence names keep their contents."""
+    slots no sequence names keep their contents.  With the conv front end the
+    windows, which hold the last three inputs, stay as they were."""
     H, d, num_slots = 2, 64, 5
     for io in ("bf16", "f32"):
         announce("prefill T=0 N=3 H=%d d=%d %s" % (H, d, io))
@@ -133,6 +134,20 @@ def test_zero_rows_pass_states_through():
             assert torch.equal(s_out[s], s_in[s])
         for s in (1, 3):
             assert torch.all(s_out[s] == 7.0)
+        # the conv front end over no rows leaves every window as it was
+        announce("prefill+conv T=0 N=3 H=%d d=%d %s" % (H, d, io))
+        C = 3 * d
+        weight = dev(rng.standard_normal((H, 4, C)).astype(np.float32))
+        window = dev(rng.standard_normal((num_slots, H, 3, C)).astype(np.float32)).to(dt)
+        win0 = window.clone()
+        s_out.fill_(7.0)
+        lap.chunk_prefill(q, k, v, g, beta, cu, state_in=s_in, state_out=s_out, slots=slots,
+                          num_slots=num_slots, conv_weight=weight, conv_window=window,
+                          conv_activation="silu")
+        torch.cuda.synchronize()
+        assert torch.equal(window, win0)
+        for s in (4, 0, 2):
+            assert torch.equal(s_out[s], s_in[s])
 
 
 def test_identity_slots():
