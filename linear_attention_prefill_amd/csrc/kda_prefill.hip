@@ -760,7 +760,7 @@ __device__ __forceinline__ ScanWork scan_work(int b, int B, int N, int H, int JT
 }
 
 template <typename E, int DK, int DV, int NS>
-__global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
+__global__ __launch_bounds__(256, (sizeof(E) == 2 && NS > 1) ? 2 : 1) void kda_scan_kernel(
     const E *__restrict__ ws, const float *__restrict__ ws_dec,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ slots,
     const float *state_in, float *state_out, E *__restrict__ o,
@@ -769,11 +769,17 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     constexpr int TPW = DK / 64;                       // key tiles per wave
     using L = WsLayout<E, DK, DV>;
     using Stage = ScanStage<E, DK, NS>;
-    // Register stages of chunk operands in flight: three for one slice; two
-    // for two or four slices, whose extra S, u and output tiles would
-    // otherwise push the kernel past two workgroups per CU.  The L2 warm-up
-    // rides on the three-stage rotation only.
-    constexpr int STAGES = NS == 1 ? 3 : 2;
+    // Register stages of chunk operands in flight.  One slice (bf16): five,
+    // at one workgroup per CU, which is what one slice per workgroup runs at
+    // anyway (with more slices than CUs a second workgroup on the CU doubles
+    // its time).  Two or four slices: two, whose extra S, u and output tiles
+    // would otherwise push the kernel past two workgroups per CU.  fp32, one
+    // slice: three, with the L2 warm-up, which rides on the three-stage
+    // rotation only.  Five stages pull records as fast as three with the
+    // warm-up, without the warm-up's extra touches of record lines, which
+    // slow the next call's intra-chunk kernel by about 3 us on one 8192-row
+    // sequence.
+    constexpr int STAGES = NS > 1 ? 2 : (sizeof(E) == 2 ? 5 : 3);
     constexpr bool kWarm = STAGES == 3;
     // rounded copies of the state slabs and of U, [slice][slab][lane][8]
     __shared__ __align__(16) E sSb[NS * KS * 64 * 8];
@@ -820,7 +826,7 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
         }
 
     // Record of chunk cc, by part; each part of a stage is refilled with the
-    // chunk three ahead as soon as its last use in the current step has been
+    // chunk STAGES ahead as soon as its last use in the current step has been
     // issued, so loads trickle out between the matrix-core products instead
     // of queueing behind them in one burst.
     const int nch = (sp.len + kChunk - 1) / kChunk;
@@ -953,7 +959,19 @@ __global__ __launch_bounds__(256, sizeof(E) == 2 ? 2 : 1) void kda_scan_kernel(
     };
 
     if (nch > 0) {
-        if constexpr (STAGES == 3) {
+        if constexpr (STAGES == 5) {
+            Stage X[5];
+#pragma unroll
+            for (int i = 0; i < 5; ++i) load_stage(X[i], i < nch ? i : nch - 1, false);
+            int cc = 0;
+            for (; cc + 4 < nch; cc += 5) {
+#pragma unroll
+                for (int i = 0; i < 5; ++i) step(X[i], cc + i, true, false);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (cc + i < nch) step(X[i], cc + i, false, false);
+        } else if constexpr (STAGES == 3) {
             Stage A, Bs, Cs;
             load_stage(A, 0, kWarm);
             load_stage(Bs, nch > 1 ? 1 : 0, false);
