@@ -760,7 +760,7 @@ __device__ __forceinline__ ScanWork scan_work(int b, int B, int N, int H, int JT
 }
 
 template <typename E, int DK, int DV, int NS>
-__global__ __launch_bounds__(256, (sizeof(E) == 2 && NS > 1) ? 2 : 1) void kda_scan_kernel(
+__global__ __launch_bounds__(256, 1) void kda_scan_kernel(
     const E *__restrict__ ws, const float *__restrict__ ws_dec,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ slots,
     const float *state_in, float *state_out, E *__restrict__ o,
@@ -769,18 +769,19 @@ __global__ __launch_bounds__(256, (sizeof(E) == 2 && NS > 1) ? 2 : 1) void kda_s
     constexpr int TPW = DK / 64;                       // key tiles per wave
     using L = WsLayout<E, DK, DV>;
     using Stage = ScanStage<E, DK, NS>;
-    // Register stages of chunk operands in flight.  One slice (bf16): five,
-    // at one workgroup per CU, which is what one slice per workgroup runs at
-    // anyway (with more slices than CUs a second workgroup on the CU doubles
-    // its time).  Two or four slices: two, whose extra S, u and output tiles
-    // would otherwise push the kernel past two workgroups per CU.  fp32, one
-    // slice: three, with the L2 warm-up, which rides on the three-stage
-    // rotation only.  Five stages pull records as fast as three with the
-    // warm-up, without the warm-up's extra touches of record lines, which
-    // slow the next call's intra-chunk kernel by about 3 us on one 8192-row
-    // sequence.
-    constexpr int STAGES = NS > 1 ? 2 : (sizeof(E) == 2 ? 5 : 3);
-    constexpr bool kWarm = STAGES == 3;
+    // Register stages of chunk operands in flight, at one workgroup per CU:
+    // a second workgroup on a CU does not take records in any faster (with
+    // more slices than CUs it doubles the CU's time), while deeper stages
+    // keep more loads in flight.  One slice (bf16): five.  Two or four
+    // slices, whose extra S, u and output tiles take registers: three (16
+    // packed sequences: 253.4 -> 251.0 us a step against two stages at two
+    // workgroups per CU).  fp32, one slice: three, with the L2 warm-up, which
+    // rides on the one-slice three-stage rotation only.  Five stages pull
+    // records as fast as three with the warm-up, without the warm-up's extra
+    // touches of record lines, which slow the next call's intra-chunk kernel
+    // by about 3 us on one 8192-row sequence.
+    constexpr int STAGES = NS > 1 ? 3 : (sizeof(E) == 2 ? 5 : 3);
+    constexpr bool kWarm = NS == 1 && STAGES == 3;
     // rounded copies of the state slabs and of U, [slice][slab][lane][8]
     __shared__ __align__(16) E sSb[NS * KS * 64 * 8];
     __shared__ __align__(16) E sUb[NS * 2 * 64 * 8];
