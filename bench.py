@@ -1,27 +1,38 @@
 #!/usr/bin/env python3
 """KDA prefill throughput on one MI355X, with the roofline of the dominant kernel.
 
-    python bench.py [--steps K] [--warmup W] [--workload single|packed|decode|decode_tokens]
+    python bench.py [--steps K] [--warmup W] [--workload packed|single|long|decode|decode_tokens]
                     [--conv] [--tokens-mode MODE] [--no-extra] [--no-cpu-baseline]
 
 A step is one kda_chunk_prefill call (intra-chunk kernel + state scan) over
 one 8192-row chunk, with inputs already resident in HBM.  The default
-workload is one sequence of 8192 rows, H=32, d_k=d_v=128, bf16 q/k/v/o, fp32
-g/beta/state, zero initial state.  Inputs rotate over several device copies so
+workload is the packed chunk the metric names: 16 sequences of Dirichlet
+lengths in 8192 rows, H=32, d_k=d_v=128, bf16 q/k/v/o, fp32 g/beta, initial
+states gathered from a 64-slot fp32 pool by an int32 slot index and final
+states scattered back.  Inputs and pools rotate over several device copies so
 that the 256 MB last-level cache cannot serve a step from the previous one.
 About 150 ms of untimed calls run before the W warmup steps so that clocks
 have settled; then exactly K steps are timed between two events.
 
 Prints ONE JSON line.  Besides the throughput it reports:
-  roofline      the dominant kernel's algorithmic bytes per launch over its
-                average duration, from HIP events recorded on the launch
-                stream before, between and after the kernels in a second pass
-                of K steps (the events cost a few microseconds a step, so the
-                timed steps run without them), against 8 TB/s;
+  roofline      the method's algorithmic bytes per step (q, k, v, g, beta
+                read, o written, states read and written) over the dominant
+                kernel's average duration, against 8 TB/s; the durations come
+                from HIP events recorded on the launch stream before, between
+                and after the kernels in a second pass of K steps (those
+                events cost a few microseconds a step, so the timed steps run
+                without them); `traffic` is that kernel's HBM bytes from the
+                rocprofv3 FETCH_SIZE / WRITE_SIZE counters (profiles/traffic.json,
+                reported while the kernel sources match), `traffic_ratio` their
+                ratio to the algorithmic bytes;
+  path          the whole step against the HBM roof and the bf16 MFMA roof;
   cpu_baseline  the fp64 oracle timed on the host cores on the same inputs;
-  kernels       both kernels' average durations and algorithmic bytes;
-  path          the whole step's algorithmic bytes per token against HBM;
-  extra         the packed 16-sequence chunk and the 64-sequence decode step.
+  kernels       both kernels' average durations;
+  extra         the other workloads, each with its own roofline and CPU
+                baseline: one 8192-row sequence, the 262,144-token sequence
+                fed as 32 chained 8192-row calls (per call and for all rows),
+                the 64-sequence decode step; plus the conv front end and the
+                multi-token decode.
 """
 from __future__ import annotations
 
@@ -291,37 +302,75 @@ def time_decode_tokens(case, steps, warmup, copies, torch, lap, only=None):
     return res
 
 
-def cpu_baseline(case, seconds):
-    """The fp64 oracle on the same inputs, repeated until `seconds` elapse
-    (a bounded sample; heads are subsampled if one call would take longer)."""
+def host_cpus():
+    """Threads the CPU baseline uses and what they run on: the CPUs this
+    process may run on (sched_getaffinity), capped by a cgroup CPU quota when
+    one is set (a quota smaller than the affinity mask would only time-slice
+    extra threads), and the CPU model."""
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        aff = os.cpu_count() or 1
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, per = f.read().split()[:2]
+            if q != "max":
+                quota = max(1, int(int(q) / int(per)))
+    except (OSError, ValueError):
+        pass
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    threads = aff if quota is None else min(aff, quota)
+    return threads, {"affinity_cpus": aff, "cgroup_quota_cpus": quota, "cpu_model": model}
+
+
+def cpu_baseline(case, seconds, s0=None, label=None):
+    """The fp64 oracle on the same inputs, repeated until `seconds` elapse (a
+    bounded sample; heads are subsampled if one call would take longer).
+    s0: initial states [N, H, d_v, d_k] (the pool rows the call gathers)."""
     from oracle import oracle
-    threads = oracle.default_threads()
+    threads, info = host_cpus()
     H = case.H
     # probe one head to size the sample
     t0 = time.perf_counter()
     oracle.recurrence(case.q[:, :1], case.k[:, :1], case.v[:, :1], case.g[:, :1],
-                      case.beta[:, :1], case.cu_seqlens, threads=1)
+                      case.beta[:, :1], case.cu_seqlens,
+                      s0=None if s0 is None else s0[:, :1], threads=1)
     per_head = time.perf_counter() - t0
-    est_call = per_head * H / threads
+    est_call = per_head * H / min(threads, H * case.N)
     heads = H if est_call <= seconds else max(1, int(H * seconds / est_call))
     sl = slice(0, heads)
     args = (case.q[:, sl], case.k[:, sl], case.v[:, sl], case.g[:, sl], case.beta[:, sl])
+    s0s = None if s0 is None else np.ascontiguousarray(s0[:, sl])
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.recurrence(*args, case.cu_seqlens, threads=threads)
+        oracle.recurrence(*args, case.cu_seqlens, s0=s0s, threads=threads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 1000:
             break
     tok_s = case.T * reps * (heads / H) / el
-    return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%s: %d of %d heads, %d rows, %d repetition(s) in %.1f s (fp64 "
-                      "token-by-token recurrence in C; tokens/s scaled to all heads)"
-                      % (case.name, heads, H, case.T, reps, el),
-            "seconds": el}
+    out = {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": "%s: %d of %d heads, %d rows, %d repetition(s) in %.1f s (fp64 "
+                     "token-by-token recurrence in C; tokens/s scaled to all heads)"
+                     % (label or case.name, heads, H, case.T, reps, el),
+           "seconds": el, "tokens_per_s_per_core": tok_s / threads}
+    out.update(info)
+    return out
 
 
-def stored_traffic(kernel_name, src_hash):
+def stored_traffic(workload, kernel_name, src_hash):
+    """HBM bytes per launch of a kernel on a workload, from the FETCH_SIZE /
+    WRITE_SIZE counters stored in profiles/traffic.json, while the kernel
+    sources they were taken at match."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -329,8 +378,93 @@ def stored_traffic(kernel_name, src_hash):
         return None
     if t.get("source_hash") != src_hash:
         return None
-    k = t.get("kernels", {}).get(kernel_name)
+    k = t.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel_name)
     return None if k is None else k.get("bytes_per_launch")
+
+
+def prefill_line(case, r, src_hash, conv=False):
+    """Throughput, kernels, roofline and path figures of one prefill workload
+    from its timings."""
+    lengths = np.diff(case.cu_seqlens).tolist()
+    T, H, dk, dv = case.T, case.H, case.d_k, case.d_v
+    es = 2 if case.io_dtype == "bf16" else 4
+    n_live = case.N
+    pb = path_bytes(T, H, dk, dv, es, n_live, r["state_in"], True)
+    pf = path_flops(lengths, H, dk, dv)
+    kern = {
+        "kda_intra_kernel": {"us": r["intra_ms"] * 1e3, "us_median": r["intra_ms_median"] * 1e3},
+        "kda_scan_kernel": {"us": r["scan_ms"] * 1e3, "us_median": r["scan_ms_median"] * 1e3},
+    }
+    dom = max(kern, key=lambda n: kern[n]["us"])
+    t_dom = kern[dom]["us"] * 1e-6
+    achieved = pb / t_dom / 1e9
+    traffic = None if conv else stored_traffic(case.name, dom, src_hash)
+    step_s = r["ms_per_step"] * 1e-3
+    line = {
+        "workload": case.name + ("+conv3_silu" if conv else ""),
+        "value": T / step_s, "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_ratio": None if traffic is None else traffic / pb,
+                     "kernel": dom, "algorithmic_bytes": pb},
+        "kernels": kern,
+        "path": {"bytes_per_step": pb, "GB/s": pb / step_s / 1e9,
+                 "frac_hbm": pb / step_s / 1e9 / HBM_PEAK_GBS,
+                 "flops_per_step": pf,
+                 "TFLOP/s": pf / step_s / 1e12,
+                 "frac_mfma_bf16": pf / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+    }
+    return line
+
+
+def time_long_context(steps, warmup, torch, lap, log_fn):
+    """The 262,144-token sequence as 32 chained 8192-row calls (state carried
+    in a one-slot pool).  A pass is all 32 calls; `steps` passes are timed
+    after `warmup` ones.  Each call reads its own rows, so no call finds its
+    inputs in the last-level cache."""
+    from linear_attention_prefill_amd import workloads as W
+    n_calls, L, H, d = W.LONG_CONTEXT_CALLS, 8192, 32, 128
+    t0 = time.time()
+    calls = [W.long_context_call(c) for c in range(n_calls)]
+    log_fn("generated the 32 long-context calls in %.1f s" % (time.time() - t0))
+    T = n_calls * L
+    Q = torch.empty((T, H, d), dtype=torch.bfloat16, device="cuda")
+    K, V = torch.empty_like(Q), torch.empty_like(Q)
+    G = torch.empty((T, H, d), dtype=torch.float32, device="cuda")
+    B = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    for c, case in enumerate(calls):
+        rows = slice(c * L, (c + 1) * L)
+        Q[rows] = torch.from_numpy(case.q).to("cuda").to(torch.bfloat16)
+        K[rows] = torch.from_numpy(case.k).to("cuda").to(torch.bfloat16)
+        V[rows] = torch.from_numpy(case.v).to("cuda").to(torch.bfloat16)
+        G[rows] = torch.from_numpy(case.g).to("cuda")
+        B[rows] = torch.from_numpy(case.beta).to("cuda")
+    cu = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+    slot0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pool = torch.zeros((1, H, d, d), dtype=torch.float32, device="cuda")
+    o = torch.empty((L, H, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(lap.prefill_workspace_size(L, 1, H, d, d, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+
+    def one_pass():
+        pool.zero_()
+        for c in range(n_calls):
+            rows = slice(c * L, (c + 1) * L)
+            lap.chunk_prefill(Q[rows], K[rows], V[rows], G[rows], B[rows], cu, state_in=pool,
+                              state_out=pool, o=o, slots=slot0, workspace=ws)
+
+    prewarm(lambda i: one_pass(), torch)
+    for _ in range(warmup):
+        one_pass()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        one_pass()
+    end.record()
+    torch.cuda.synchronize()
+    pass_ms = start.elapsed_time(end) / steps
+    return calls, {"pass_ms": pass_ms, "call_ms": pass_ms / n_calls, "rows": T}
 
 
 def main():
@@ -338,9 +472,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["single", "packed", "decode", "decode_tokens"],
-                    default="single",
-                    help="single: 1 x 8192 rows (default); packed: 16 sequences in 8192 rows; "
+    ap.add_argument("--workload", choices=["packed", "single", "long", "decode", "decode_tokens"],
+                    default="packed",
+                    help="packed: 16 sequences in 8192 rows (default, the metric's chunk); "
+                         "single: 1 x 8192 rows; long: 262,144 rows as 32 chained calls; "
                          "decode: 64 sequences x 1 token (profiling the decode kernel); "
                          "decode_tokens: 64 sequences x 4 draft tokens (multi-token decode)")
     ap.add_argument("--copies", type=int, default=3, help="rotated device copies of the inputs")
@@ -348,7 +483,8 @@ def main():
                     help="prefill workloads: run the short conv front end (SiLU) before the path")
     ap.add_argument("--tokens-mode", choices=["verify_commit", "verify", "commit"], default=None,
                     help="decode_tokens workload: time only this mode (default: all three)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU baseline of the headline workload (the extra workloads get a third)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -369,6 +505,18 @@ def main():
         sys.stderr.write("bench.py needs a GPU\n")
         sys.exit(1)
     lap.load_library()
+    src_hash = kernel_source_hash()
+    extra_cpu_s = args.cpu_seconds / 3
+
+    def decode_line(dc, rd, conv=False):
+        line = {"workload": dc.name + ("+conv3_silu" if conv else ""),
+                "value": dc.N / (rd["us"] * 1e-6), "unit": "tokens/s",
+                "ms_per_step": rd["us"] * 1e-3,
+                "roofline": {"bound": "hbm", "achieved": rd["GB/s"], "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": rd["frac_hbm"], "traffic": None,
+                             "kernel": "kda_decode_conv_kernel" if conv else "kda_decode_kernel",
+                             "algorithmic_bytes": rd["bytes"]}}
+        return line
 
     if args.workload == "decode":
         dc = W.decode_case()
@@ -377,15 +525,14 @@ def main():
             cw = W.draw_conv(12, dc.state_pool.shape[0], dc.H, dc.d_k, dc.d_v, dc.io_dtype)
             conv = (cw[0], cw[1], "silu")
         rd = time_decode(dc, args.steps, args.warmup, 4, torch, lap, conv=conv)
+        ln = decode_line(dc, rd, bool(conv))
         out = {"metric": "KDA decode step: state read-modify-write bandwidth on 1 MI355X",
                "value": rd["GB/s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
                "warmup": args.warmup, "ms_per_step": rd["us"] * 1e-3, "higher_is_better": True,
                "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-               "config": {"workload": dc.name + ("+conv3_silu" if conv else ""), "num_seqs": dc.N,
+               "config": {"workload": ln["workload"], "num_seqs": dc.N,
                           "heads": dc.H, "d_k": dc.d_k, "d_v": dc.d_v, "pools_rotated": 4},
-               "roofline": {"bound": "hbm", "achieved": rd["GB/s"], "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": rd["frac_hbm"], "traffic": None,
-                            "kernel": "kda_decode_conv_kernel" if conv else "kda_decode_kernel"}}
+               "roofline": ln["roofline"]}
         print(json.dumps(out), flush=True)
         return
     if args.workload == "decode_tokens":
@@ -405,14 +552,23 @@ def main():
                "modes": rm}
         print(json.dumps(out), flush=True)
         return
+    if args.workload == "long":
+        calls, rl = time_long_context(args.steps, args.warmup, torch, lap, log)
+        out = {"metric": "KDA prefill tokens/s on 1 MI355X, 262,144-token sequence as 32 chained "
+                         "8192-row calls",
+               "value": rl["rows"] / (rl["pass_ms"] * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup, "ms_per_step": rl["pass_ms"],
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+               "data": "synthetic",
+               "config": {"workload": "long_context_32x8192_H32_d128_bf16", "calls": len(calls)},
+               "per_call_ms": rl["call_ms"]}
+        print(json.dumps(out), flush=True)
+        return
 
     t0 = time.time()
-    case = W.single_seq_prefill() if args.workload == "single" else W.packed_varlen_prefill()
+    case = W.packed_varlen_prefill() if args.workload == "packed" else W.single_seq_prefill()
     log("generated %s in %.1f s" % (case.name, time.time() - t0))
-    lengths = np.diff(case.cu_seqlens).tolist()
     T, H, dk, dv = case.T, case.H, case.d_k, case.d_v
-    es = 2 if case.io_dtype == "bf16" else 4
-    n_chunks = chunk_count(lengths)
 
     conv = None
     if args.conv:
@@ -420,30 +576,13 @@ def main():
                          dv, case.io_dtype)
         conv = (cw[0], cw[1], "silu")
     r = time_prefill(case, args.steps, args.warmup, args.copies, torch, lap, conv=conv)
-    log("prefill%s %.1f us/step (intra %.1f us, scan %.1f us)"
-        % (" with conv" if conv else "", r["ms_per_step"] * 1e3, r["intra_ms"] * 1e3,
+    log("%s%s: %.1f us/step (intra %.1f us, scan %.1f us)"
+        % (case.name, " with conv" if conv else "", r["ms_per_step"] * 1e3, r["intra_ms"] * 1e3,
            r["scan_ms"] * 1e3))
-    n_live = case.N
-    ib = intra_bytes(T, H, dk, dv, es, n_chunks)
-    sb = scan_bytes(T, H, dk, dv, es, n_chunks, n_live, r["state_in"], True)
-    pb = path_bytes(T, H, dk, dv, es, n_live, r["state_in"], True)
-    pf = path_flops(lengths, H, dk, dv)
-    kern = {
-        "kda_intra_kernel": {"us": r["intra_ms"] * 1e3, "us_median": r["intra_ms_median"] * 1e3,
-                             "bytes_per_launch": ib,
-                             "GB/s": ib / (r["intra_ms"] * 1e-3) / 1e9},
-        "kda_scan_kernel": {"us": r["scan_ms"] * 1e3, "us_median": r["scan_ms_median"] * 1e3,
-                            "bytes_per_launch": sb,
-                            "GB/s": sb / (r["scan_ms"] * 1e-3) / 1e9},
-    }
-    dom = max(kern, key=lambda n: kern[n]["us"])
-    achieved = kern[dom]["GB/s"]
-    src_hash = kernel_source_hash()
-    traffic = stored_traffic(dom, src_hash)
-    value = T / (r["ms_per_step"] * 1e-3)
+    head = prefill_line(case, r, src_hash, conv=bool(conv))
     out = {
         "metric": METRIC,
-        "value": value,
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -454,48 +593,65 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": case.name + ("+conv3_silu" if conv else ""), "total_rows": T, "num_seqs": case.N, "heads": H,
-                   "d_k": dk, "d_v": dv, "chunk": 64, "io_dtype": case.io_dtype,
-                   "state": "fp32", "initial_state": "pool" if r["state_in"] else "zero",
+        "config": {"workload": head["workload"], "total_rows": T, "num_seqs": case.N,
+                   "heads": H, "d_k": dk, "d_v": dv, "chunk": 64, "io_dtype": case.io_dtype,
+                   "state": "fp32",
+                   "initial_state": "pool-gathered" if r["state_in"] else "zero",
                    "input_copies_rotated": args.copies},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic, "kernel": dom},
-        "kernels": kern,
-        "path": {"bytes_per_step": pb, "GB/s": pb / (r["ms_per_step"] * 1e-3) / 1e9,
-                 "frac_hbm": pb / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                 "flops_per_step": pf,
-                 "frac_mfma_bf16": pf / (r["ms_per_step"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "roofline": head["roofline"],
+        "kernels": head["kernels"],
+        "path": head["path"],
         "kernel_source_hash": src_hash,
     }
+    slots0 = lambda c: None if c.state_pool is None else c.state_pool[c.slots]
     if not args.no_extra:
         extra = {}
-        if args.workload == "single":
-            pc = W.packed_varlen_prefill()
-            rp = time_prefill(pc, max(5, args.steps // 2), 2, args.copies, torch, lap)
-            extra["packed"] = {"workload": pc.name, "us": rp["ms_per_step"] * 1e3,
-                               "tokens/s": pc.T / (rp["ms_per_step"] * 1e-3),
-                               "intra_us": rp["intra_ms"] * 1e3, "scan_us": rp["scan_ms"] * 1e3}
-            log("packed %.1f us/step" % (rp["ms_per_step"] * 1e3))
-            cw = W.draw_conv(11, 1, H, dk, dv, case.io_dtype)
-            rc = time_prefill(case, max(5, args.steps // 2), 2, args.copies, torch, lap,
-                              conv=(cw[0], cw[1], "silu"))
-            conv_us = (rc["ms_per_step"] - rc["intra_ms"] - rc["scan_ms"]) * 1e3
-            extra["prefill_conv"] = {"workload": case.name + "+conv3_silu",
-                                     "us": rc["ms_per_step"] * 1e3,
-                                     "tokens/s": T / (rc["ms_per_step"] * 1e-3),
-                                     "conv_us": conv_us, "intra_us": rc["intra_ms"] * 1e3,
-                                     "scan_us": rc["scan_ms"] * 1e3}
-            log("prefill with conv %.1f us/step (conv front end %.1f us)"
-                % (rc["ms_per_step"] * 1e3, conv_us))
+        other = W.single_seq_prefill() if args.workload == "packed" else W.packed_varlen_prefill()
+        ro = time_prefill(other, args.steps, args.warmup, args.copies, torch, lap)
+        lo = prefill_line(other, ro, src_hash)
+        log("%s: %.1f us/step" % (other.name, ro["ms_per_step"] * 1e3))
+        if not args.no_cpu_baseline:
+            lo["cpu_baseline"] = cpu_baseline(other, extra_cpu_s, s0=slots0(other))
+        extra["single" if args.workload == "packed" else "packed"] = lo
+
+        calls, rl = time_long_context(max(3, args.steps // 4), 1, torch, lap, log)
+        ll = {"workload": "long_context_32x8192_H32_d128_bf16",
+              "value": rl["rows"] / (rl["pass_ms"] * 1e-3), "unit": "tokens/s",
+              "ms_all_rows": rl["pass_ms"], "ms_per_call": rl["call_ms"],
+              "per_call_tokens/s": 8192 / (rl["call_ms"] * 1e-3),
+              "path": {"bytes_per_call": path_bytes(8192, 32, 128, 128, 2, 1, True, True),
+                       "frac_hbm": path_bytes(8192, 32, 128, 128, 2, 1, True, True)
+                       / (rl["call_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+        log("long context: %.2f ms for 262,144 rows, %.1f us a call"
+            % (rl["pass_ms"], rl["call_ms"] * 1e3))
+        if not args.no_cpu_baseline:
+            c0 = calls[0]
+            ll["cpu_baseline"] = cpu_baseline(c0, extra_cpu_s,
+                                              label="long-context call 0 (per-row cost is that "
+                                                    "of every call)")
+        extra["long_context"] = ll
+        del calls
+
         dc = W.decode_case()
         rd = time_decode(dc, max(10, args.steps), 3, 4, torch, lap)
-        rd["workload"] = dc.name
-        extra["decode"] = rd
+        ld = decode_line(dc, rd)
         log("decode %.1f us, %.0f GB/s" % (rd["us"], rd["GB/s"]))
+        if not args.no_cpu_baseline:
+            ld["cpu_baseline"] = cpu_baseline(dc, extra_cpu_s, s0=slots0(dc))
+        extra["decode"] = ld
+
+        cw = W.draw_conv(11, 1 if case.state_pool is None else case.state_pool.shape[0], H, dk,
+                         dv, case.io_dtype)
+        rc = time_prefill(case, max(5, args.steps // 2), 2, args.copies, torch, lap,
+                          conv=(cw[0], cw[1], "silu"))
+        lc = prefill_line(case, rc, src_hash, conv=True)
+        lc["conv_us"] = (rc["ms_per_step"] - rc["intra_ms"] - rc["scan_ms"]) * 1e3
+        extra["prefill_conv"] = lc
+        log("%s with conv %.1f us/step (conv front end %.1f us)"
+            % (case.name, rc["ms_per_step"] * 1e3, lc["conv_us"]))
         cw = W.draw_conv(12, dc.state_pool.shape[0], dc.H, dc.d_k, dc.d_v, dc.io_dtype)
         rdc = time_decode(dc, max(10, args.steps), 3, 4, torch, lap, conv=(cw[0], cw[1], "silu"))
-        rdc["workload"] = dc.name + "+conv3_silu"
-        extra["decode_conv"] = rdc
+        extra["decode_conv"] = decode_line(dc, rdc, conv=True)
         log("decode with conv %.1f us, %.0f GB/s" % (rdc["us"], rdc["GB/s"]))
         mc = W.decode_tokens_case()
         rm = time_decode_tokens(mc, max(10, args.steps), 3, 4, torch, lap)
@@ -514,8 +670,9 @@ def main():
         out["calibration"] = {"kernel": "torch add (elementwise)", "read_bytes": 4 * n,
                               "write_bytes": 4 * n}
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(case, args.cpu_seconds)
-        log("cpu baseline %.0f tokens/s on %d threads" % (cb["value"], cb["cores"]))
+        cb = cpu_baseline(case, args.cpu_seconds, s0=slots0(case))
+        log("cpu baseline %.0f tokens/s on %d threads (%s)" % (cb["value"], cb["cores"],
+                                                               cb["cpu_model"]))
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
 

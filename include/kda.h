@@ -29,8 +29,9 @@
  *   slots     [N] int32 on the device, or NULL for slot n = n.
  *
  * Ownership and execution.  The caller owns every buffer, including the
- * workspace; the library allocates nothing, keeps no mutable global state and
- * caches no tensors.  Every call validates its arguments on the host and
+ * workspace; the library allocates nothing and caches no tensors.  Its only
+ * process-wide state is a per-device cache of the compute-unit count, which
+ * sizes the persistent grids.  Every call validates its arguments on the host and
  * returns a status before anything is launched; then it enqueues its kernels
  * on `stream` (a hipStream_t; NULL is the null stream) and returns without
  * synchronising.  It never reads device memory on the host, so a call can be
@@ -42,7 +43,15 @@
  * kernels clamp it so that no access leaves the buffers: cu_seqlens entries
  * are clamped to [0, T] and each sequence to [cu[n], T]; a slot outside
  * [0, num_slots) marks a padded sequence.  Results for non-monotone
- * cu_seqlens or duplicate slots are unspecified.
+ * cu_seqlens or duplicate slots are unspecified.  kda_prefill_check tests
+ * these preconditions, and g <= 0, on the device when a caller asks for it.
+ *
+ * g <= 0 (a decaying state) is a precondition of the prefill's split decay
+ * factors, which never exceed 1 under it.  With some g > 0 the same
+ * factoring runs with factors above 1: a state that grows by at most a few
+ * e-folds per 64-row chunk is computed to the usual accuracy (a GPU test
+ * covers g up to +0.02), while a chunk whose cumulative growth of a channel
+ * passes about 2^64 can overflow and gives unspecified results.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -137,7 +146,11 @@ typedef struct {
  * Bytes of device workspace kda_chunk_prefill needs for `desc` (0 if desc is
  * invalid).  The workspace holds the per-chunk operands that pass from the
  * intra-chunk kernel to the state scan, and with a conv mode the convolved
- * q, k and v; it is scratch for one call.
+ * q, k and v.  As in the "kern" page, section "The manifest", workspace is
+ * scratch that lasts one call; the caller allocates it, as its hosts
+ * allocate their own pools (same page, section "Hosts"), and may reuse it
+ * for every call whose size it covers once the previous call on it is done
+ * in stream order.
  */
 size_t kda_prefill_workspace_size(const kda_prefill_desc_t *desc);
 
@@ -309,10 +322,42 @@ kda_status_t kda_decode_tokens(const void *q, const void *k, const void *v,
                                int64_t state_slot_stride, int64_t state_head_stride,
                                void *stream);
 
-/* Static description of a status code. */
+/*
+ * Opt-in check of the device-side preconditions that kda_chunk_prefill
+ * documents but does not test (testing them inside the call would need a
+ * host sync; the "kern" page, section "The manifest", rejects calls outside
+ * their bounds before they launch, and this gives a caller that guarantee
+ * for the device data).  Enqueued on `stream`: it sets *flags (device int32,
+ * written by the call, no need to clear it) to the OR of
+ *   KDA_CHECK_CU_SEQLENS  cu_seqlens[0] != 0, cu_seqlens[N] != T, or a
+ *                         decreasing step;
+ *   KDA_CHECK_G           some g > 0 or NaN;
+ *   KDA_CHECK_SLOTS       two sequences name the same slot in [0, num_slots)
+ *                         (looked for when N <= 4096);
+ * or 0 when all hold.  g may be NULL when T = 0, slots NULL for slot n = n.
+ * Only the desc's sizes are used.  It reads nothing outside the buffers the
+ * desc sizes, so it is safe on malformed data.  Errors: KDA_ERR_NULL for a
+ * NULL desc, cu_seqlens or flags, or a NULL g with T > 0; desc errors as for
+ * kda_chunk_prefill; KDA_ERR_ALIGN; KDA_ERR_HIP if a launch fails.
+ */
+enum { KDA_CHECK_CU_SEQLENS = 1, KDA_CHECK_G = 2, KDA_CHECK_SLOTS = 4 };
+kda_status_t kda_prefill_check(const float *g, const int32_t *cu_seqlens, const int32_t *slots,
+                               const kda_prefill_desc_t *desc, int32_t *flags, void *stream);
+
+/*
+ * Static description of a status code.  Every call validates its arguments
+ * on the host and returns one of these codes before anything launches, as
+ * the "kern" page, section "The manifest", rejects a call outside its bounds
+ * before it launches.
+ */
 const char *kda_status_string(kda_status_t status);
 
-/* Library ABI version (major * 100 + minor). */
+/*
+ * Library ABI version (major * 100 + minor), so that a host can check which
+ * C ABI the library it loaded implements before it binds the calls (the
+ * "kern" page, section "Hosts": the runtime checks what a host hands it
+ * against what it declares).
+ */
 int32_t kda_version(void);
 
 #ifdef __cplusplus

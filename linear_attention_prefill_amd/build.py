@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["kda_prefill.hip", "kda_decode.hip", "kda_conv.hip"]
+HIP_SOURCES = ["kda_prefill.hip", "kda_decode.hip", "kda_conv.hip", "kda_check.hip"]
 CXX_SOURCES = ["kda_api.cpp"]
 
 # Packed fp32 VALU ops are disabled for all device code.

@@ -6,6 +6,8 @@
 
 #include <limits.h>
 
+#include <atomic>
+
 namespace {
 
 using bf16 = __bf16;
@@ -57,12 +59,26 @@ hipError_t dispatch_decode_conv(const kda::DecodeArgs &a, const kda::ConvArgs &c
     return kda::launch_decode_conv<E, 128, 128>(a, c, s);
 }
 
-// Compute units of the current device (persistent grids are sized by it).
-int device_cus() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
+// Compute units of the device a stream runs on (persistent grids are sized
+// by it), queried once per device id.  The cache is the library's only
+// process-wide state; it holds a hardware constant, so concurrent first calls
+// store the same value.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus(hipStream_t s) {
+    int dev = 0;
+    if (!s || hipStreamGetDevice(s, &dev) != hipSuccess) {
+        if (hipGetDevice(&dev) != hipSuccess) return 256;
+    }
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = g_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
         return 256;
+    if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 
@@ -161,6 +177,7 @@ kda_status_t prefill_impl(const void *q, const void *k, const void *v, const flo
         return KDA_ERR_SHAPE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();       // an earlier call's error is not this call's
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens;
     if (with_conv) {
@@ -183,7 +200,7 @@ kda_status_t prefill_impl(const void *q, const void *k, const void *v, const flo
     a.slot_stride = ss;
     a.head_stride = hs;
     for (int i = 0; i < 3; ++i) a.events[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
-    a.num_cus = device_cus();
+    a.num_cus = device_cus(s);
     const hipError_t e = bf ? dispatch_prefill<bf16>(a, d.d_k, d.d_v, s)
                             : dispatch_prefill<float>(a, d.d_k, d.d_v, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -218,6 +235,7 @@ kda_status_t decode_impl(const void *q, const void *k, const void *v, const floa
     a.head_stride = hs;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf = io_dtype == KDA_BF16;
+    (void)hipGetLastError();       // an earlier call's error is not this call's
     hipError_t e;
     if (conv_mode != KDA_CONV_NONE)
         e = bf ? dispatch_decode_conv<bf16>(a, c, d_k, d_v, s)
@@ -332,8 +350,26 @@ kda_status_t kda_decode_tokens(const void *q, const void *k, const void *v, cons
     a.accept = num_accepted;
     a.commit = commit ? 1 : 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();       // an earlier call's error is not this call's
     const hipError_t e = io_dtype == KDA_BF16 ? dispatch_decode_tokens<bf16>(a, d_k, d_v, s)
                                               : dispatch_decode_tokens<float>(a, d_k, d_v, s);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_prefill_check(const float *g, const int32_t *cu_seqlens, const int32_t *slots,
+                               const kda_prefill_desc_t *desc, int32_t *flags, void *stream) {
+    const kda_status_t st = check_desc(desc);
+    if (st != KDA_OK) return st;
+    if (!cu_seqlens || !flags) return KDA_ERR_NULL;
+    if (desc->total_rows > 0 && !g) return KDA_ERR_NULL;
+    const void *ptrs[] = {g, cu_seqlens, slots, flags};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+    (void)hipGetLastError();       // an earlier call's error is not this call's
+    const hipError_t e = kda::launch_prefill_check(g, cu_seqlens, slots, desc->total_rows,
+                                                   desc->num_seqs, desc->num_heads, desc->d_k,
+                                                   desc->num_slots, flags,
+                                                   static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -351,6 +387,6 @@ const char *kda_status_string(kda_status_t status) {
     return "unknown status";
 }
 
-int32_t kda_version(void) { return 103; }
+int32_t kda_version(void) { return 104; }
 
 }  // extern "C"

@@ -78,6 +78,13 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 template <typename E, int DK, int DV>
 hipError_t launch_decode_tokens(const DecodeArgs &a, hipStream_t stream);
 
+// Opt-in check of the prefill's device data (kda_prefill_check): clears
+// *flags, then ORs in a KDA_CHECK_* bit per violated precondition.
+constexpr int kCheckMaxPairsSeqs = 4096;   // duplicate slots looked for up to this N
+hipError_t launch_prefill_check(const float *g, const int32_t *cu, const int32_t *slots, int T,
+                                int N, int H, int dk, int num_slots, int32_t *flags,
+                                hipStream_t stream);
+
 size_t prefill_workspace_bytes(int T, int N, int H, int dk, int dv, bool bf16);
 
 // Workspace bytes of the convolved q, k, v (placed after the records).

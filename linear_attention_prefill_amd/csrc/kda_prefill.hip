@@ -781,6 +781,7 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
     // touches of record lines, which slow the next call's intra-chunk kernel
     // by about 3 us on one 8192-row sequence.
     constexpr int STAGES = NS > 1 ? 3 : (sizeof(E) == 2 ? 5 : 3);
+    static_assert(STAGES == 3 || STAGES == 5, "register stages");
     constexpr bool kWarm = NS == 1 && STAGES == 3;
     // rounded copies of the state slabs and of U, [slice][slab][lane][8]
     __shared__ __align__(16) E sSb[NS * KS * 64 * 8];
@@ -972,7 +973,7 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (cc + i < nch) step(X[i], cc + i, false, false);
-        } else if constexpr (STAGES == 3) {
+        } else {
             Stage A, Bs, Cs;
             load_stage(A, 0, kWarm);
             load_stage(Bs, nch > 1 ? 1 : 0, false);
@@ -985,16 +986,6 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
             }
             if (cc < nch) step(A, cc, false, kWarm);
             if (cc + 1 < nch) step(Bs, cc + 1, false, false);
-        } else {
-            Stage A, Bs;
-            load_stage(A, 0, false);
-            load_stage(Bs, nch > 1 ? 1 : 0, false);
-            int cc = 0;
-            for (; cc + 1 < nch; cc += 2) {
-                step(A, cc, true, false);
-                step(Bs, cc + 1, true, false);
-            }
-            if (cc < nch) step(A, cc, false, false);
         }
     }
 
@@ -1016,6 +1007,9 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     E *ws = reinterpret_cast<E *>(a.workspace);
     float *ws_dec = reinterpret_cast<float *>(reinterpret_cast<char *>(a.workspace) +
                                               (size_t)max_chunks * a.H * L::kRecElems * sizeof(E));
+    // An error left by an unrelated earlier call is not this call's: clear
+    // it, so that the checks below see only this call's launches.
+    (void)hipGetLastError();
     if (a.events[0]) (void)hipEventRecord(a.events[0], stream);
     if (max_chunks > 0) {
         const long long items = (long long)max_chunks * a.H;
@@ -1023,6 +1017,10 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
         kda_intra_kernel<E, DK, DV><<<dim3(grid), dim3(kIntraThreads), 0, stream>>>(
             static_cast<const E *>(a.q), static_cast<const E *>(a.k), static_cast<const E *>(a.v),
             a.g, a.beta, a.cu_seqlens, a.T, a.N, a.H, ws, ws_dec);
+        // A failed intra launch leaves stale records: the scan must not run
+        // on them and overwrite o and the caller's states.
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     if (a.events[1]) (void)hipEventRecord(a.events[1], stream);
     // The scan is bound by the record bytes each CU takes in, and a workgroup

@@ -88,6 +88,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_decode_tokens.restype = ctypes.c_int
     lib.kda_decode_tokens.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       i32, i32, i32, i32, i32, i32, i32, f32, i32, i64, i64, vp]
+    lib.kda_prefill_check.restype = ctypes.c_int
+    lib.kda_prefill_check.argtypes = [vp, vp, vp, ctypes.POINTER(PrefillDesc), vp, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_version.restype = i32
@@ -130,9 +132,41 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _stream_obj(stream):
+    return torch.cuda.current_stream() if stream is None else stream
+
+
 def _stream(stream) -> ctypes.c_void_p:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(_stream_obj(stream).cuda_stream)
+
+
+# kda_prefill_check flag bits (kda.h) and what each says.
+CHECK_BITS = {1: "cu_seqlens must start at 0, end at T and never decrease",
+              2: "g must be <= 0 (and not NaN)",
+              4: "two live sequences name the same slot"}
+
+
+def check_prefill_inputs(g, cu_seqlens, slots=None, num_slots=None, stream=None) -> int:
+    """Opt-in check of the device-side preconditions of chunk_prefill
+    (``kda_prefill_check``): returns the KDA_CHECK_* bits of the violated
+    ones, 0 when all hold.  Reads the flag back, so it synchronises with the
+    launch stream."""
+    lib = load_library()
+    _dev(g, "g", torch.float32)
+    T, H, dk = g.shape
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    N = cu_seqlens.shape[0] - 1
+    _dev(slots, "slots", torch.int32, (N,) if slots is not None else None)
+    if num_slots is None:
+        num_slots = N
+    desc = make_desc(T, N, H, dk, dk, num_slots, KDA_F32)
+    s = _stream_obj(stream)
+    with torch.cuda.stream(s):
+        flags = torch.empty(4, dtype=torch.int32, device=g.device)
+    _check(lib.kda_prefill_check(_ptr(g) if T > 0 else None, _ptr(cu_seqlens), _ptr(slots),
+                                 ctypes.byref(desc), _ptr(flags), _stream(stream)))
+    s.synchronize()
+    return int(flags[0].item())
 
 
 def make_desc(T, N, H, d_k, d_v, num_slots, io_dtype, scale=1.0, slot_stride=0,
@@ -208,7 +242,8 @@ def prefill_workspace_size(T, N, H, d_k, d_v, dtype=torch.bfloat16, conv=False) 
 def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o=None,
                   slots=None, num_slots=None, scale=1.0, workspace=None, stream=None,
                   events=None, state_slot_stride=0, state_head_stride=0, conv_weight=None,
-                  conv_window=None, conv_activation="none", conv_strides=(0, 0, 0, 0)):
+                  conv_window=None, conv_activation="none", conv_strides=(0, 0, 0, 0),
+                  check_inputs=False):
     """KDA chunked prefill over packed sequences (see ``kda_chunk_prefill``).
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype); g: [T, H, d_k]
@@ -224,7 +259,11 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
     events: optional three recorded
     torch.cuda.Event(enable_timing=True) objects, recorded before the
     intra-chunk kernel, between the kernels and after the scan
-    (``kda_chunk_prefill_timed``).  Returns o [T, H, d_v].
+    (``kda_chunk_prefill_timed``).  check_inputs: first run the opt-in check
+    of the device data (``kda_prefill_check``, which synchronises) and raise
+    ValueError if it fails.  Tensors the call allocates (o when None, the
+    workspace when None) come from the launch stream's memory pool.  Returns
+    o [T, H, d_v].
     """
     lib = load_library()
     _dev(q, "q")
@@ -246,8 +285,15 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
     for name, p in (("state_in", state_in), ("state_out", state_out)):
         _check_pool(p, name, num_slots, H, dk, dv, state_slot_stride, state_head_stride)
     _dev(slots, "slots", torch.int32, (N,) if slots is not None else None)
+    if check_inputs:
+        bad = check_prefill_inputs(g, cu_seqlens, slots, num_slots=num_slots, stream=stream)
+        if bad:
+            raise ValueError("prefill inputs break the preconditions of kda.h: "
+                             + "; ".join(m for b, m in CHECK_BITS.items() if bad & b))
+    s = _stream_obj(stream)
     if o is None:
-        o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
+        with torch.cuda.stream(s):   # owned by the launch stream's memory pool
+            o = torch.empty((T, H, dv), dtype=q.dtype, device=q.device)
     _dev(o, "o", q.dtype, (T, H, dv))
     conv = None
     if conv_weight is not None:
@@ -256,7 +302,11 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
                      _conv_mode(conv_activation) if conv is not None else 0)
     need = int(lib.kda_prefill_workspace_size(ctypes.byref(desc)))
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        # Allocated from the launch stream's pool: when it is freed on return
+        # the caching allocator hands its blocks out again only to work on
+        # that stream, which runs after this call's kernels.
+        with torch.cuda.stream(s):
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace", torch.uint8)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(state_in),
             _ptr(state_out), _ptr(o), _ptr(slots), ctypes.byref(desc), _ptr(workspace),
@@ -311,7 +361,8 @@ def decode_step(q, k, v, g, beta, state_pool, slots, o=None, scale=1.0, stream=N
     _check_pool(state_pool, "state_pool", num_slots, H, dk, dv, state_slot_stride, state_head_stride)
     _dev(slots, "slots", torch.int32, (N,))
     if o is None:
-        o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+        with torch.cuda.stream(_stream_obj(stream)):
+            o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
     _dev(o, "o", q.dtype, (N, H, dv))
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), _ptr(slots),
             _ptr(o), N, H, dk, dv, num_slots, io, float(scale), int(state_slot_stride),
@@ -347,7 +398,8 @@ def decode_tokens(q, k, v, g, beta, state_pool, slots, o=None, num_accepted=None
     if outputs:
         _dev(q, "q", k.dtype, (N, T, H, dk))
         if o is None:
-            o = torch.empty((N, T, H, dv), dtype=k.dtype, device=k.device)
+            with torch.cuda.stream(_stream_obj(stream)):
+                o = torch.empty((N, T, H, dv), dtype=k.dtype, device=k.device)
         _dev(o, "o", k.dtype, (N, T, H, dv))
     else:
         if q is not None:

@@ -33,33 +33,40 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
-_lib = None
+# The same source in fp32 working precision, for the noise-floor measurement
+# only (see kda_oracle.c, "Working precision").
+_LIB_PATH_F32 = os.path.join(_HERE, "libkda_oracle_f32.so")
+_libs = {}
 
 
 def build(force: bool = True) -> str:
-    """Compile the C oracle with gcc into ``oracle/libkda_oracle.so``."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
-                               _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB_PATH)
+    """Compile the C oracle with gcc into ``oracle/libkda_oracle.so`` (fp64)
+    and ``oracle/libkda_oracle_f32.so`` (the fp32 noise-floor build)."""
+    for path, extra in ((_LIB_PATH, []), (_LIB_PATH_F32, ["-DKDA_REAL=float"])):
+        if force or not os.path.exists(path):
+            tmp = path + ".tmp%d" % os.getpid()
+            subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
+                                   *extra, _SRC, "-o", tmp, "-lm"])
+            os.replace(tmp, path)
     return _LIB_PATH
 
 
-def _load():
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+def _load(precision="f64"):
+    if precision not in ("f64", "f32"):
+        raise ValueError("precision must be 'f64' or 'f32'")
+    if precision not in _libs:
+        path = _LIB_PATH if precision == "f64" else _LIB_PATH_F32
+        if not os.path.exists(path):
             build(force=False)
-        lib = ctypes.CDLL(_LIB_PATH)
+        lib = ctypes.CDLL(path)
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(ctypes.c_int32)
         lib.kda_oracle_prefill.restype = ctypes.c_int
         lib.kda_oracle_prefill.argtypes = [dp, dp, dp, dp, dp, ip, ctypes.c_int32, ctypes.c_int32,
                                            ctypes.c_int32, ctypes.c_int32, dp, dp, dp,
                                            ctypes.c_double, ctypes.c_int32]
-        _lib = lib
-    return _lib
+        _libs[precision] = lib
+    return _libs[precision]
 
 
 MAX_THREADS = 16   # the host CPU share one GPU job may use
@@ -81,8 +88,10 @@ def _ptr(a, ctype):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
 
-def recurrence(q, k, v, g, beta, cu_seqlens, s0=None, scale=1.0, threads=None):
-    """Run the token-by-token fp64 recurrence.
+def recurrence(q, k, v, g, beta, cu_seqlens, s0=None, scale=1.0, threads=None,
+               precision="f64"):
+    """Run the token-by-token fp64 recurrence (precision="f32": the same loop
+    in fp32, only for noise-floor measurements).
 
     q, k, g: [T, H, d_k]; v: [T, H, d_v]; beta: [T, H]; cu_seqlens: [N+1];
     s0: per-sequence initial states [N, H, d_v, d_k] or None (zeros).
@@ -107,7 +116,7 @@ def recurrence(q, k, v, g, beta, cu_seqlens, s0=None, scale=1.0, threads=None):
         return o, s_out
     nt = threads if threads is not None else default_threads()
     dp = ctypes.c_double
-    rc = _load().kda_oracle_prefill(
+    rc = _load(precision).kda_oracle_prefill(
         _ptr(q, dp), _ptr(k, dp), _ptr(v, dp), _ptr(g, dp), _ptr(beta, dp),
         _ptr(cu, ctypes.c_int32), N, H, dk, dv,
         _ptr(s0, dp) if s0 is not None else None, _ptr(s_out, dp), _ptr(o, dp),

@@ -87,16 +87,42 @@ def oracle_prefill(case, pool=None, o_init=None, num_slots=None):
 
 
 def per_sequence_errors(case, o_gpu, o_ref, pool_gpu=None, pool_ref=None, live=None):
-    """Max over sequences of the normwise error of o, and of the final state."""
+    """Max over (sequence, head) pairs of the normwise error of o, and of the
+    final state: each head is normalised by its own largest reference value,
+    so a head with small outputs is held to the same relative bar as the
+    largest one."""
     cu = case.cu_seqlens
     eo, es = 0.0, 0.0
     for n in range(case.N):
         if live is not None and not live[n]:
             continue
         a, b = int(cu[n]), int(cu[n + 1])
-        if b > a:
-            eo = max(eo, rel_err(o_gpu[a:b], o_ref[a:b]))
-        if pool_gpu is not None:
-            s = int(case.slots[n]) if case.slots is not None else n
-            es = max(es, rel_err(pool_gpu[s], pool_ref[s]))
+        s = int(case.slots[n]) if case.slots is not None else n
+        for h in range(case.H):
+            if b > a:
+                eo = max(eo, rel_err(o_gpu[a:b, h], o_ref[a:b, h]))
+            if pool_gpu is not None:
+                es = max(es, rel_err(pool_gpu[s, h], pool_ref[s, h]))
     return eo, es
+
+
+def per_head_error(x, ref):
+    """Max over heads of the normwise error of outputs [..., H, d]: each head's
+    block (all leading rows, all d columns) is normalised by its own largest
+    reference value."""
+    x = np.asarray(x)
+    ref = np.asarray(ref)
+    return max(rel_err(x[..., h, :], ref[..., h, :]) for h in range(x.shape[-2]))
+
+
+def block_error(x, ref, block_dims):
+    """Max of the normwise error over blocks made of the last `block_dims`
+    axes: block_dims = 2 gives one error per (slot, head) state [d_v, d_k],
+    block_dims = 1 one per (token, head) output row."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if x.size == 0:
+        return 0.0
+    n = int(np.prod(x.shape[-block_dims:]))
+    xb, rb = x.reshape(-1, n), ref.reshape(-1, n)
+    return max(rel_err(xb[i], rb[i]) for i in range(xb.shape[0]))

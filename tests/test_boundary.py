@@ -47,7 +47,7 @@ def test_header_declares_expected_entry_points():
     for n in ("kda_chunk_prefill", "kda_decode_step", "kda_prefill_workspace_size",
               "kda_status_string", "kda_version", "kda_chunk_prefill_timed",
               "kda_decode_step_lines", "kda_decode_tokens", "kda_chunk_prefill_conv",
-              "kda_decode_step_conv"):
+              "kda_decode_step_conv", "kda_prefill_check"):
         assert n in names
 
 
@@ -57,7 +57,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 103
+    assert lib.kda_version() == 104
     for code in range(8):
         s = lib.kda_status_string(code).decode()
         assert s and s != "unknown status"
@@ -274,3 +274,20 @@ def test_conv_extent_matches_the_layouts():
     # a window right after each head's 64 KiB state in 884,736-byte pages
     ss, hs = 2 * (884736 // 4), 2 * (67840 // 4)
     assert K.conv_extent(4, 12, d, d, (ss, hs, C, d)) == 3 * ss + 11 * hs + 3 * C
+
+
+def test_prefill_check_rejects_before_launch(lib):
+    """kda_prefill_check validates its host arguments before anything runs."""
+    fake = ctypes.c_void_p(0x10000)
+    flags = ctypes.c_void_p(0x20000)
+    d = _desc()
+    assert lib.kda_prefill_check(None, fake, None, ctypes.byref(d), flags, None) == 1   # g NULL, T > 0
+    assert lib.kda_prefill_check(fake, None, None, ctypes.byref(d), flags, None) == 1   # cu NULL
+    assert lib.kda_prefill_check(fake, fake, None, ctypes.byref(d), None, None) == 1    # flags NULL
+    assert lib.kda_prefill_check(fake, fake, None, None, flags, None) == 1              # desc NULL
+    assert lib.kda_prefill_check(ctypes.c_void_p(0x10004), fake, None, ctypes.byref(d), flags,
+                                 None) == 4                                             # misaligned
+    bad = _desc(dk=96)
+    assert lib.kda_prefill_check(fake, fake, None, ctypes.byref(bad), flags, None) == 6
+    bad = _desc(N=0)
+    assert lib.kda_prefill_check(fake, fake, None, ctypes.byref(bad), flags, None) == 2

@@ -14,7 +14,8 @@ import torch
 
 from linear_attention_prefill_amd import workloads as W
 from oracle import oracle
-from kda_testlib import TOL, announce, dev, per_sequence_errors, rel_err, torch_dtype
+from kda_testlib import (TOL, announce, block_error, dev, per_head_error, per_sequence_errors,
+                         rel_err, torch_dtype)
 import linear_attention_prefill_amd as lap
 
 pytestmark = [pytest.mark.gpu,
@@ -126,11 +127,11 @@ def test_decode_conv_parity_and_prefill_continuity(dk, dv, io, act):
         outs.append(o.float().cpu().numpy())
     for n in range(3):
         a = 41 * n
-        assert rel_err(o_p[P * n:P * n + P], o_r[a:a + P]) <= TOL[io]
+        assert per_head_error(o_p[P * n:P * n + P], o_r[a:a + P]) <= TOL[io]
         for j, t in enumerate(range(P, 41)):
-            assert rel_err(outs[j][n], o_r[a + t]) <= TOL[io]
+            assert block_error(outs[j][n], o_r[a + t], 1) <= TOL[io]
         s = slots[n]
-        assert rel_err(pool_d.cpu().numpy()[s], pool_r[s]) <= TOL[io]
+        assert block_error(pool_d.cpu().numpy()[s], pool_r[s], 2) <= TOL[io]
     np.testing.assert_array_equal(win_d.float().cpu().numpy(), win_r.astype(np.float32))
 
 
@@ -155,9 +156,9 @@ def test_decode_conv_full_size_with_padding():
                                                  o_init=np.full((N, H, d), 3.0))
     o_g, pool_g = o.float().cpu().numpy(), pool.cpu().numpy()
     live = slots >= 0
-    assert rel_err(o_g[live], o_r[live]) <= TOL["bf16"]
+    assert block_error(o_g[live], o_r[live], 1) <= TOL["bf16"]
     assert np.all(o_g[~live] == 3.0)
-    assert rel_err(pool_g, pool_r) <= TOL["bf16"]
+    assert block_error(pool_g, pool_r, 2) <= TOL["bf16"]
     np.testing.assert_array_equal(win_d.float().cpu().numpy(), win_r.astype(np.float32))
 
 
@@ -209,8 +210,8 @@ def test_conv_window_inside_hybrid_page_lines():
                                                     dc.slots, weight, win_r, activation="silu")
     out = buf.cpu().numpy()
     ob = out.view(np.uint16)
-    assert rel_err(o.float().cpu().numpy(), o_r) <= TOL["bf16"]
-    assert rel_err(od.float().cpu().numpy(), od_r) <= TOL["bf16"]
+    assert per_head_error(o.float().cpu().numpy(), o_r) <= TOL["bf16"]
+    assert block_error(od.float().cpu().numpy(), od_r, 1) <= TOL["bf16"]
     wr = (torch.from_numpy(win_r2.astype(np.float32)).to(torch.bfloat16).view(torch.int16)
           .numpy().view(np.uint16))
     for s in range(S):
@@ -219,3 +220,38 @@ def test_conv_window_inside_hybrid_page_lines():
             assert rel_err(out[a:a + d * d].reshape(d, d), pool_r2[s, h]) <= TOL["bf16"]
             b = 2 * (a + d * d)
             np.testing.assert_array_equal(ob[b:b + 3 * C], wr[s, h].reshape(-1))
+
+
+@pytest.mark.parametrize("workload", ["single", "packed"])
+def test_prefill_conv_full_size(workload):
+    """The conv front end at the full prefill shapes that bench.py times with
+    the conv (8192 rows, H = 32, d = 128, bf16, SiLU): one sequence from a
+    one-slot window pool, and the 16 packed sequences with their 64-slot state
+    and window pools.  Windows bit for bit, o and states per (sequence, head)
+    against the oracle."""
+    c = W.single_seq_prefill() if workload == "single" else W.packed_varlen_prefill()
+    S = 1 if c.state_pool is None else c.state_pool.shape[0]
+    weight, window = W.draw_conv(11, S, c.H, c.d_k, c.d_v, c.io_dtype)
+    dt = torch.bfloat16
+    pool = (np.zeros((1, c.H, c.d_v, c.d_k), dtype=np.float32) if c.state_pool is None
+            else c.state_pool)
+    slots = np.zeros(1, dtype=np.int32) if c.slots is None else c.slots
+    q, k, v = dev(c.q, dt), dev(c.k, dt), dev(c.v, dt)
+    o = torch.zeros((c.T, c.H, c.d_v), dtype=dt, device="cuda")
+    p = dev(pool)
+    win_d = dev(window, dt)
+    announce("prefill conv full size %s" % c.name)
+    lap.chunk_prefill(q, k, v, dev(c.g), dev(c.beta), dev(c.cu_seqlens), state_in=p,
+                      state_out=p, o=o, slots=dev(slots), num_slots=S, conv_weight=dev(weight),
+                      conv_window=win_d, conv_activation="silu")
+    torch.cuda.synchronize()
+    o_g, pool_g, win_g = o.float().cpu().numpy(), p.cpu().numpy(), win_d.float().cpu().numpy()
+    o_r, pool_r, _, win_r = oracle.chunk_prefill_conv(c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens,
+                                                      weight, window, pool, slots,
+                                                      activation="silu")
+    ref_case = W.Case(c.name, c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens, c.io_dtype,
+                      state_pool=pool, slots=slots)
+    eo, es = per_sequence_errors(ref_case, o_g, o_r, pool_g, pool_r)
+    announce("  max relative error per (sequence, head): o %.3e  state %.3e" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
+    np.testing.assert_array_equal(win_g, win_r.astype(np.float32))

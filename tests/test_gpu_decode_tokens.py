@@ -13,7 +13,7 @@ import torch
 
 from linear_attention_prefill_amd import workloads as W
 from oracle import oracle
-from kda_testlib import TOL, announce, dev, rel_err, torch_dtype
+from kda_testlib import TOL, announce, block_error, dev, rel_err, torch_dtype
 import linear_attention_prefill_amd as lap
 
 pytestmark = [pytest.mark.gpu,
@@ -95,8 +95,8 @@ def test_tokens_bitwise_against_single_steps(dk, dv, io, T):
     for n in range(N):
         s = int(c.slots[n])
         if 0 <= s < S:
-            assert rel_err(o_f[n], o_r[n]) <= TOL[io]
-            assert rel_err(pool_f[s], pool_r[s]) <= TOL[io]
+            assert block_error(o_f[n], o_r[n], 1) <= TOL[io]
+            assert block_error(pool_f[s], pool_r[s], 2) <= TOL[io]
 
 
 def test_tokens_full_size_with_acceptance():
@@ -119,8 +119,8 @@ def test_tokens_full_size_with_acceptance():
         s = int(c.slots[n])
         if s < 0:
             continue
-        worst_o = max(worst_o, rel_err(o_g[n], o_r[n]))
-        worst_s = max(worst_s, rel_err(pool_g[s], pool_r[s]))
+        worst_o = max(worst_o, block_error(o_g[n], o_r[n], 1))
+        worst_s = max(worst_s, block_error(pool_g[s], pool_r[s], 2))
     announce("  o err %.3e  state err %.3e" % (worst_o, worst_s))
     assert worst_o <= TOL["bf16"] and worst_s <= TOL["bf16"]
 
@@ -156,4 +156,4 @@ def test_tokens_with_line_addressed_pool():
     np.testing.assert_array_equal(out[mask], np.full(mask.sum(), fill, dtype=np.float32))
     for n in range(N):
         if c.slots[n] >= 0:
-            assert rel_err(o_g[n], o_r[n]) <= TOL["bf16"]
+            assert block_error(o_g[n], o_r[n], 1) <= TOL["bf16"]

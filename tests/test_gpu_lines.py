@@ -18,7 +18,8 @@ import torch
 
 from linear_attention_prefill_amd import workloads as W
 from oracle import oracle
-from kda_testlib import TOL, announce, dev, oracle_prefill, per_sequence_errors, rel_err, torch_dtype
+from kda_testlib import (TOL, announce, block_error, dev, oracle_prefill, per_sequence_errors,
+                         rel_err, torch_dtype)
 import linear_attention_prefill_amd as lap
 
 pytestmark = [pytest.mark.gpu,
@@ -128,8 +129,8 @@ def test_decode_with_line_addressed_pool(dk, dv, io):
     for n in range(c.N):
         s = int(c.slots[n])
         if 0 <= s < S:
-            assert rel_err(o_g[n], o_r[n]) <= TOL[io]
-            assert rel_err(pool_g[s], pool_r[s]) <= TOL[io]
+            assert block_error(o_g[n], o_r[n], 1) <= TOL[io]
+            assert block_error(pool_g[s], pool_r[s], 2) <= TOL[io]
         else:
             assert np.all(o_g[n] == 5.0)
     gaps = gap_mask(S, H, dk, dv, ss, hs)
@@ -175,7 +176,7 @@ def test_hybrid_page_geometry():
     flat = pool.cpu().numpy()
     od_r, pool_r2 = oracle.decode_step(dc.q, dc.k, dc.v, dc.g, dc.beta, pool_r, dc.slots,
                                        scale=dc.scale)
-    assert rel_err(od.float().cpu().numpy(), od_r) <= TOL["bf16"]
-    assert rel_err(unpack(flat, S, H, d, d, ss, hs), pool_r2) <= TOL["bf16"]
+    assert block_error(od.float().cpu().numpy(), od_r, 1) <= TOL["bf16"]
+    assert block_error(unpack(flat, S, H, d, d, ss, hs), pool_r2, 2) <= TOL["bf16"]
     gaps = gap_mask(S, H, d, d, ss, hs)
     np.testing.assert_array_equal(flat[gaps], np.full(gaps.sum(), fill, dtype=np.float32))

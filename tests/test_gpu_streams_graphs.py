@@ -123,3 +123,34 @@ def test_decode_and_conv_decode_graph_replays_match_eager():
         assert torch.equal(pool_g, pool_e), rep
         assert torch.equal(win_g, win_e), rep
         _ = (pool_e * 0.5).sum().item()
+
+
+def test_explicit_stream_argument_owns_its_allocations():
+    """stream= names a stream other than the current one, with the default
+    stream current throughout.  The workspace and o that the binding
+    allocates belong to that stream's memory pool, so memory the default
+    stream allocates and fills at once, while the call's kernels still run,
+    cannot be the call's workspace: results match an eager call bit for
+    bit."""
+    c = W.random_case(321, [8192], H=8, d_k=128, d_v=128, io_dtype="bf16", num_slots=2)
+    dt = torch.bfloat16
+    a = _prefill_args(c, dt)
+    announce("prefill reference on the current stream")
+    p_ref = dev(c.state_pool)
+    o_ref = lap.chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu_seqlens"],
+                              state_in=p_ref, state_out=p_ref, slots=a["slots"])
+    torch.cuda.synchronize()
+    ws_bytes = lap.prefill_workspace_size(c.T, c.N, c.H, c.d_k, c.d_v, dt)
+    side = torch.cuda.Stream()
+    pool = dev(c.state_pool)
+    torch.cuda.synchronize()
+    announce("prefill with stream=side, default stream allocating meanwhile")
+    o = lap.chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu_seqlens"],
+                          state_in=pool, state_out=pool, slots=a["slots"], stream=side)
+    junk = [torch.full((ws_bytes // 4 + 1024,), 1e30, dtype=torch.float32, device="cuda")
+            for _ in range(2)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    assert torch.equal(o, o_ref)
+    assert torch.equal(pool, p_ref)
