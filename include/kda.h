@@ -71,7 +71,8 @@ typedef enum {
     KDA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
     KDA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
     KDA_ERR_UNSUPPORTED = 6, /* d_k or d_v not 64 or 128 */
-    KDA_ERR_HIP = 7          /* a kernel launch failed */
+    KDA_ERR_HIP = 7,         /* a kernel launch failed */
+    KDA_ERR_TOO_LARGE = 8    /* the call needs more than the static scratch holds */
 } kda_status_t;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
@@ -321,6 +322,32 @@ kda_status_t kda_decode_tokens(const void *q, const void *k, const void *v,
                                int32_t io_dtype, float scale, int32_t commit,
                                int64_t state_slot_stride, int64_t state_head_stride,
                                void *stream);
+
+/*
+ * kda_chunk_prefill for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments without the workspace; same kernels and, bit
+ * for bit, the same results.  The workspace is a static device array of
+ * KDA_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs this
+ * call on until the process ends: enough for one packed 8192-row chunk of up
+ * to 16 sequences at H = 32, d_k = d_v = 128 in bf16 (317.25 MiB of
+ * records).  A call whose kda_prefill_workspace_size exceeds it returns
+ * KDA_ERR_TOO_LARGE before anything runs.  The first call on a device looks
+ * up that device's copy of the array (hipGetSymbolAddress); no call
+ * allocates.  Every call on one GPU shares its array: calls that overlap on
+ * one GPU (different streams, or host threads, without ordering between
+ * them) race and give unspecified results.  Nothing in the array needs
+ * clearing: a call reads only bytes it wrote earlier in the same call.
+ * No conv mode (the desc's conv_mode must be KDA_CONV_NONE).  Errors as for
+ * kda_chunk_prefill, plus KDA_ERR_TOO_LARGE.
+ */
+#define KDA_STATIC_SCRATCH_BYTES ((size_t)320 << 20)
+kda_status_t kda_chunk_prefill_static(const void *q, const void *k, const void *v,
+                                      const float *g, const float *beta,
+                                      const int32_t *cu_seqlens,
+                                      const float *state_in, float *state_out,
+                                      void *o, const int32_t *slots,
+                                      const kda_prefill_desc_t *desc, void *stream);
 
 /*
  * Opt-in check of the device-side preconditions that kda_chunk_prefill

@@ -3,6 +3,6 @@
 The computation runs in hand-written HIP kernels for gfx950 behind the C ABI
 of ``libkda.so`` (``include/kda.h``); ``kda`` is its thin binding.
 """
-from .kda import (KdaError, check_prefill_inputs, chunk_prefill, conv_extent,  # noqa: F401
-                  decode_step, decode_tokens, line_extent, load_library,
-                  prefill_workspace_size)
+from .kda import (KdaError, check_prefill_inputs, chunk_prefill,  # noqa: F401
+                  chunk_prefill_no_alloc, conv_extent, decode_step, decode_tokens, line_extent,
+                  load_library, prefill_workspace_size)

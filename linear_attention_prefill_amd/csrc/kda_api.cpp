@@ -145,7 +145,8 @@ kda_status_t prefill_impl(const void *q, const void *k, const void *v, const flo
                           const float *beta, const int32_t *cu_seqlens, const float *state_in,
                           float *state_out, void *o, const int32_t *slots,
                           const kda_prefill_desc_t *desc, const kda_conv_t *conv, bool with_conv,
-                          void *workspace, size_t ws_bytes, void *stream, void *const *events) {
+                          void *workspace, size_t ws_bytes, void *stream, void *const *events,
+                          bool static_ws = false) {
     const kda_status_t st = check_desc(desc);
     if (st != KDA_OK) return st;
     const kda_prefill_desc_t d = *desc;
@@ -161,7 +162,8 @@ kda_status_t prefill_impl(const void *q, const void *k, const void *v, const flo
     const size_t need = rec_bytes + (with_conv ? kda::conv_workspace_bytes(
                                                      d.total_rows, d.num_heads, d.d_k, d.d_v, bf)
                                                : 0);
-    if (need > 0 && !workspace) return KDA_ERR_NULL;
+    if (static_ws && need > KDA_STATIC_SCRATCH_BYTES) return KDA_ERR_TOO_LARGE;
+    if (need > 0 && !workspace && !static_ws) return KDA_ERR_NULL;
     const void *ptrs[] = {q, k, v, g, beta, cu_seqlens, state_in, state_out, o, slots, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p)) return KDA_ERR_ALIGN;
@@ -171,12 +173,14 @@ kda_status_t prefill_impl(const void *q, const void *k, const void *v, const flo
         if (cs != KDA_OK) return cs;
         if (((long long)d.total_rows / 64 + 1) * d.num_heads > INT_MAX) return KDA_ERR_SHAPE;
     }
-    if (ws_bytes < need) return KDA_ERR_WORKSPACE;
+    if (!static_ws && ws_bytes < need) return KDA_ERR_WORKSPACE;
     int64_t ss = 0, hs = 0;
     if (!resolve_strides(d.state_slot_stride, d.state_head_stride, d.num_heads, d.d_k, d.d_v, &ss, &hs))
         return KDA_ERR_SHAPE;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (static_ws && need > 0 && kda::static_scratch(s, &workspace) != hipSuccess)
+        return KDA_ERR_HIP;
     (void)hipGetLastError();       // an earlier call's error is not this call's
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens;
@@ -277,6 +281,15 @@ kda_status_t kda_chunk_prefill_conv(const void *q, const void *k, const void *v,
                                     void *stream, void *const *events) {
     return prefill_impl(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, slots, desc, conv,
                         true, workspace, ws_bytes, stream, events);
+}
+
+kda_status_t kda_chunk_prefill_static(const void *q, const void *k, const void *v,
+                                      const float *g, const float *beta,
+                                      const int32_t *cu_seqlens, const float *state_in,
+                                      float *state_out, void *o, const int32_t *slots,
+                                      const kda_prefill_desc_t *desc, void *stream) {
+    return prefill_impl(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, slots, desc, nullptr,
+                        false, nullptr, 0, stream, nullptr, true);
 }
 
 kda_status_t kda_chunk_prefill(const void *q, const void *k, const void *v, const float *g,
@@ -383,10 +396,13 @@ const char *kda_status_string(kda_status_t status) {
         case KDA_ERR_WORKSPACE: return "workspace too small";
         case KDA_ERR_UNSUPPORTED: return "d_k and d_v must be 64 or 128";
         case KDA_ERR_HIP: return "a HIP kernel launch failed";
+        case KDA_ERR_TOO_LARGE:
+            return "the call needs more workspace than the static scratch holds "
+                   "(KDA_STATIC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }
 
-int32_t kda_version(void) { return 104; }
+int32_t kda_version(void) { return 105; }
 
 }  // extern "C"

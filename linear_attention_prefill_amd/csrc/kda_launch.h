@@ -85,6 +85,10 @@ hipError_t launch_prefill_check(const float *g, const int32_t *cu, const int32_t
                                 int N, int H, int dk, int num_slots, int32_t *flags,
                                 hipStream_t stream);
 
+// Device address of the static scratch that backs kda_chunk_prefill_static
+// on the device `stream` runs on (looked up on the first call per device).
+hipError_t static_scratch(hipStream_t stream, void **ptr);
+
 size_t prefill_workspace_bytes(int T, int N, int H, int dk, int dv, bool bf16);
 
 // Workspace bytes of the convolved q, k, v (placed after the records).

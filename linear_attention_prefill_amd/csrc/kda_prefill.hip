@@ -45,8 +45,10 @@
 // the record bytes each CU takes in, which a workgroup takes in once for its
 // NS slices: each call uses the largest NS of 1, 2 or 4 (bf16 for NS > 1)
 // that still leaves every CU a workgroup.
+#include <mutex>
 #include <type_traits>
 
+#include "kda.h"
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -1042,6 +1044,47 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
         if (slices >= 2LL * a.num_cus) return scan(std::integral_constant<int, 2>{});
     }
     return scan(std::integral_constant<int, 1>{});
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch of the allocation-free prefill
+// ---------------------------------------------------------------------------
+
+// Every GPU the library runs kda_chunk_prefill_static on holds its own copy
+// of this array until the process ends.  In host code its name is only a
+// stand-in for the symbol: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, kept per device below.
+static __device__ __align__(256) unsigned char scratch[KDA_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+hipError_t static_scratch(hipStream_t stream, void **ptr) {
+    int dev = 0;
+    if (!stream || hipStreamGetDevice(stream, &dev) != hipSuccess) {
+        const hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+    }
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        // the symbol's address on `dev`, looked up with `dev` current
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 size_t prefill_workspace_bytes(int T, int N, int H, int dk, int dv, bool bf16) {

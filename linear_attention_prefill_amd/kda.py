@@ -20,7 +20,11 @@ KDA_F32 = 0
 KDA_BF16 = 1
 
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
-          4: "KDA_ERR_ALIGN", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_HIP"}
+          4: "KDA_ERR_ALIGN", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_HIP",
+          8: "KDA_ERR_TOO_LARGE"}
+
+# Bytes of the static scratch behind kda_chunk_prefill_static (kda.h).
+STATIC_SCRATCH_BYTES = 320 << 20
 
 
 class PrefillDesc(ctypes.Structure):
@@ -88,6 +92,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_decode_tokens.restype = ctypes.c_int
     lib.kda_decode_tokens.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                       i32, i32, i32, i32, i32, i32, i32, f32, i32, i64, i64, vp]
+    lib.kda_chunk_prefill_static.restype = ctypes.c_int
+    lib.kda_chunk_prefill_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             ctypes.POINTER(PrefillDesc), vp]
     lib.kda_prefill_check.restype = ctypes.c_int
     lib.kda_prefill_check.argtypes = [vp, vp, vp, ctypes.POINTER(PrefillDesc), vp, vp]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -322,6 +329,46 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
         _check(lib.kda_chunk_prefill(*args))
     else:
         _check(lib.kda_chunk_prefill_timed(*args, handles))
+    return o
+
+
+def chunk_prefill_no_alloc(q, k, v, g, beta, cu_seqlens, o, state_in=None, state_out=None,
+                           slots=None, num_slots=None, scale=1.0, stream=None,
+                           state_slot_stride=0, state_head_stride=0):
+    """chunk_prefill through ``kda_chunk_prefill_static``, for callers that
+    cannot allocate: o is required, no workspace is passed and nothing is
+    allocated, here or in the library (its workspace is a static device array
+    of STATIC_SCRATCH_BYTES per GPU).  Calls that overlap on one GPU race.
+    Same arguments and results as chunk_prefill otherwise; no conv front end.
+    Returns o."""
+    lib = load_library()
+    _dev(q, "q")
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    io = _io_code(q.dtype)
+    _dev(k, "k", q.dtype, (T, H, dk))
+    _dev(v, "v", q.dtype, (T, H, dv))
+    _dev(g, "g", torch.float32, (T, H, dk))
+    _dev(beta, "beta", torch.float32, (T, H))
+    _dev(cu_seqlens, "cu_seqlens", torch.int32)
+    N = cu_seqlens.shape[0] - 1
+    pools = [p for p in (state_in, state_out) if p is not None]
+    lines = bool(state_slot_stride or state_head_stride)
+    if num_slots is None:
+        if lines and pools:
+            raise ValueError("num_slots is required for pools addressed by lines")
+        num_slots = pools[0].shape[0] if pools else N
+    for name, p in (("state_in", state_in), ("state_out", state_out)):
+        _check_pool(p, name, num_slots, H, dk, dv, state_slot_stride, state_head_stride)
+    _dev(slots, "slots", torch.int32, (N,) if slots is not None else None)
+    if o is None:
+        raise ValueError("o is required: this entry point allocates nothing")
+    _dev(o, "o", q.dtype, (T, H, dv))
+    desc = make_desc(T, N, H, dk, dv, num_slots, io, scale, state_slot_stride, state_head_stride)
+    _check(lib.kda_chunk_prefill_static(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                        _ptr(cu_seqlens), _ptr(state_in), _ptr(state_out),
+                                        _ptr(o), _ptr(slots), ctypes.byref(desc),
+                                        _stream(stream)))
     return o
 
 

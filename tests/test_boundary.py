@@ -47,7 +47,7 @@ def test_header_declares_expected_entry_points():
     for n in ("kda_chunk_prefill", "kda_decode_step", "kda_prefill_workspace_size",
               "kda_status_string", "kda_version", "kda_chunk_prefill_timed",
               "kda_decode_step_lines", "kda_decode_tokens", "kda_chunk_prefill_conv",
-              "kda_decode_step_conv", "kda_prefill_check"):
+              "kda_decode_step_conv", "kda_prefill_check", "kda_chunk_prefill_static"):
         assert n in names
 
 
@@ -57,8 +57,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 104
-    for code in range(8):
+    assert lib.kda_version() == 105
+    for code in range(9):
         s = lib.kda_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.kda_status_string(99).decode() == "unknown status"
@@ -291,3 +291,20 @@ def test_prefill_check_rejects_before_launch(lib):
     assert lib.kda_prefill_check(fake, fake, None, ctypes.byref(bad), flags, None) == 6
     bad = _desc(N=0)
     assert lib.kda_prefill_check(fake, fake, None, ctypes.byref(bad), flags, None) == 2
+
+
+def test_static_prefill_rejects_before_launch(lib):
+    """kda_chunk_prefill_static checks its arguments, and that the call fits
+    the static scratch, before it looks anything up on a device."""
+    fake = ctypes.c_void_p(0x10000)
+    args = [fake] * 6 + [None, None, fake, None]
+    big = _desc(T=16384, N=1, H=32, slots=1)
+    assert lib.kda_chunk_prefill_static(*args, ctypes.byref(big), None) == 8
+    d = _desc()
+    bad = list(args)
+    bad[0] = None
+    assert lib.kda_chunk_prefill_static(*bad, ctypes.byref(d), None) == 1
+    assert lib.kda_chunk_prefill_static(*args, None, None) == 1
+    conv = _desc(conv=1)
+    assert lib.kda_chunk_prefill_static(*args, ctypes.byref(conv), None) == 1
+    assert lib.kda_prefill_workspace_size(ctypes.byref(d)) <= K.STATIC_SCRATCH_BYTES
