@@ -17,14 +17,15 @@ have settled; then exactly K steps are timed between two events.
 Prints ONE JSON line.  Besides the throughput it reports:
   roofline      the method's algorithmic bytes per step (q, k, v, g, beta
                 read, o written, states read and written) over the dominant
-                kernel's average duration, against 8 TB/s; the durations come
+                kernel's time per step (the sum over its launches when a call
+                runs as several windows of chunks), against 8 TB/s; the durations come
                 from HIP events recorded on the launch stream before, between
                 and after the kernels in a second pass of K steps (those
                 events cost a few microseconds a step, so the timed steps run
                 without them); `traffic` is that kernel's HBM bytes from the
-                rocprofv3 FETCH_SIZE / WRITE_SIZE counters (profiles/traffic.json,
-                reported while the kernel sources match), `traffic_ratio` their
-                ratio to the algorithmic bytes;
+                rocprofv3 FETCH_SIZE / WRITE_SIZE counters per step
+                (profiles/traffic.json, reported while the kernel sources
+                match), `traffic_ratio` their ratio to the algorithmic bytes;
   path          the whole step against the HBM roof and the bf16 MFMA roof;
   cpu_baseline  the fp64 oracle timed on the host cores on the same inputs;
   kernels       both kernels' average durations;
@@ -200,24 +201,26 @@ def time_prefill(case, steps, warmup, copies, torch, lap, conv=None):
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     # per-kernel durations: the same steps again with events recorded on the
-    # launch stream before, between and after the two kernels (events between
-    # kernels cost a few microseconds a step, so they stay out of the timed
-    # steps above)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for trio in evs:          # torch creates the underlying hipEvents on first record
-        for e in trio:
+    # launch stream before the first kernel and after every kernel (intra and
+    # scan of each window in turn; events between kernels cost a few
+    # microseconds a step, so they stay out of the timed steps above)
+    nw = lap.prefill_windows(T, case.N, H, dk, dv, dt)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nw + 1)]
+           for _ in range(steps)]
+    for row in evs:           # torch creates the underlying hipEvents on first record
+        for e in row:
             e.record()
     torch.cuda.synchronize()
     for i in range(steps):
         call(i, evs[i])
     torch.cuda.synchronize()
-    intra = [e[0].elapsed_time(e[1]) for e in evs]
-    scan = [e[1].elapsed_time(e[2]) for e in evs]
+    intra = [sum(e[2 * w].elapsed_time(e[2 * w + 1]) for w in range(nw)) for e in evs]
+    scan = [sum(e[2 * w + 1].elapsed_time(e[2 * w + 2]) for w in range(nw)) for e in evs]
     return {
         "ms_per_step": total_ms / steps,
         "intra_ms": float(np.mean(intra)), "scan_ms": float(np.mean(scan)),
         "intra_ms_median": float(np.median(intra)), "scan_ms_median": float(np.median(scan)),
-        "state_in": state_in,
+        "state_in": state_in, "windows": nw,
     }
 
 
@@ -368,9 +371,10 @@ def cpu_baseline(case, seconds, s0=None, label=None):
 
 
 def stored_traffic(workload, kernel_name, src_hash):
-    """HBM bytes per launch of a kernel on a workload, from the FETCH_SIZE /
-    WRITE_SIZE counters stored in profiles/traffic.json, while the kernel
-    sources they were taken at match."""
+    """HBM bytes per step of a kernel on a workload (all its launches in the
+    step), from the FETCH_SIZE / WRITE_SIZE counters stored in
+    profiles/traffic.json, while the kernel sources they were taken at
+    match."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -378,8 +382,10 @@ def stored_traffic(workload, kernel_name, src_hash):
         return None
     if t.get("source_hash") != src_hash:
         return None
-    k = t.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel_name)
-    return None if k is None else k.get("bytes_per_launch")
+    w = t.get("workloads", {}).get(workload, {})
+    k = w.get("kernels", {}).get(kernel_name)
+    # counters are per dispatch; a step launches each kernel once per window
+    return None if k is None else k.get("bytes_per_launch") * w.get("windows_per_step", 1)
 
 
 def prefill_line(case, r, src_hash, conv=False):
@@ -403,6 +409,7 @@ def prefill_line(case, r, src_hash, conv=False):
     line = {
         "workload": case.name + ("+conv3_silu" if conv else ""),
         "value": T / step_s, "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
+        "windows": r.get("windows", 1),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "traffic_ratio": None if traffic is None else traffic / pb,

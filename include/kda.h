@@ -140,8 +140,18 @@ typedef struct {
     int64_t state_slot_stride;  /* fp32 elements between slots' lines; 0 = dense */
     int64_t state_head_stride;  /* fp32 elements between heads of a line; 0 = dense */
     int32_t conv_mode;   /* kda_conv_mode_t; not NONE only with kda_chunk_prefill_conv */
-    int32_t reserved;    /* 0 */
+    int32_t window_chunks;  /* chunk ids per window (kda_prefill_windows); 0 = the library's choice */
 } kda_prefill_desc_t;
+
+/*
+ * Number of windows of chunk ids a prefill call with `desc` runs as (0 if
+ * desc is invalid): each window is an intra-chunk kernel that writes the
+ * records of its chunks into the workspace and a state scan that consumes
+ * them, so the workspace holds one window's records (the prhub report on
+ * SGLang PR #32890, section "实现拆解", splits the prefill into the same two
+ * stages).
+ */
+int32_t kda_prefill_windows(const kda_prefill_desc_t *desc);
 
 /*
  * Bytes of device workspace kda_chunk_prefill needs for `desc` (0 if desc is
@@ -198,12 +208,15 @@ kda_status_t kda_chunk_prefill(const void *q, const void *k, const void *v,
                                void *stream);
 
 /*
- * kda_chunk_prefill with per-kernel timing: when `events` is not NULL it
- * points to three hipEvent_t that are recorded on `stream` before the
- * intra-chunk kernel, between it and the state scan, and after the scan, so
- * the caller can read each kernel's duration with hipEventElapsedTime.  The
- * events are created and owned by the caller.  Results and errors are those of
- * kda_chunk_prefill.
+ * kda_chunk_prefill with per-kernel timing.  A call runs as one or more
+ * windows of chunk ids (kda_prefill_windows), each an intra-chunk kernel and
+ * a state scan.  When `events` is not NULL it points to num_events hipEvent_t:
+ * events[0] is recorded on `stream` before the first kernel and events[i]
+ * after the i-th kernel launch, in launch order (intra of window 0, scan of
+ * window 0, intra of window 1, ...), as long as i < num_events; so 2 W + 1
+ * events time every kernel of a W-window call with hipEventElapsedTime.  The
+ * events are created and owned by the caller.  Results and errors are those
+ * of kda_chunk_prefill.
  */
 kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v,
                                      const float *g, const float *beta,
@@ -212,14 +225,14 @@ kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v
                                      void *o, const int32_t *slots,
                                      const kda_prefill_desc_t *desc,
                                      void *workspace, size_t ws_bytes,
-                                     void *stream, void *const *events);
+                                     void *stream, void *const *events, int32_t num_events);
 
 /*
  * kda_chunk_prefill_timed with the short conv front end (desc->conv_mode not
  * KDA_CONV_NONE; see "Short conv front end" above): q, k and v are the raw
  * inputs, conv->window is read and then rewritten, and the rest of the step
  * runs on the convolved values.  The conv runs first, then the window
- * update, then the two kernels that `events` (optional, as for
+ * update, then the kernels that `events` (optional, as for
  * kda_chunk_prefill_timed) bracket.  Errors as for kda_chunk_prefill, plus
  * KDA_ERR_NULL for a NULL conv, weight or window, and KDA_ERR_SHAPE for a
  * conv mode out of range or window strides that break the rules above.
@@ -233,7 +246,7 @@ kda_status_t kda_chunk_prefill_conv(const void *q, const void *k, const void *v,
                                     void *o, const int32_t *slots,
                                     const kda_prefill_desc_t *desc, const kda_conv_t *conv,
                                     void *workspace, size_t ws_bytes,
-                                    void *stream, void *const *events);
+                                    void *stream, void *const *events, int32_t num_events);
 
 /*
  * kda_decode_step with the state pool addressed by lines (see "State

@@ -26,6 +26,13 @@ CXX_SOURCES = ["kda_api.cpp"]
 
 # Packed fp32 VALU ops are disabled for all device code.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The state scan's matrix-core accumulators (the state and the output
+# tiles) are also scaled and converted on the VALU every step: with them in
+# accumulation registers the compiler moved them to and from vector registers
+# around every such use (2 to 5 accumulator moves per product).  Keeping the
+# products' C/D operands in vector registers removes those moves (16 packed
+# sequences: scan 108 -> 103 us).
+PER_SOURCE_FLAGS = {"kda_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",
           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
@@ -64,7 +71,7 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         cmd = [hipcc, "-x", "hip", "--offload-arch=" + ARCH, *COMMON, *DEVICE_FLAGS,
-               "-c", os.path.join(CSRC, src), "-o", obj]
+               *PER_SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if resource_usage:
             cmd.append("-Rpass-analysis=kernel-resource-usage")
         jobs.append((src, obj, cmd))

@@ -90,6 +90,7 @@ kda_status_t check_desc(const kda_prefill_desc_t *d) {
     if (d->total_rows < 0 || d->num_seqs < 1 || d->num_heads < 1 || d->num_slots < 0)
         return KDA_ERR_SHAPE;
     if (d->conv_mode < KDA_CONV_NONE || d->conv_mode > KDA_CONV_SILU) return KDA_ERR_SHAPE;
+    if (d->window_chunks < 0) return KDA_ERR_SHAPE;
     if (d->num_heads > 65535) return KDA_ERR_SHAPE;                       // grid.y of the window kernel
     const long long chunks = (long long)d->total_rows / 64 + d->num_seqs;
     if (chunks > INT_MAX) return KDA_ERR_SHAPE;
@@ -146,7 +147,7 @@ kda_status_t prefill_impl(const void *q, const void *k, const void *v, const flo
                           float *state_out, void *o, const int32_t *slots,
                           const kda_prefill_desc_t *desc, const kda_conv_t *conv, bool with_conv,
                           void *workspace, size_t ws_bytes, void *stream, void *const *events,
-                          bool static_ws = false) {
+                          int32_t num_events, bool static_ws = false) {
     const kda_status_t st = check_desc(desc);
     if (st != KDA_OK) return st;
     const kda_prefill_desc_t d = *desc;
@@ -158,7 +159,7 @@ kda_status_t prefill_impl(const void *q, const void *k, const void *v, const flo
     if (d.total_rows > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_NULL;
     const bool bf = d.io_dtype == KDA_BF16;
     const size_t rec_bytes = kda::prefill_workspace_bytes(d.total_rows, d.num_seqs, d.num_heads,
-                                                          d.d_k, d.d_v, bf);
+                                                          d.d_k, d.d_v, bf, d.window_chunks);
     const size_t need = rec_bytes + (with_conv ? kda::conv_workspace_bytes(
                                                      d.total_rows, d.num_heads, d.d_k, d.d_v, bf)
                                                : 0);
@@ -203,8 +204,10 @@ kda_status_t prefill_impl(const void *q, const void *k, const void *v, const flo
     a.scale = d.scale;
     a.slot_stride = ss;
     a.head_stride = hs;
-    for (int i = 0; i < 3; ++i) a.events[i] = events ? static_cast<hipEvent_t>(events[i]) : nullptr;
+    a.events = reinterpret_cast<const hipEvent_t *>(events);
+    a.num_events = events ? num_events : 0;
     a.num_cus = device_cus(s);
+    a.window_chunks = d.window_chunks;
     const hipError_t e = bf ? dispatch_prefill<bf16>(a, d.d_k, d.d_v, s)
                             : dispatch_prefill<float>(a, d.d_k, d.d_v, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -253,11 +256,17 @@ kda_status_t decode_impl(const void *q, const void *k, const void *v, const floa
 
 extern "C" {
 
+int32_t kda_prefill_windows(const kda_prefill_desc_t *desc) {
+    if (check_desc(desc) != KDA_OK) return 0;
+    return kda::prefill_plan(desc->total_rows, desc->num_seqs, desc->num_heads, desc->d_k,
+                             desc->d_v, desc->io_dtype == KDA_BF16, desc->window_chunks).windows;
+}
+
 size_t kda_prefill_workspace_size(const kda_prefill_desc_t *desc) {
     if (check_desc(desc) != KDA_OK) return 0;
     const bool bf = desc->io_dtype == KDA_BF16;
     size_t n = kda::prefill_workspace_bytes(desc->total_rows, desc->num_seqs, desc->num_heads,
-                                            desc->d_k, desc->d_v, bf);
+                                            desc->d_k, desc->d_v, bf, desc->window_chunks);
     if (desc->conv_mode != KDA_CONV_NONE)
         n += kda::conv_workspace_bytes(desc->total_rows, desc->num_heads, desc->d_k, desc->d_v, bf);
     return n;
@@ -268,9 +277,10 @@ kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v
                                      const int32_t *cu_seqlens, const float *state_in,
                                      float *state_out, void *o, const int32_t *slots,
                                      const kda_prefill_desc_t *desc, void *workspace,
-                                     size_t ws_bytes, void *stream, void *const *events) {
+                                     size_t ws_bytes, void *stream, void *const *events,
+                                     int32_t num_events) {
     return prefill_impl(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, slots, desc, nullptr,
-                        false, workspace, ws_bytes, stream, events);
+                        false, workspace, ws_bytes, stream, events, num_events);
 }
 
 kda_status_t kda_chunk_prefill_conv(const void *q, const void *k, const void *v, const float *g,
@@ -278,9 +288,9 @@ kda_status_t kda_chunk_prefill_conv(const void *q, const void *k, const void *v,
                                     const float *state_in, float *state_out, void *o,
                                     const int32_t *slots, const kda_prefill_desc_t *desc,
                                     const kda_conv_t *conv, void *workspace, size_t ws_bytes,
-                                    void *stream, void *const *events) {
+                                    void *stream, void *const *events, int32_t num_events) {
     return prefill_impl(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, slots, desc, conv,
-                        true, workspace, ws_bytes, stream, events);
+                        true, workspace, ws_bytes, stream, events, num_events);
 }
 
 kda_status_t kda_chunk_prefill_static(const void *q, const void *k, const void *v,
@@ -289,7 +299,7 @@ kda_status_t kda_chunk_prefill_static(const void *q, const void *k, const void *
                                       float *state_out, void *o, const int32_t *slots,
                                       const kda_prefill_desc_t *desc, void *stream) {
     return prefill_impl(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, slots, desc, nullptr,
-                        false, nullptr, 0, stream, nullptr, true);
+                        false, nullptr, 0, stream, nullptr, 0, true);
 }
 
 kda_status_t kda_chunk_prefill(const void *q, const void *k, const void *v, const float *g,
@@ -298,7 +308,7 @@ kda_status_t kda_chunk_prefill(const void *q, const void *k, const void *v, cons
                                const int32_t *slots, const kda_prefill_desc_t *desc,
                                void *workspace, size_t ws_bytes, void *stream) {
     return kda_chunk_prefill_timed(q, k, v, g, beta, cu_seqlens, state_in, state_out, o, slots,
-                                   desc, workspace, ws_bytes, stream, nullptr);
+                                   desc, workspace, ws_bytes, stream, nullptr, 0);
 }
 
 kda_status_t kda_decode_step_lines(const void *q, const void *k, const void *v, const float *g,

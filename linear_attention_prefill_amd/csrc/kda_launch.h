@@ -20,8 +20,25 @@ struct PrefillArgs {
     float scale;
     int64_t slot_stride, head_stride;   // state addressing, fp32 elements (resolved)
     int num_cus;            // compute units of the device (persistent grids)
-    hipEvent_t events[3];   // optional: before intra, between, after scan
+    int window_chunks = 0;  // chunk ids per window; 0 = the default policy
+    // optional timing events: [0] before the first kernel, then one after
+    // each kernel launch (intra and scan of each window in turn)
+    const hipEvent_t *events = nullptr;
+    int num_events = 0;
 };
+
+// How a prefill call splits into windows of chunk ids and lays out its
+// workspace: window_chunks x H records (w, Q e^Gam, K~^T, A_qk, u in the io
+// type), then the decay factors e^{Gam_C} (fp32), then, when there is more
+// than one window, the states carried between windows ([N][H][d_v][d_k]
+// fp32).
+struct PrefillPlan {
+    int chunk_ids;          // T / 64 + N
+    int windows;
+    int window_chunks;
+    size_t dec_offset, carry_offset, bytes;
+};
+PrefillPlan prefill_plan(int T, int N, int H, int dk, int dv, bool bf16, int window_chunks);
 
 // Most tokens a multi-token decode call may carry per sequence.
 constexpr int kMaxDecodeTokens = 16;
@@ -89,7 +106,7 @@ hipError_t launch_prefill_check(const float *g, const int32_t *cu, const int32_t
 // on the device `stream` runs on (looked up on the first call per device).
 hipError_t static_scratch(hipStream_t stream, void **ptr);
 
-size_t prefill_workspace_bytes(int T, int N, int H, int dk, int dv, bool bf16);
+size_t prefill_workspace_bytes(int T, int N, int H, int dk, int dv, bool bf16, int window_chunks);
 
 // Workspace bytes of the convolved q, k, v (placed after the records).
 size_t conv_workspace_bytes(int T, int H, int dk, int dv, bool bf16);

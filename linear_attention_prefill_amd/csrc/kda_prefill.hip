@@ -64,6 +64,12 @@ constexpr float kDiagSpanLimit = 64.f;
 constexpr int kIntraThreads = 512;     // 8 waves: two per SIMD
 constexpr int kCuCache = 256;          // sequence bounds kept in LDS when N < this
 constexpr int kScanWarmAhead = 2;      // chunks between a scan stage's record and the one it warms
+#ifndef KDA_NS8_STAGES
+#define KDA_NS8_STAGES 3
+#endif
+#ifndef KDA_SINGLE_CHAIN
+#define KDA_SINGLE_CHAIN 0
+#endif
 
 // LDS of the intra-chunk kernel.  For bf16, V is staged as a row-major tile
 // and read back as fragments; for fp32 (twice the bytes) it is read from
@@ -142,7 +148,7 @@ template <typename E, int DK, int DV>
 __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
-    const int32_t *__restrict__ cu, int T, int N, int H,
+    const int32_t *__restrict__ cu, int T, int N, int H, int c_lo, int c_hi,
     E *__restrict__ ws, float *__restrict__ ws_dec) {
     static_assert(DK == 64 || DK == 128, "d_k");
     static_assert(DV == 64 || DV == 128, "d_v");
@@ -182,7 +188,6 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
     // row of 16 lanes spans the chunk and a quad of lanes one 16-row block.
     const int r4 = lane & 15, cq = 4 * wave + lg, ch0 = 4 * cq;
     const bool fthread = wave < FW;
-    const int n_items = (T / kChunk + N) * H;
     const int stride = gridDim.x;
 
     // Sequence bounds: up to 64 in one register (lane i holds cu[i], read
@@ -208,10 +213,11 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
         if (cu_reg) return __builtin_amdgcn_readlane(cu_v, i);
         return __builtin_amdgcn_readfirstlane(cu_lds ? sCu[i] : cu_s[i]);
     };
-    // Items (chunk id cid, head h; item = cid H + h) are walked from the last
-    // one down in steps of the grid, so the records the state scan reads
-    // first are the ones written last and are still in the caches when it
-    // starts.  The step is kept as a quotient and remainder of H, so the walk
+    // Items (chunk id cid, head h; item = cid H + h) of the window
+    // [c_lo, c_hi) of chunk ids are walked from the last one down in steps of
+    // the grid, so the records the state scan reads first are the ones
+    // written last and are still in the caches when it starts.  Item (cid, h)
+    // writes record (cid - c_lo) H + h of the window's workspace.  The step is kept as a quotient and remainder of H, so the walk
     // needs no division.  find_chunk returns the first item at or below (cid,
     // h) on this walk that belongs to a sequence (ids between sequences'
     // chunk ranges are skipped).
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
         }
     };
     auto find_chunk = [&](int cid, int h) -> ChunkRef {
-        for (; cid >= 0; step_down(cid, h)) {
+        for (; cid >= c_lo; step_down(cid, h)) {
             int lo = 0, hi = N - 1;
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
 
     ChunkRef cur;
     {
-        const int item0 = n_items - 1 - (int)blockIdx.x;
+        const int item0 = c_hi * H - 1 - (int)blockIdx.x;
         cur = find_chunk(item0 / H, item0 % H);
     }
 #pragma unroll
@@ -300,7 +306,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
         E *const sV = sVb + buf * LD::V_ELEMS;
         float *const sBs = sBsb + buf * (4 * DK);
         const int C = cur.C;
-        const size_t rec = (size_t)cur.item;           // = cid * H + h
+        const size_t rec = (size_t)(cur.item - c_lo * H);   // = (cid - c_lo) H + h
         E *const Rw = ws + rec * L::kRecElems;
         E *const Rq = Rw + L::kWElems;
         E *const Rk = Rq + L::kQElems;
@@ -766,7 +772,8 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
     const E *__restrict__ ws, const float *__restrict__ ws_dec,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ slots,
     const float *state_in, float *state_out, E *__restrict__ o,
-    int T, int N, int H, int num_slots, float scale, int64_t slot_stride, int64_t head_stride) {
+    int T, int N, int H, int num_slots, float scale, int64_t slot_stride, int64_t head_stride,
+    int c_lo, int c_hi, float *__restrict__ carry) {
     constexpr int VT = DV / kSub, KS = DK / kSlab;
     constexpr int TPW = DK / 64;                       // key tiles per wave
     using L = WsLayout<E, DK, DV>;
@@ -782,8 +789,8 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
     // records as fast as three with the warm-up, without the warm-up's extra
     // touches of record lines, which slow the next call's intra-chunk kernel
     // by about 3 us on one 8192-row sequence.
-    constexpr int STAGES = NS > 1 ? 3 : (sizeof(E) == 2 ? 5 : 3);
-    static_assert(STAGES == 3 || STAGES == 5, "register stages");
+    constexpr int STAGES = NS > 4 ? KDA_NS8_STAGES : (NS > 1 ? 3 : (sizeof(E) == 2 ? 5 : 3));
+    static_assert(STAGES >= 2 && STAGES <= 5, "register stages");
     constexpr bool kWarm = NS == 1 && STAGES == 3;
     // rounded copies of the state slabs and of U, [slice][slab][lane][8]
     __shared__ __align__(16) E sSb[NS * KS * 64 * 8];
@@ -799,14 +806,29 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
     if (slots && (slot < 0 || slot >= num_slots)) return;   // padded sequence
     const SeqSpan sp = seq_span(cu, n, T);
     const int j0 = jt * NS * kSub;                     // first column; slice ns at j0 + 16 ns
+    // This launch's chunks of the sequence: those whose ids lie in the window
+    // [c_lo, c_hi).  The state comes from state_in at the sequence's first
+    // chunk and from the carry buffer after an earlier window; it goes to
+    // state_out after the last chunk and to the carry buffer otherwise.  A
+    // sequence with no rows is passed through by the window that holds its
+    // (empty) first chunk id.
+    const int nch_all = (sp.len + kChunk - 1) / kChunk;
+    const int j_lo = max(0, c_lo - sp.first_chunk);
+    const int j_hi = min(nch_all, c_hi - sp.first_chunk);
+    if (nch_all == 0 ? (sp.first_chunk < c_lo || sp.first_chunk >= c_hi) : j_lo >= j_hi) return;
+    const bool first_part = j_lo == 0, last_part = j_hi == nch_all;
+    float *const carry_blk = carry + ((size_t)n * H + h) * ((size_t)DV * DK);
 
     // my key tiles t = wave * TPW + i of slice ns, C layout: lane holds
     // S[16t + 4g + r][j0 + 16 ns + i]
     f32x4 S[NS][TPW];
+    const float *s_src = first_part ? (state_in ? state_in + slot * slot_stride + h * head_stride
+                                                : nullptr)
+                                    : carry_blk;
 #pragma unroll
     for (int ns = 0; ns < NS; ++ns) {
-        if (state_in) {
-            const float *src = state_in + slot * slot_stride + h * head_stride + (size_t)(j0 + ns * kSub + li) * DK;
+        if (s_src) {
+            const float *src = s_src + (size_t)(j0 + ns * kSub + li) * DK;
 #pragma unroll
             for (int i = 0; i < TPW; ++i)
                 S[ns][i] = *reinterpret_cast<const f32x4 *>(src + (wave * TPW + i) * kSub + 4 * lg);
@@ -833,8 +855,9 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
     // chunk STAGES ahead as soon as its last use in the current step has been
     // issued, so loads trickle out between the matrix-core products instead
     // of queueing behind them in one burst.
-    const int nch = (sp.len + kChunk - 1) / kChunk;
-    auto rec_of = [&](int cc) { return (size_t)(sp.first_chunk + cc) * H + h; };
+    // chunks j_lo .. j_hi - 1 of the sequence, renumbered from 0
+    const int nch = j_hi - j_lo;
+    auto rec_of = [&](int cc) { return (size_t)(sp.first_chunk + j_lo + cc - c_lo) * H + h; };
     // L2 warm-up.  All slices of a head ask for the same record lines at
     // about the same time, so without it most operand loads wait on an L2
     // miss still in flight.  Whenever the first stage of the rotation is
@@ -911,18 +934,27 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
 #pragma unroll
             for (int s = 0; s < KS; ++s) Sb[s] = load_frag<E>(sSb + ns * (KS * 512) + s * 512, lane);
             f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
-#pragma unroll
-            for (int s = 0; s < KS; s += 2) {
-                mma(a0, X.wf[s], Sb[s]);
-                mma(a1, X.wf[s + 1], Sb[s + 1]);
-            }
-            un[ns] = to_f32<E>(X.u[ns]) - (a0 + a1);
             o0[ns] = f32x4{0.f, 0.f, 0.f, 0.f};
             o1[ns] = o0[ns];
+            if constexpr (KDA_SINGLE_CHAIN && NS > 1) {
 #pragma unroll
-            for (int s = 0; s < KS; s += 2) {
-                mma(o0[ns], Sb[s], X.qf[s]);
-                mma(o1[ns], Sb[s + 1], X.qf[s + 1]);
+                for (int s = 0; s < KS; ++s) {
+                    mma(a0, X.wf[s], Sb[s]);
+                    mma(o0[ns], Sb[s], X.qf[s]);
+                }
+                un[ns] = to_f32<E>(X.u[ns]) - a0;
+            } else {
+#pragma unroll
+                for (int s = 0; s < KS; s += 2) {
+                    mma(a0, X.wf[s], Sb[s]);
+                    mma(a1, X.wf[s + 1], Sb[s + 1]);
+                }
+                un[ns] = to_f32<E>(X.u[ns]) - (a0 + a1);
+#pragma unroll
+                for (int s = 0; s < KS; s += 2) {
+                    mma(o0[ns], Sb[s], X.qf[s]);
+                    mma(o1[ns], Sb[s + 1], X.qf[s + 1]);
+                }
             }
         }
         if (refill) load_w(X, nx, warm);
@@ -930,12 +962,19 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
         for (int ns = 0; ns < NS; ++ns)
             store4<E>(sUb + ns * 1024 + ((wave >> 1) * 64 + lane) * 8 + (wave & 1) * 4, un[ns]);
         if (refill) load_q(X, nx);
-#pragma unroll
-        for (int ns = 0; ns < NS; ++ns)
+        {
+            float dfac[TPW][4];
 #pragma unroll
             for (int i = 0; i < TPW; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) S[ns][i][r] *= __shfl(X.d, i * kSub + 4 * lg + r);
+                for (int r = 0; r < 4; ++r) dfac[i][r] = __shfl(X.d, i * kSub + 4 * lg + r);
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+                for (int i = 0; i < TPW; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[ns][i][r] *= dfac[i][r];
+        }
         __syncthreads();
         const int row = wave * kSub + li;
 #pragma unroll
@@ -946,7 +985,10 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
             // my tile of O = Q~ S + A_qk U, transposed: lane holds row
             // 16 wave + i, columns j0 + 16 ns + 4g + r
             mma(o0[ns], ub[0], X.af[0]);
-            if (wave >= 2) mma(o1[ns], ub[1], X.af[1]);
+            if (wave >= 2) {
+                if constexpr (KDA_SINGLE_CHAIN && NS > 1) mma(o0[ns], ub[1], X.af[1]);
+                else mma(o1[ns], ub[1], X.af[1]);
+            }
             // my key tiles of S = diag(e^{Gam_C}) S + K~^T U
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
@@ -957,23 +999,23 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
         if (refill) load_k(X, nx);
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns)
-            if (row < sp.len - cc * kChunk)
-                store4<E>(o + ((size_t)(sp.start + cc * kChunk + row) * H + h) * DV + j0 + ns * kSub + 4 * lg,
+            if (row < sp.len - (j_lo + cc) * kChunk)
+                store4<E>(o + ((size_t)(sp.start + (j_lo + cc) * kChunk + row) * H + h) * DV + j0 + ns * kSub + 4 * lg,
                           (o0[ns] + o1[ns]) * scale);
     };
 
     if (nch > 0) {
-        if constexpr (STAGES == 5) {
-            Stage X[5];
+        if constexpr (!kWarm) {
+            Stage X[STAGES];
 #pragma unroll
-            for (int i = 0; i < 5; ++i) load_stage(X[i], i < nch ? i : nch - 1, false);
+            for (int i = 0; i < STAGES; ++i) load_stage(X[i], i < nch ? i : nch - 1, false);
             int cc = 0;
-            for (; cc + 4 < nch; cc += 5) {
+            for (; cc + STAGES - 1 < nch; cc += STAGES) {
 #pragma unroll
-                for (int i = 0; i < 5; ++i) step(X[i], cc + i, true, false);
+                for (int i = 0; i < STAGES; ++i) step(X[i], cc + i, true, false);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < STAGES - 1; ++i)
                 if (cc + i < nch) step(X[i], cc + i, false, false);
         } else {
             Stage A, Bs, Cs;
@@ -991,10 +1033,13 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
         }
     }
 
-    if (state_out) {
+    float *const s_dst = last_part ? (state_out ? state_out + slot * slot_stride + h * head_stride
+                                                : nullptr)
+                                   : carry_blk;
+    if (s_dst) {
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
-            float *dst = state_out + slot * slot_stride + h * head_stride + (size_t)(j0 + ns * kSub + li) * DK;
+            float *dst = s_dst + (size_t)(j0 + ns * kSub + li) * DK;
 #pragma unroll
             for (int i = 0; i < TPW; ++i)
                 *reinterpret_cast<f32x4 *>(dst + (wave * TPW + i) * kSub + 4 * lg) = S[ns][i];
@@ -1004,46 +1049,60 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
 
 template <typename E, int DK, int DV>
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
-    using L = WsLayout<E, DK, DV>;
-    const int max_chunks = a.T / kChunk + a.N;
-    E *ws = reinterpret_cast<E *>(a.workspace);
-    float *ws_dec = reinterpret_cast<float *>(reinterpret_cast<char *>(a.workspace) +
-                                              (size_t)max_chunks * a.H * L::kRecElems * sizeof(E));
+    const PrefillPlan pl = prefill_plan(a.T, a.N, a.H, DK, DV, sizeof(E) == 2, a.window_chunks);
+    char *const base = reinterpret_cast<char *>(a.workspace);
+    E *const ws = reinterpret_cast<E *>(base);
+    float *const ws_dec = reinterpret_cast<float *>(base + pl.dec_offset);
+    float *const carry = reinterpret_cast<float *>(base + pl.carry_offset);
     // An error left by an unrelated earlier call is not this call's: clear
     // it, so that the checks below see only this call's launches.
     (void)hipGetLastError();
-    if (a.events[0]) (void)hipEventRecord(a.events[0], stream);
-    if (max_chunks > 0) {
-        const long long items = (long long)max_chunks * a.H;
-        const int grid = (int)(items < (long long)a.num_cus ? items : (long long)a.num_cus);
-        kda_intra_kernel<E, DK, DV><<<dim3(grid), dim3(kIntraThreads), 0, stream>>>(
-            static_cast<const E *>(a.q), static_cast<const E *>(a.k), static_cast<const E *>(a.v),
-            a.g, a.beta, a.cu_seqlens, a.T, a.N, a.H, ws, ws_dec);
-        // A failed intra launch leaves stale records: the scan must not run
-        // on them and overwrite o and the caller's states.
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (a.events[1]) (void)hipEventRecord(a.events[1], stream);
+    int ev = 0;
+    auto mark = [&]() {
+        if (ev < a.num_events && a.events[ev]) (void)hipEventRecord(a.events[ev], stream);
+        ++ev;
+    };
     // The scan is bound by the record bytes each CU takes in, and a workgroup
     // of NS 16-column slices takes them in once for all NS.  So each call
     // gets the largest NS (1, 2 or 4; bf16 for NS > 1) that still leaves at
     // least one workgroup per CU.
     const long long slices = (long long)a.N * a.H * (DV / kSub);
-    auto scan = [&](auto ns) -> hipError_t {
+    auto scan = [&](auto ns, int c_lo, int c_hi) -> hipError_t {
         constexpr int NS = decltype(ns)::value;
         kda_scan_kernel<E, DK, DV, NS><<<dim3((int)(slices / NS)), dim3(256), 0, stream>>>(
             ws, ws_dec, a.cu_seqlens, a.slots, a.state_in, a.state_out, static_cast<E *>(a.o),
-            a.T, a.N, a.H, a.num_slots, a.scale, a.slot_stride, a.head_stride);
-        const hipError_t e = hipGetLastError();
-        if (a.events[2]) (void)hipEventRecord(a.events[2], stream);
-        return e;
+            a.T, a.N, a.H, a.num_slots, a.scale, a.slot_stride, a.head_stride, c_lo, c_hi, carry);
+        return hipGetLastError();
     };
-    if constexpr (sizeof(E) == 2) {
-        if (slices >= 4LL * a.num_cus) return scan(std::integral_constant<int, 4>{});
-        if (slices >= 2LL * a.num_cus) return scan(std::integral_constant<int, 2>{});
+    auto scan_window = [&](int c_lo, int c_hi) -> hipError_t {
+        if constexpr (sizeof(E) == 2) {
+            if (slices >= 4LL * a.num_cus) return scan(std::integral_constant<int, 4>{}, c_lo, c_hi);
+            if (slices >= 2LL * a.num_cus) return scan(std::integral_constant<int, 2>{}, c_lo, c_hi);
+        }
+        return scan(std::integral_constant<int, 1>{}, c_lo, c_hi);
+    };
+    // Windows of chunk ids, each an intra launch that writes its records and
+    // a scan launch that reads them while they are recent (the workspace
+    // holds one window's records and is reused by the next).
+    mark();
+    for (int w = 0; w < pl.windows; ++w) {
+        const int c_lo = w * pl.window_chunks;
+        const int c_hi = c_lo + pl.window_chunks < pl.chunk_ids ? c_lo + pl.window_chunks : pl.chunk_ids;
+        const long long items = (long long)(c_hi - c_lo) * a.H;
+        const int grid = (int)(items < (long long)a.num_cus ? items : (long long)a.num_cus);
+        kda_intra_kernel<E, DK, DV><<<dim3(grid), dim3(kIntraThreads), 0, stream>>>(
+            static_cast<const E *>(a.q), static_cast<const E *>(a.k), static_cast<const E *>(a.v),
+            a.g, a.beta, a.cu_seqlens, a.T, a.N, a.H, c_lo, c_hi, ws, ws_dec);
+        // A failed intra launch leaves stale records: the scan must not run
+        // on them and overwrite o and the caller's states.
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        mark();
+        e = scan_window(c_lo, c_hi);
+        if (e != hipSuccess) return e;
+        mark();
     }
-    return scan(std::integral_constant<int, 1>{});
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------
@@ -1087,11 +1146,37 @@ hipError_t static_scratch(hipStream_t stream, void **ptr) {
     return hipSuccess;
 }
 
-size_t prefill_workspace_bytes(int T, int N, int H, int dk, int dv, bool bf16) {
+PrefillPlan prefill_plan(int T, int N, int H, int dk, int dv, bool bf16, int window_chunks) {
+    PrefillPlan p;
     const size_t es = bf16 ? 2 : 4;
-    const size_t rec = (size_t)kChunk * (3 * dk + dv) + 6 * 512;
-    const size_t max_chunks = (size_t)(T / kChunk) + (size_t)N;
-    return max_chunks * (size_t)H * (rec * es + (size_t)dk * 4);
+    const size_t rec = ((size_t)kChunk * (3 * dk + dv) + 6 * 512) * es;
+    p.chunk_ids = T / kChunk + N;
+    // Default: two windows for calls with few (sequence, head) pairs and
+    // enough chunks, one otherwise.  Such calls scan long chains with one
+    // slice per workgroup, which take records in at a per-CU rate that is
+    // higher when they come from the last-level cache; half the records of
+    // an 8192-row call (150 MB at H = 32) stay there until the scan reads
+    // them (one 8192-row sequence at H = 32: scan 129 -> 109 us, intra
+    // 131 -> 145 us, step 256 -> 244 us).  Calls with many pairs run many
+    // short chains whose workgroups would each start twice (16 packed
+    // sequences: step 258 -> 277 us with two windows).
+    size_t wc = (size_t)p.chunk_ids;
+    if (window_chunks > 0) wc = (size_t)window_chunks;
+    else if ((long long)N * H <= 64 && p.chunk_ids >= 32) wc = ((size_t)p.chunk_ids + 1) / 2;
+    if (wc < 1) wc = 1;
+    p.windows = (int)(((size_t)p.chunk_ids + wc - 1) / wc);
+    if (p.windows < 1) p.windows = 1;
+    p.window_chunks = (p.chunk_ids + p.windows - 1) / p.windows;
+    const size_t recs = (size_t)p.window_chunks * H;
+    p.dec_offset = recs * rec;
+    p.carry_offset = (p.dec_offset + recs * (size_t)dk * 4 + 255) / 256 * 256;
+    const size_t carry = p.windows > 1 ? (size_t)N * H * dv * dk * 4 : 0;
+    p.bytes = p.carry_offset + carry;
+    return p;
+}
+
+size_t prefill_workspace_bytes(int T, int N, int H, int dk, int dv, bool bf16, int window_chunks) {
+    return prefill_plan(T, N, H, dk, dv, bf16, window_chunks).bytes;
 }
 
 size_t conv_workspace_bytes(int T, int H, int dk, int dv, bool bf16) {

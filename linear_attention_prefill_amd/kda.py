@@ -33,7 +33,7 @@ class PrefillDesc(ctypes.Structure):
                 ("num_slots", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("state_slot_stride", ctypes.c_int64),
                 ("state_head_stride", ctypes.c_int64), ("conv_mode", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("window_chunks", ctypes.c_int32)]
 
 
 class ConvDesc(ctypes.Structure):
@@ -73,11 +73,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_chunk_prefill_timed.restype = ctypes.c_int
     lib.kda_chunk_prefill_timed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                             ctypes.POINTER(PrefillDesc), vp, sz, vp,
-                                            ctypes.POINTER(ctypes.c_void_p)]
+                                            ctypes.POINTER(ctypes.c_void_p), i32]
     lib.kda_chunk_prefill_conv.restype = ctypes.c_int
     lib.kda_chunk_prefill_conv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                            ctypes.POINTER(PrefillDesc), ctypes.POINTER(ConvDesc),
-                                           vp, sz, vp, ctypes.POINTER(ctypes.c_void_p)]
+                                           vp, sz, vp, ctypes.POINTER(ctypes.c_void_p), i32]
+    lib.kda_prefill_windows.restype = i32
+    lib.kda_prefill_windows.argtypes = [ctypes.POINTER(PrefillDesc)]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                     i32, i32, i32, i32, i32, i32, f32, vp]
@@ -177,10 +179,10 @@ def check_prefill_inputs(g, cu_seqlens, slots=None, num_slots=None, stream=None)
 
 
 def make_desc(T, N, H, d_k, d_v, num_slots, io_dtype, scale=1.0, slot_stride=0,
-              head_stride=0, conv_mode=0) -> PrefillDesc:
+              head_stride=0, conv_mode=0, window_chunks=0) -> PrefillDesc:
     return PrefillDesc(int(T), int(N), int(H), int(d_k), int(d_v), int(num_slots),
                        int(io_dtype), float(scale), int(slot_stride), int(head_stride),
-                       int(conv_mode), 0)
+                       int(conv_mode), int(window_chunks))
 
 
 def conv_extent(num_slots, H, d_k, d_v, strides) -> int:
@@ -241,8 +243,18 @@ def _check_pool(p, name, num_slots, H, dk, dv, slot_stride, head_stride):
         _dev(p, name, torch.float32, (num_slots, H, dv, dk))
 
 
-def prefill_workspace_size(T, N, H, d_k, d_v, dtype=torch.bfloat16, conv=False) -> int:
-    d = make_desc(T, N, H, d_k, d_v, N, _io_code(dtype), conv_mode=1 if conv else 0)
+def prefill_windows(T, N, H, d_k, d_v, dtype=torch.bfloat16, window_chunks=0) -> int:
+    """Windows of chunk ids a prefill call of these sizes runs as
+    (``kda_prefill_windows``): its kernels are an intra-chunk kernel and a
+    state scan per window, in that order."""
+    d = make_desc(T, N, H, d_k, d_v, N, _io_code(dtype), window_chunks=window_chunks)
+    return int(load_library().kda_prefill_windows(ctypes.byref(d)))
+
+
+def prefill_workspace_size(T, N, H, d_k, d_v, dtype=torch.bfloat16, conv=False,
+                           window_chunks=0) -> int:
+    d = make_desc(T, N, H, d_k, d_v, N, _io_code(dtype), conv_mode=1 if conv else 0,
+                  window_chunks=window_chunks)
     return int(load_library().kda_prefill_workspace_size(ctypes.byref(d)))
 
 
@@ -250,7 +262,7 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
                   slots=None, num_slots=None, scale=1.0, workspace=None, stream=None,
                   events=None, state_slot_stride=0, state_head_stride=0, conv_weight=None,
                   conv_window=None, conv_activation="none", conv_strides=(0, 0, 0, 0),
-                  check_inputs=False):
+                  check_inputs=False, window_chunks=0):
     """KDA chunked prefill over packed sequences (see ``kda_chunk_prefill``).
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype); g: [T, H, d_k]
@@ -263,13 +275,15 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
     [num_slots, H, 3, 2 d_k + d_v] or any tensor the conv_strides (slot,
     head, row, part) address) q, k, v are raw inputs to the short conv front
     end (``kda_chunk_prefill_conv``); the window is updated in place.
-    events: optional three recorded
-    torch.cuda.Event(enable_timing=True) objects, recorded before the
-    intra-chunk kernel, between the kernels and after the scan
-    (``kda_chunk_prefill_timed``).  check_inputs: first run the opt-in check
+    events: optional list of recorded torch.cuda.Event(enable_timing=True)
+    objects: the first is recorded before the first kernel and the i-th after
+    the i-th kernel launch (intra and scan of each window in turn; 2 W + 1
+    events for W = prefill_windows(...) windows; ``kda_chunk_prefill_timed``).  check_inputs: first run the opt-in check
     of the device data (``kda_prefill_check``, which synchronises) and raise
     ValueError if it fails.  Tensors the call allocates (o when None, the
-    workspace when None) come from the launch stream's memory pool.  Returns
+    workspace when None) come from the launch stream's memory pool.
+    window_chunks: chunk ids per window (kda.h, kda_prefill_windows); 0 lets
+    the library choose.  Returns
     o [T, H, d_v].
     """
     lib = load_library()
@@ -306,7 +320,7 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
     if conv_weight is not None:
         conv = _conv_desc(conv_weight, conv_window, H, dk, dv, q.dtype, conv_strides, num_slots)
     desc = make_desc(T, N, H, dk, dv, num_slots, io, scale, state_slot_stride, state_head_stride,
-                     _conv_mode(conv_activation) if conv is not None else 0)
+                     _conv_mode(conv_activation) if conv is not None else 0, window_chunks)
     need = int(lib.kda_prefill_workspace_size(ctypes.byref(desc)))
     if workspace is None:
         # Allocated from the launch stream's pool: when it is freed on return
@@ -318,23 +332,23 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(state_in),
             _ptr(state_out), _ptr(o), _ptr(slots), ctypes.byref(desc), _ptr(workspace),
             workspace.numel(), _stream(stream))
-    handles = None
+    handles, n_ev = None, 0
     if events is not None:
-        if len(events) != 3:
-            raise ValueError("events must hold three torch.cuda.Event objects")
-        handles = (ctypes.c_void_p * 3)(*[_event_handle(e) for e in events])
+        n_ev = len(events)
+        handles = (ctypes.c_void_p * max(n_ev, 1))(*[_event_handle(e) for e in events])
     if conv is not None:
-        _check(lib.kda_chunk_prefill_conv(*args[:11], ctypes.byref(conv), *args[11:], handles))
+        _check(lib.kda_chunk_prefill_conv(*args[:11], ctypes.byref(conv), *args[11:], handles,
+                                          n_ev))
     elif handles is None:
         _check(lib.kda_chunk_prefill(*args))
     else:
-        _check(lib.kda_chunk_prefill_timed(*args, handles))
+        _check(lib.kda_chunk_prefill_timed(*args, handles, n_ev))
     return o
 
 
 def chunk_prefill_no_alloc(q, k, v, g, beta, cu_seqlens, o, state_in=None, state_out=None,
                            slots=None, num_slots=None, scale=1.0, stream=None,
-                           state_slot_stride=0, state_head_stride=0):
+                           state_slot_stride=0, state_head_stride=0, window_chunks=0):
     """chunk_prefill through ``kda_chunk_prefill_static``, for callers that
     cannot allocate: o is required, no workspace is passed and nothing is
     allocated, here or in the library (its workspace is a static device array
@@ -364,7 +378,8 @@ def chunk_prefill_no_alloc(q, k, v, g, beta, cu_seqlens, o, state_in=None, state
     if o is None:
         raise ValueError("o is required: this entry point allocates nothing")
     _dev(o, "o", q.dtype, (T, H, dv))
-    desc = make_desc(T, N, H, dk, dv, num_slots, io, scale, state_slot_stride, state_head_stride)
+    desc = make_desc(T, N, H, dk, dv, num_slots, io, scale, state_slot_stride, state_head_stride,
+                     window_chunks=window_chunks)
     _check(lib.kda_chunk_prefill_static(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                         _ptr(cu_seqlens), _ptr(state_in), _ptr(state_out),
                                         _ptr(o), _ptr(slots), ctypes.byref(desc),

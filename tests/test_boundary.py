@@ -47,7 +47,8 @@ def test_header_declares_expected_entry_points():
     for n in ("kda_chunk_prefill", "kda_decode_step", "kda_prefill_workspace_size",
               "kda_status_string", "kda_version", "kda_chunk_prefill_timed",
               "kda_decode_step_lines", "kda_decode_tokens", "kda_chunk_prefill_conv",
-              "kda_decode_step_conv", "kda_prefill_check", "kda_chunk_prefill_static"):
+              "kda_decode_step_conv", "kda_prefill_check", "kda_chunk_prefill_static",
+              "kda_prefill_windows"):
         assert n in names
 
 
@@ -217,7 +218,7 @@ def _conv(w=A, win=A, ss=0, hs=0, rs=0, ps=0):
 def _prefill_conv(lib, desc, conv, ws_bytes=1 << 40):
     return lib.kda_chunk_prefill_conv(A, A, A, A, A, A, None, None, A, None, ctypes.byref(desc),
                                       ctypes.byref(conv) if conv is not None else None, A,
-                                      ws_bytes, None, None)
+                                      ws_bytes, None, None, 0)
 
 
 def test_prefill_conv_rejects_bad_arguments(lib):
@@ -298,7 +299,8 @@ def test_static_prefill_rejects_before_launch(lib):
     the static scratch, before it looks anything up on a device."""
     fake = ctypes.c_void_p(0x10000)
     args = [fake] * 6 + [None, None, fake, None]
-    big = _desc(T=16384, N=1, H=32, slots=1)
+    big = _desc(T=16384, N=16, H=32, slots=16)
+    assert lib.kda_prefill_workspace_size(ctypes.byref(big)) > K.STATIC_SCRATCH_BYTES
     assert lib.kda_chunk_prefill_static(*args, ctypes.byref(big), None) == 8
     d = _desc()
     bad = list(args)

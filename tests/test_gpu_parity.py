@@ -342,11 +342,22 @@ def test_decay_range_paths(mu_g, io):
     _check_case(c)
 
 
+def _scan_slices_per_workgroup(n_slices, dv, cus=256):
+    """The number of 16-column slices a bf16 scan workgroup takes: the largest
+    of 8, 4 and 2 that divides d_v / 16 and still leaves every CU one
+    workgroup, else 1."""
+    for ns in (8, 4, 2):
+        if (dv // 16) % ns == 0 and n_slices >= ns * cus:
+            return ns
+    return 1
+
+
 @pytest.mark.parametrize("dk,dv,H,ns", [(128, 128, 4, 4), (128, 128, 2, 2), (64, 64, 4, 2),
-                                        (128, 64, 4, 2), (64, 64, 8, 4)])
+                                        (128, 64, 4, 2), (64, 64, 8, 4), (128, 128, 8, 8),
+                                        (64, 128, 8, 8)])
 def test_many_pairs_multi_slice_scan(dk, dv, H, ns):
     """Enough (sequence, head, 16-column slice) triples for bf16 calls to take
-    the scan whose workgroups apply each chunk's operands to ns = 2 or 4
+    the scan whose workgroups apply each chunk's operands to ns = 2, 4 or 8
     slices (at least ns slices per CU on a 256-CU part); ragged and empty
     sequences, padded slots and in-place pools included."""
     rng = np.random.default_rng(17 + dk + dv + H)
@@ -356,7 +367,7 @@ def test_many_pairs_multi_slice_scan(dk, dv, H, ns):
     c = W.random_case(400 + dk + dv + H, lengths, H=H, d_k=dk, d_v=dv, io_dtype="bf16",
                       num_slots=60, slots=slots)
     n_slices = c.N * c.H * (dv // 16)
-    assert ns * 256 <= n_slices < (2 * ns if ns < 4 else 10 ** 9) * 256
+    assert _scan_slices_per_workgroup(n_slices, dv) == ns
     announce("%d-slice scan %s" % (ns, c.name))
     o_g, _, _, _, _ = _check_case(c)
     cu = c.cu_seqlens
@@ -432,7 +443,7 @@ def test_two_slice_scan_long_sequences():
     c = W.random_case(702, [4096, 4096], H=32, d_k=128, d_v=128, io_dtype="bf16", num_slots=4,
                       pool_std=0.02)
     n_slices = c.N * c.H * (c.d_v // 16)
-    assert 2 * 256 <= n_slices < 4 * 256
+    assert _scan_slices_per_workgroup(n_slices, c.d_v) == 2
     _check_case(c)
 
 
@@ -487,3 +498,61 @@ def test_check_inputs_flags_each_violation():
     torch.cuda.synchronize()
     o_r, _, _ = oracle_prefill(c)
     assert per_sequence_errors(c, o.float().cpu().numpy(), o_r)[0] <= TOL["bf16"]
+
+
+WINDOW_LENGTHS = [1, 63, 64, 65, 2, 127, 128, 129, 0, 31, 33, 96, 250, 1, 17, 60]
+
+
+@pytest.mark.parametrize("window_chunks,io", [(1, "bf16"), (2, "bf16"), (5, "bf16"), (3, "f32")])
+def test_windows_match_one_window(window_chunks, io):
+    """A call run as windows of chunk ids (intra kernel and scan per window,
+    states carried between windows in fp32) gives the same bits as one
+    window: the records, their use and the carried states are the same
+    numbers.  Window edges fall inside sequences, between them and on empty
+    ones; checked against the oracle too."""
+    c = W.random_case(711 + window_chunks, WINDOW_LENGTHS, H=2, d_k=128, d_v=128, io_dtype=io)
+    dt = torch_dtype(io)
+    nw = lap.prefill_windows(c.T, c.N, c.H, c.d_k, c.d_v, dt, window_chunks=window_chunks)
+    assert nw == -(-(c.T // 64 + c.N) // window_chunks)
+    outs = []
+    for wc in (0, window_chunks):
+        pool = dev(c.state_pool)
+        o = torch.full((c.T, c.H, c.d_v), 3.0, dtype=dt, device="cuda")
+        announce("prefill %s window_chunks=%d" % (c.name, wc))
+        lap.chunk_prefill(dev(c.q, dt), dev(c.k, dt), dev(c.v, dt), dev(c.g), dev(c.beta),
+                          dev(c.cu_seqlens), state_in=pool, state_out=pool, o=o,
+                          slots=dev(c.slots), window_chunks=wc)
+        torch.cuda.synchronize()
+        outs.append((o, pool))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    o_r, pool_r, _ = oracle_prefill(c, o_init=np.full((c.T, c.H, c.d_v), 3.0))
+    eo, es = per_sequence_errors(c, outs[1][0].float().cpu().numpy(), o_r,
+                                 outs[1][1].cpu().numpy(), pool_r)
+    announce("  max relative error: o %.3g, state %.3g (tolerance %.3g)" % (eo, es, TOL[io]))
+    assert eo <= TOL[io] and es <= TOL[io]
+
+
+@pytest.mark.parametrize("workload,window_chunks", [("packed", 37), ("single", 33)])
+def test_windows_full_size(workload, window_chunks):
+    """The full packed chunk and the full single sequence run as 4 windows,
+    bit for bit against one window, with the state carried in place (packed)
+    and out of a null state_in (single)."""
+    c = W.packed_varlen_prefill() if workload == "packed" else W.single_seq_prefill()
+    dt = torch.bfloat16
+    q, k, v, g, beta = dev(c.q, dt), dev(c.k, dt), dev(c.v, dt), dev(c.g), dev(c.beta)
+    cu = dev(c.cu_seqlens)
+    outs = []
+    for wc in (0, window_chunks):
+        if c.state_pool is not None:
+            pool, pin, slots = dev(c.state_pool), None, dev(c.slots)
+            pin = pool
+        else:
+            pool = torch.zeros((1, c.H, c.d_v, c.d_k), dtype=torch.float32, device="cuda")
+            pin, slots = None, None
+        announce("prefill %s window_chunks=%d" % (c.name, wc))
+        o = lap.chunk_prefill(q, k, v, g, beta, cu, state_in=pin, state_out=pool, slots=slots,
+                              window_chunks=wc)
+        torch.cuda.synchronize()
+        outs.append((o, pool))
+    assert lap.prefill_windows(c.T, c.N, c.H, c.d_k, c.d_v, dt, window_chunks=window_chunks) == 4
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])

@@ -56,14 +56,14 @@ def test_no_alloc_matches_workspace_entry_on_two_calls():
 
 
 def test_no_alloc_rejects_calls_beyond_the_scratch():
-    T, H, d = 16384, 32, 128
-    assert lap.prefill_workspace_size(T, 1, H, d, d) > lap.kda.STATIC_SCRATCH_BYTES
+    T, N, H, d = 16384, 16, 32, 128
+    assert lap.prefill_workspace_size(T, N, H, d, d) > lap.kda.STATIC_SCRATCH_BYTES
     dt = torch.bfloat16
     q = torch.zeros((T, H, d), dtype=dt, device="cuda")
     g = torch.zeros((T, H, d), dtype=torch.float32, device="cuda")
     beta = torch.zeros((T, H), dtype=torch.float32, device="cuda")
     o = torch.full((T, H, d), 3.0, dtype=dt, device="cuda")
-    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    cu = torch.arange(0, T + 1, T // N, dtype=torch.int32, device="cuda")
     announce("allocation-free prefill, oversize call")
     with pytest.raises(lap.KdaError) as err:
         lap.chunk_prefill_no_alloc(q, q, q, g, beta, cu, o)
