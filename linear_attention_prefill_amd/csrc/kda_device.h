@@ -214,7 +214,7 @@ template <typename E, int DK, int DV> struct WsLayout {
     static constexpr int kQElems = kChunk * DK;           // q*exp(Gamma): same
     static constexpr int kKElems = DK * kChunk;           // K~^T: (DK/16) x 2 frags
     static constexpr int kAElems = 6 * 512;               // A_qk: the 6 lower frags
-    static constexpr int kUElems = kChunk * DV;           // u: (DV/16) tiles x 64 lanes x 16
+    static constexpr int kUElems = kChunk * DV;           // u: (DV/16) tiles x 4 row tiles x 64 lanes x 4
     static constexpr int kRecElems = kWElems + kQElems + kKElems + kAElems + kUElems;
 };
 

@@ -670,7 +670,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 mma(acc, tm_frag(m, 0), vf[0]);
                 if (m >= 2) mma(acc, tm_frag(m, 1), vf[1]);
-                store4<E>(Ru + wave * (64 * 16) + lane * 16 + 4 * m, acc);
+                store4<E>(Ru + wave * (64 * 16) + m * 256 + lane * 4, acc);
             }
         }
         {
@@ -881,7 +881,7 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns)
             X.u[ns] = *reinterpret_cast<const typename Raw4<E>::type *>(
-                Ru + (jt * NS + ns) * (64 * 16) + lane * 16 + 4 * wave);
+                Ru + (jt * NS + ns) * (64 * 16) + wave * 256 + lane * 4);
     };
     auto load_q = [&](Stage &X, int cc) {
         const E *Rq = ws + rec_of(cc) * L::kRecElems + L::kWElems;
@@ -893,7 +893,9 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
         const E *Rk = ws + rec * L::kRecElems + L::kWElems + L::kQElems;
         const E *Ra = Rk + L::kKElems;
         X.af[0] = load_frag<E>(Ra + tri_frag(wave, 0) * 512, lane);
-        X.af[1] = load_frag<E>(Ra + tri_frag(wave, 1) * 512, lane);   // unused by waves 0, 1
+        // waves 0 and 1 have no second fragment: they reload their first,
+        // which the L1 serves, instead of pulling an unused kilobyte
+        X.af[1] = load_frag<E>(Ra + tri_frag(wave, wave >= 2 ? 1 : 0) * 512, lane);
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
             const int t = wave * TPW + i;
