@@ -64,9 +64,6 @@ constexpr float kDiagSpanLimit = 64.f;
 constexpr int kIntraThreads = 512;     // 8 waves: two per SIMD
 constexpr int kCuCache = 256;          // sequence bounds kept in LDS when N < this
 constexpr int kScanWarmAhead = 2;      // chunks between a scan stage's record and the one it warms
-#ifndef KDA_NS8_STAGES
-#define KDA_NS8_STAGES 3
-#endif
 #ifndef KDA_SINGLE_CHAIN
 #define KDA_SINGLE_CHAIN 0
 #endif
@@ -789,7 +786,7 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
     // records as fast as three with the warm-up, without the warm-up's extra
     // touches of record lines, which slow the next call's intra-chunk kernel
     // by about 3 us on one 8192-row sequence.
-    constexpr int STAGES = NS > 4 ? KDA_NS8_STAGES : (NS > 1 ? 3 : (sizeof(E) == 2 ? 5 : 3));
+    constexpr int STAGES = NS > 1 ? 3 : (sizeof(E) == 2 ? 5 : 3);
     static_assert(STAGES >= 2 && STAGES <= 5, "register stages");
     constexpr bool kWarm = NS == 1 && STAGES == 3;
     // rounded copies of the state slabs and of U, [slice][slab][lane][8]

@@ -344,20 +344,20 @@ def test_decay_range_paths(mu_g, io):
 
 def _scan_slices_per_workgroup(n_slices, dv, cus=256):
     """The number of 16-column slices a bf16 scan workgroup takes: the largest
-    of 8, 4 and 2 that divides d_v / 16 and still leaves every CU one
-    workgroup, else 1."""
-    for ns in (8, 4, 2):
+    of 4 and 2 that divides d_v / 16 and still leaves every CU ns
+    workgroups' worth of slices, else 1."""
+    for ns in (4, 2):
         if (dv // 16) % ns == 0 and n_slices >= ns * cus:
             return ns
     return 1
 
 
 @pytest.mark.parametrize("dk,dv,H,ns", [(128, 128, 4, 4), (128, 128, 2, 2), (64, 64, 4, 2),
-                                        (128, 64, 4, 2), (64, 64, 8, 4), (128, 128, 8, 8),
-                                        (64, 128, 8, 8)])
+                                        (128, 64, 4, 2), (64, 128, 4, 4), (128, 128, 5, 4),
+                                        (64, 128, 5, 4)])
 def test_many_pairs_multi_slice_scan(dk, dv, H, ns):
     """Enough (sequence, head, 16-column slice) triples for bf16 calls to take
-    the scan whose workgroups apply each chunk's operands to ns = 2, 4 or 8
+    the scan whose workgroups apply each chunk's operands to ns = 2 or 4
     slices (at least ns slices per CU on a 256-CU part); ragged and empty
     sequences, padded slots and in-place pools included."""
     rng = np.random.default_rng(17 + dk + dv + H)
@@ -372,6 +372,52 @@ def test_many_pairs_multi_slice_scan(dk, dv, H, ns):
     o_g, _, _, _, _ = _check_case(c)
     cu = c.cu_seqlens
     assert np.all(o_g[cu[5]:cu[6]] == 3.0)           # the padded sequence keeps its rows
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+def test_many_pairs_ragged(dk, dv):
+    """280 (sequence, head) pairs of ragged, empty and one-row sequences of
+    1..6 chunks, a padded slot and a pool updated in place, at every d_k, d_v:
+    bf16 calls that take the scan with the most slices per workgroup their
+    d_v allows."""
+    rng = np.random.default_rng(23 + dk + dv)
+    lengths = [int(x) for x in rng.choice([0, 1, 2, 63, 64, 65, 128, 129, 200, 321, 384], size=70)]
+    slots = [int(s) for s in rng.permutation(80)[:70]]
+    slots[9] = -1
+    c = W.random_case(430 + dk + dv, lengths, H=4, d_k=dk, d_v=dv, io_dtype="bf16",
+                      num_slots=80, slots=slots)
+    assert _scan_slices_per_workgroup(c.N * c.H * (dv // 16), dv) == (4 if dv == 128 else 2)
+    announce("many pairs %s" % c.name)
+    o_g, _, _, _, _ = _check_case(c)
+    cu = c.cu_seqlens
+    assert np.all(o_g[cu[9]:cu[10]] == 3.0)           # the padded sequence keeps its rows
+
+
+def test_many_pairs_windows_match_one_window():
+    """A four-slice scan run as windows of 3 chunk ids (fp32 states carried
+    between windows) gives the bits of one window, and the oracle's
+    results."""
+    rng = np.random.default_rng(29)
+    lengths = [int(x) for x in rng.choice([0, 1, 64, 65, 200, 450], size=70)]
+    c = W.random_case(439, lengths, H=4, d_k=128, d_v=128, io_dtype="bf16", num_slots=70)
+    assert _scan_slices_per_workgroup(c.N * c.H * (c.d_v // 16), c.d_v) == 4
+    dt = torch.bfloat16
+    outs = []
+    for wc in (0, 3):
+        pool = dev(c.state_pool)
+        o = torch.full((c.T, c.H, c.d_v), 3.0, dtype=dt, device="cuda")
+        announce("prefill %s window_chunks=%d" % (c.name, wc))
+        lap.chunk_prefill(dev(c.q, dt), dev(c.k, dt), dev(c.v, dt), dev(c.g), dev(c.beta),
+                          dev(c.cu_seqlens), state_in=pool, state_out=pool, o=o,
+                          slots=dev(c.slots), window_chunks=wc)
+        torch.cuda.synchronize()
+        outs.append((o, pool))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    o_r, pool_r, _ = oracle_prefill(c, o_init=np.full((c.T, c.H, c.d_v), 3.0))
+    eo, es = per_sequence_errors(c, outs[1][0].float().cpu().numpy(), o_r,
+                                 outs[1][1].cpu().numpy(), pool_r)
+    announce("  max relative error: o %.3g, state %.3g (tolerance %.3g)" % (eo, es, TOL["bf16"]))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
 
 
 def test_malformed_device_data_stays_in_bounds():
