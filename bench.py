@@ -202,10 +202,12 @@ def time_prefill(case, steps, warmup, copies, torch, lap, conv=None):
     total_ms = start.elapsed_time(end)
     # per-kernel durations: the same steps again with events recorded on the
     # launch stream before the first kernel and after every kernel (intra and
-    # scan of each window in turn; events between kernels cost a few
-    # microseconds a step, so they stay out of the timed steps above)
+    # scan of each window in turn, then the fused prefill if the call runs
+    # it; events between kernels cost a few microseconds a step, so they stay
+    # out of the timed steps above)
     nw = lap.prefill_windows(T, case.N, H, dk, dv, dt)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nw + 1)]
+    fused = lap.prefill_fuse_chunks(T, case.N, H, dk, dv, dt) >= 0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * nw + 1 + int(fused))]
            for _ in range(steps)]
     for row in evs:           # torch creates the underlying hipEvents on first record
         for e in row:
@@ -216,11 +218,13 @@ def time_prefill(case, steps, warmup, copies, torch, lap, conv=None):
     torch.cuda.synchronize()
     intra = [sum(e[2 * w].elapsed_time(e[2 * w + 1]) for w in range(nw)) for e in evs]
     scan = [sum(e[2 * w + 1].elapsed_time(e[2 * w + 2]) for w in range(nw)) for e in evs]
+    fz = [e[2 * nw].elapsed_time(e[2 * nw + 1]) if fused else 0.0 for e in evs]
     return {
         "ms_per_step": total_ms / steps,
         "intra_ms": float(np.mean(intra)), "scan_ms": float(np.mean(scan)),
         "intra_ms_median": float(np.median(intra)), "scan_ms_median": float(np.median(scan)),
-        "state_in": state_in, "windows": nw,
+        "fused_ms": float(np.mean(fz)), "fused_ms_median": float(np.median(fz)),
+        "state_in": state_in, "windows": nw, "fused": fused,
     }
 
 
@@ -401,6 +405,9 @@ def prefill_line(case, r, src_hash, conv=False):
         "kda_intra_kernel": {"us": r["intra_ms"] * 1e3, "us_median": r["intra_ms_median"] * 1e3},
         "kda_scan_kernel": {"us": r["scan_ms"] * 1e3, "us_median": r["scan_ms_median"] * 1e3},
     }
+    if r.get("fused"):
+        kern["kda_fused_prefill_kernel"] = {"us": r["fused_ms"] * 1e3,
+                                            "us_median": r["fused_ms_median"] * 1e3}
     dom = max(kern, key=lambda n: kern[n]["us"])
     t_dom = kern[dom]["us"] * 1e-6
     achieved = pb / t_dom / 1e9
@@ -652,7 +659,7 @@ def main():
         rc = time_prefill(case, max(5, args.steps // 2), 2, args.copies, torch, lap,
                           conv=(cw[0], cw[1], "silu"))
         lc = prefill_line(case, rc, src_hash, conv=True)
-        lc["conv_us"] = (rc["ms_per_step"] - rc["intra_ms"] - rc["scan_ms"]) * 1e3
+        lc["conv_us"] = (rc["ms_per_step"] - rc["intra_ms"] - rc["scan_ms"] - rc["fused_ms"]) * 1e3
         extra["prefill_conv"] = lc
         log("%s with conv %.1f us/step (conv front end %.1f us)"
             % (case.name, rc["ms_per_step"] * 1e3, lc["conv_us"]))

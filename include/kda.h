@@ -141,6 +141,9 @@ typedef struct {
     int64_t state_head_stride;  /* fp32 elements between heads of a line; 0 = dense */
     int32_t conv_mode;   /* kda_conv_mode_t; not NONE only with kda_chunk_prefill_conv */
     int32_t window_chunks;  /* chunk ids per window (kda_prefill_windows); 0 = the library's choice */
+    int32_t fuse_chunks;    /* bf16: sequences of at most this many 64-row chunks run in the fused
+                             * prefill (kda_prefill_fuse_chunks); 0 = the library's choice,
+                             * < 0 = none */
 } kda_prefill_desc_t;
 
 /*
@@ -152,6 +155,22 @@ typedef struct {
  * stages).
  */
 int32_t kda_prefill_windows(const kda_prefill_desc_t *desc);
+
+/*
+ * The fused prefill (bf16 only): each (sequence, head) pair of a sequence of
+ * at most F chunks runs whole in one workgroup, which computes a chunk's
+ * intra-chunk terms and applies them to the state it keeps in registers at
+ * once, so no per-chunk record goes through memory (the prhub report on
+ * SGLang PR #32890, sections "实现拆解" and "关键文件", fuses the
+ * intra-chunk stages into one persistent kernel; here the state stage joins
+ * them).  Longer sequences take the windows of intra-chunk kernel and scan.
+ * The fused kernel runs a pair's chunks one after another, so it pays off
+ * for many short sequences and not for long ones.  Returns F for `desc`
+ * (-1: no sequence is fused, or desc is invalid): desc->fuse_chunks when it
+ * is positive, none when it is negative, else the library's choice from the
+ * sizes alone.
+ */
+int32_t kda_prefill_fuse_chunks(const kda_prefill_desc_t *desc);
 
 /*
  * Bytes of device workspace kda_chunk_prefill needs for `desc` (0 if desc is
@@ -213,8 +232,10 @@ kda_status_t kda_chunk_prefill(const void *q, const void *k, const void *v,
  * a state scan.  When `events` is not NULL it points to num_events hipEvent_t:
  * events[0] is recorded on `stream` before the first kernel and events[i]
  * after the i-th kernel launch, in launch order (intra of window 0, scan of
- * window 0, intra of window 1, ...), as long as i < num_events; so 2 W + 1
- * events time every kernel of a W-window call with hipEventElapsedTime.  The
+ * window 0, intra of window 1, ..., then the fused prefill when
+ * kda_prefill_fuse_chunks is not negative), as long as i < num_events; so
+ * 2 W + 1 events (2 W + 2 with the fused prefill) time every kernel of a
+ * W-window call with hipEventElapsedTime.  The
  * events are created and owned by the caller.  Results and errors are those
  * of kda_chunk_prefill.
  */

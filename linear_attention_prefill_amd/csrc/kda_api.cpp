@@ -208,6 +208,7 @@ kda_status_t prefill_impl(const void *q, const void *k, const void *v, const flo
     a.num_events = events ? num_events : 0;
     a.num_cus = device_cus(s);
     a.window_chunks = d.window_chunks;
+    a.fuse_chunks = d.fuse_chunks;
     const hipError_t e = bf ? dispatch_prefill<bf16>(a, d.d_k, d.d_v, s)
                             : dispatch_prefill<float>(a, d.d_k, d.d_v, s);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
@@ -260,6 +261,12 @@ int32_t kda_prefill_windows(const kda_prefill_desc_t *desc) {
     if (check_desc(desc) != KDA_OK) return 0;
     return kda::prefill_plan(desc->total_rows, desc->num_seqs, desc->num_heads, desc->d_k,
                              desc->d_v, desc->io_dtype == KDA_BF16, desc->window_chunks).windows;
+}
+
+int32_t kda_prefill_fuse_chunks(const kda_prefill_desc_t *desc) {
+    if (check_desc(desc) != KDA_OK) return -1;
+    return kda::prefill_fuse_max(desc->total_rows, desc->num_seqs, desc->num_heads,
+                                 desc->io_dtype == KDA_BF16, desc->fuse_chunks);
 }
 
 size_t kda_prefill_workspace_size(const kda_prefill_desc_t *desc) {
@@ -413,6 +420,6 @@ const char *kda_status_string(kda_status_t status) {
     return "unknown status";
 }
 
-int32_t kda_version(void) { return 105; }
+int32_t kda_version(void) { return 106; }
 
 }  // extern "C"

@@ -21,6 +21,7 @@ struct PrefillArgs {
     int64_t slot_stride, head_stride;   // state addressing, fp32 elements (resolved)
     int num_cus;            // compute units of the device (persistent grids)
     int window_chunks = 0;  // chunk ids per window; 0 = the default policy
+    int fuse_chunks = 0;    // fused prefill for sequences of <= this many chunks; 0 = default, < 0 none
     // optional timing events: [0] before the first kernel, then one after
     // each kernel launch (intra and scan of each window in turn)
     const hipEvent_t *events = nullptr;
@@ -39,6 +40,8 @@ struct PrefillPlan {
     size_t dec_offset, carry_offset, bytes;
 };
 PrefillPlan prefill_plan(int T, int N, int H, int dk, int dv, bool bf16, int window_chunks);
+// Most chunks of a sequence the fused prefill takes (-1: none).
+int prefill_fuse_max(int T, int N, int H, bool bf16, int fuse_chunks);
 
 // Most tokens a multi-token decode call may carry per sequence.
 constexpr int kMaxDecodeTokens = 16;

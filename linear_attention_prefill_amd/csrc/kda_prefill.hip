@@ -67,6 +67,9 @@ constexpr int kScanWarmAhead = 2;      // chunks between a scan stage's record a
 #ifndef KDA_SINGLE_CHAIN
 #define KDA_SINGLE_CHAIN 0
 #endif
+#ifndef KDA_FUSE_DEFAULT
+#define KDA_FUSE_DEFAULT(T, N) -1
+#endif
 
 // LDS of the intra-chunk kernel.  For bf16, V is staged as a row-major tile
 // and read back as fragments; for fp32 (twice the bytes) it is read from
@@ -75,13 +78,14 @@ constexpr int kScanWarmAhead = 2;      // chunks between a scan stage's record a
 // waves that would otherwise wait on the first inverse level, K e^Gam as the
 // w product's operand), which keeps their products and stores out of the
 // VALU-bound factor phase and 34 KB out of LDS.
-template <typename E, int DK, int DV> struct IntraLds {
+template <typename E, int DK, int DV, bool FUSED> struct IntraLds {
     static constexpr bool kStage = sizeof(E) == 2;  // V staged in LDS
     // bf16: k P, V and e^{Gam_s} (all the w and u products read from the row
     // factors) in two buffers, alternating by item, so that the next item's
     // factor phase needs no barrier after this item's w and u.  fp32 has no
-    // room for the second k P.
-    static constexpr int NB = sizeof(E) == 2 ? 2 : 1;
+    // room for the second k P, and the fused prefill needs that room for the
+    // chunk operands of its state step (its items end in a barrier anyway).
+    static constexpr int NB = sizeof(E) == 2 && !FUSED ? 2 : 1;
     // Pitches.  A k P / q P row of d_k + 4 elements (4 mod 8) spreads the
     // factor phase's row writes and the fragment reads over the LDS banks:
     // against d_k + 8 (bf16) it stalls a third fewer cycles on bank
@@ -141,15 +145,35 @@ struct ChunkRef {
 // Index p = I (I + 1) / 2 + J of the block pair (I, J), J <= I < 4.
 __device__ __forceinline__ int pair_row(int p) { return p < 1 ? 0 : (p < 3 ? 1 : (p < 6 ? 2 : 3)); }
 
-template <typename E, int DK, int DV>
-__global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
+// The fused prefill's part of a call: chains (sequence, head) of at most
+// fuse_max chunks run whole in one workgroup; the intra-chunk kernel and the
+// scan skip them.  fuse_max < 0: no chain is fused.
+struct FuseArgs {
+    const int32_t *slots;
+    const float *state_in;
+    float *state_out;
+    void *o;
+    int num_slots;
+    float scale;
+    int64_t slot_stride, head_stride;
+    int fuse_max;
+};
+
+// The body of both persistent 8-wave kernels.  FUSED = false: the
+// intra-chunk kernel, which writes each item's record to the workspace.
+// FUSED = true (bf16): the fused prefill, which walks whole chains and keeps
+// the record of the current chunk in LDS, where the state step that follows
+// its intra-chunk phases reads it (no record round trip through memory).
+template <typename E, int DK, int DV, bool FUSED>
+__device__ __forceinline__ void intra_chunks(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu, int T, int N, int H, int c_lo, int c_hi,
-    E *__restrict__ ws, float *__restrict__ ws_dec) {
+    E *__restrict__ ws, float *__restrict__ ws_dec, const FuseArgs &fa) {
     static_assert(DK == 64 || DK == 128, "d_k");
     static_assert(DV == 64 || DV == 128, "d_v");
-    using LD = IntraLds<E, DK, DV>;
+    static_assert(!FUSED || sizeof(E) == 2, "the fused prefill is bf16");
+    using LD = IntraLds<E, DK, DV, FUSED>;
     using L = WsLayout<E, DK, DV>;
     using R4 = typename Raw4<E>::type;
     constexpr int NTH = kIntraThreads;
@@ -176,7 +200,17 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
     __shared__ __align__(16) float sF[10 * DK];        // F_IJ, J <= I, index I(I+1)/2 + J
     __shared__ __align__(16) float sBeta[kChunk];
     __shared__ int sExact[4 * C4];                     // per block and 4-channel column
-    __shared__ int sCu[kCuCache];
+    __shared__ int sCu[FUSED ? 1 : kCuCache];
+    __shared__ int sCum[FUSED ? 1 : kCuCache + 1];     // chunks before each sequence (dense walk)
+    __shared__ int sWsum[4];
+    // fused: the chunk's K~^T and A_qk fragments and e^{Gam_C}; its Q~ and w
+    // fragments take the k Qf rows, which are dead once K~^T is formed
+    __shared__ __align__(16) E sKt[FUSED ? DK * kChunk : 8];
+    __shared__ __align__(16) E sAq[FUSED ? 6 * 512 : 8];
+    __shared__ __align__(16) float sDec[FUSED ? DK : 4];
+    static_assert(!FUSED || 2 * kChunk * DK * sizeof(E) <= sizeof(sKQ), "Q~ and w in the k Qf rows");
+    E *const sQt = reinterpret_cast<E *>(sKQ);         // fused: Q~ fragments
+    E *const sW = sQt + kChunk * DK;                   // fused: w fragments
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
@@ -189,10 +223,39 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
 
     // Sequence bounds: up to 64 in one register (lane i holds cu[i], read
     // back with readlane), else up to kCuCache in LDS, else scalar loads.
-    const bool cu_reg = N < 64, cu_lds = N < kCuCache;
+    const bool cu_reg = N < 64, cu_lds = !FUSED && N < kCuCache;
     const int cu_v = (cu_reg && lane <= N) ? cu[lane] : 0;
     if (!cu_reg && cu_lds)
         for (int i = tid; i <= N; i += NTH) sCu[i] = cu[i];
+    // Dense walk (one window, N < kCuCache): the chunks this kernel runs
+    // (sequences of more than fuse_max chunks) are numbered 0 .. R - 1 in
+    // sequence order and the grid steps over those numbers.  The id walk
+    // below also steps over the gap id each sequence leaves in the closed-form
+    // chunk ids, which idles workgroups when sequences are short (N sequences
+    // of one chunk: every other id is a gap).
+    const bool dense = !FUSED && N < kCuCache && c_lo == 0 && c_hi == T / kChunk + N;
+    if (dense) {
+        int x = 0;
+        if (tid < N) {
+            const int s0 = clamp_row(cu[tid], T), s1 = clamp_row(cu[tid + 1], T);
+            x = s1 > s0 ? (s1 - s0 + kChunk - 1) / kChunk : 0;
+            if (x <= fa.fuse_max) x = 0;
+        }
+        if (tid < kCuCache) {
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int y = __shfl_up(x, d);
+                if (lane >= d) x += y;
+            }
+            if (lane == 63) sWsum[wave] = x;
+        }
+        __syncthreads();
+        if (tid < kCuCache) {
+            for (int w = 0; w < wave; ++w) x += sWsum[w];
+            sCum[tid + 1] = x;
+            if (tid == 0) sCum[0] = 0;
+        }
+    }
     // Tm diag(beta) fragments (m, s), s <= m / 2: lane (i, g) holds row
     // 16 m + i, columns 32 s + kk(g, e), as the w and u products take them.
     // Their right halves for even m are the zero blocks (0, 1) and (2, 3),
@@ -237,7 +300,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
             const int start = clamp_row(cu_at(lo), T), end = clamp_row(cu_at(lo + 1), T);
             const int len = end > start ? end - start : 0;
             const int jc = cid - (start / kChunk + lo);
-            if (jc >= 0 && jc * kChunk < len)
+            if (jc >= 0 && jc * kChunk < len && (len + kChunk - 1) / kChunk > fa.fuse_max)
                 return ChunkRef{cid * H + h, cid, h, start + jc * kChunk, min(kChunk, len - jc * kChunk)};
         }
         return ChunkRef{-1, 0, 0, 0, 0};
@@ -276,8 +339,118 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
         }
     };
 
+    // ---- fused: the walk over chains ----
+    // Chains are the (sequence, head) pairs whose sequence has at most
+    // fuse_max chunks and a live slot.  With fewer than 64 sequences the
+    // fused sequences are ranked longest first (ties by index) and chain c is
+    // head c % H of the (c / H)-th of them; otherwise chain c is pair
+    // (c / H, c % H) and the others are passed over.  Workgroup b takes
+    // chains b, b + G, b + 2G, ...; a chain's state stays in registers (wave
+    // w < d_v / 16 holds value columns 16 w .. 16 w + 15) for all its chunks.
+    struct FChain {
+        int c, n, h, slot, start, len, nch;
+    };
+    int fl_len = -1, fl_rank = 0, nf_seq = 0;
+    if constexpr (FUSED) {
+        if (cu_reg) {
+            const int s0 = clamp_row(cu_v, T), s1 = clamp_row(__shfl_down(cu_v, 1), T);
+            const int len = s1 > s0 ? s1 - s0 : 0;
+            const bool fus = lane < N && (len + kChunk - 1) / kChunk <= fa.fuse_max;
+            fl_len = fus ? len : -1;
+            for (int m = 0; m < N; ++m) {
+                const int lm = __shfl(fl_len, m);
+                fl_rank += (lm > fl_len || (lm == fl_len && m < lane)) ? 1 : 0;
+            }
+            nf_seq = __popcll(__ballot(fus));
+        }
+    }
+    const int chains = cu_reg ? nf_seq * H : N * H;
+    auto resolve = [&](int c) -> FChain {
+        for (; c < chains; c += stride) {
+            const int h = c % H;
+            int n = c / H;
+            if (cu_reg) n = __ffsll((long long)__ballot(fl_len >= 0 && fl_rank == c / H)) - 1;
+            const SeqSpan sp = seq_span(cu, n, T);
+            const int nch = (sp.len + kChunk - 1) / kChunk;
+            if (nch > fa.fuse_max) continue;
+            const int slot = fa.slots ? fa.slots[n] : n;
+            if (fa.slots && (slot < 0 || slot >= fa.num_slots)) continue;
+            return FChain{c, n, h, slot, sp.start, sp.len, nch};
+        }
+        return FChain{-1, 0, 0, 0, 0, 0, 0};
+    };
+    auto state_at = [&](const float *base, const FChain &ch) {
+        return base + ch.slot * fa.slot_stride + ch.h * fa.head_stride + (size_t)(wave * kSub + li) * DK + 4 * lg;
+    };
+    // A chain with no rows passes its state through (zero without state_in).
+    auto pass_state = [&](const FChain &ch) {
+        if (wave >= VT || !fa.state_out) return;
+        float *dst = const_cast<float *>(state_at(fa.state_out, ch));
+        const float *src = fa.state_in ? state_at(fa.state_in, ch) : nullptr;
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+            *reinterpret_cast<f32x4 *>(dst + t * kSub) =
+                src ? *reinterpret_cast<const f32x4 *>(src + t * kSub) : f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto next_chain = [&](int c) -> FChain {   // the first chain at or after c with rows
+        FChain ch = resolve(c);
+        while (ch.c >= 0 && ch.nch == 0) {
+            pass_state(ch);
+            ch = resolve(ch.c + stride);
+        }
+        return ch;
+    };
+    auto item_of = [&](const FChain &ch, int j) -> ChunkRef {
+        if (ch.c < 0) return ChunkRef{-1, 0, 0, 0, 0};
+        const int cid = ch.start / kChunk + ch.n + j;
+        return ChunkRef{cid * H + ch.h, cid, ch.h, ch.start + j * kChunk, min(kChunk, ch.len - j * kChunk)};
+    };
+    // key tile t of this wave's state slice, C layout: S[16t + 4g + r][16 wave + i]
+    f32x4 S[FUSED ? KT : 1];
+    auto state_load = [&](const FChain &ch) {
+        if (wave >= VT) return;
+        const float *src = fa.state_in ? state_at(fa.state_in, ch) : nullptr;
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+            S[t] = src ? *reinterpret_cast<const f32x4 *>(src + t * kSub) : f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto state_store = [&](const FChain &ch) {
+        if (wave >= VT || !fa.state_out) return;
+        float *dst = const_cast<float *>(state_at(fa.state_out, ch));
+#pragma unroll
+        for (int t = 0; t < KT; ++t) *reinterpret_cast<f32x4 *>(dst + t * kSub) = S[t];
+    };
+    bf16x4 ureg[4];                                    // fused: this wave's u tile, row tile m
+
+    // dense walk: real item r = k H + h (k-th chunk run here, head h), taken
+    // from the last one down in steps of the grid
+    auto find_real = [&](int r) -> ChunkRef {
+        if (r < 0) return ChunkRef{-1, 0, 0, 0, 0};
+        const int kc = r / H, h = r - kc * H;
+        int lo = 0, hi = N - 1;                        // the last sequence with sCum <= kc
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sCum[mid] <= kc) lo = mid; else hi = mid - 1;
+        }
+        const int start = clamp_row(cu_at(lo), T), end = clamp_row(cu_at(lo + 1), T);
+        const int len = end > start ? end - start : 0;
+        const int jc = kc - sCum[lo];
+        const int cid = start / kChunk + lo + jc;
+        return ChunkRef{cid * H + h, cid, h, start + jc * kChunk, min(kChunk, len - jc * kChunk)};
+    };
+    const int real_items = dense ? __builtin_amdgcn_readfirstlane(sCum[N]) * H : 0;
+    int rcur = real_items - 1 - (int)blockIdx.x;
+
     ChunkRef cur;
-    {
+    FChain ch{-1, 0, 0, 0, 0, 0, 0};
+    int jcur = 0;
+    if constexpr (FUSED) {
+        ch = next_chain((int)blockIdx.x);
+        cur = item_of(ch, 0);
+        if (ch.c >= 0) state_load(ch);
+    } else if (dense) {
+        cur = find_real(rcur);
+    } else {
         const int item0 = c_hi * H - 1 - (int)blockIdx.x;
         cur = find_chunk(item0 / H, item0 % H);
     }
@@ -304,14 +477,31 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
         float *const sBs = sBsb + buf * (4 * DK);
         const int C = cur.C;
         const size_t rec = (size_t)(cur.item - c_lo * H);   // = (cid - c_lo) H + h
-        E *const Rw = ws + rec * L::kRecElems;
-        E *const Rq = Rw + L::kWElems;
-        E *const Rk = Rq + L::kQElems;
-        E *const Ra = Rk + L::kKElems;
+        E *const Rw = FUSED ? sW : ws + rec * L::kRecElems;
+        E *const Rq = FUSED ? sQt : Rw + L::kWElems;
+        E *const Rk = FUSED ? sKt : Rq + L::kQElems;
+        E *const Ra = FUSED ? sAq : Rk + L::kKElems;
         E *const Ru = Ra + L::kAElems;
-        int ncid = cur.cid, nh = cur.h;
-        step_down(ncid, nh);
-        const ChunkRef nxt = find_chunk(ncid, nh);
+        float *const Rd = FUSED ? sDec : ws_dec + rec * DK;
+        FChain nch_ch = ch;
+        int nj = jcur + 1;
+        const ChunkRef nxt = [&]() -> ChunkRef {
+            if constexpr (FUSED) {
+                if (nj >= ch.nch) {
+                    nch_ch = next_chain(ch.c + stride);
+                    nj = 0;
+                }
+                return item_of(nch_ch, nj);
+            } else {
+                if (dense) {
+                    rcur -= stride;
+                    return find_real(rcur);
+                }
+                int ncid = cur.cid, nh = cur.h;
+                step_down(ncid, nh);
+                return find_chunk(ncid, nh);
+            }
+        }();
 
         // ---- per-row factors (log2 units); everything derived from k, q, V
         // leaves the registers ----
@@ -381,7 +571,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
                 f32x4 d;
 #pragma unroll
                 for (int x = 0; x < 4; ++x) d[x] = fast_exp2(total[x]);
-                *reinterpret_cast<f32x4 *>(ws_dec + rec * DK + ch0) = d;
+                *reinterpret_cast<f32x4 *>(Rd + ch0) = d;
             }
         }
         if constexpr (LD::kStage) {
@@ -547,19 +737,38 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
         load_row(nxt, 1);
         __syncthreads();   // sA holds A_kk below the diagonal and the diagonal inverses
 
+        // Q e^Gam = (q P) e^{Gam_s} in the scan's fragment order: fragment
+        // (m, s) holds row 16m + i, channels 32s + kk(g, e).
+        auto form_q = [&](int f) {
+            const int row = (f / KS) * kSub + li, c0 = (f % KS) * kSlab + 4 * lg;
+            Frag<E> fr = frag_from_runs<E>(sQP + row * KPP + c0, sQP + row * KPP + c0 + 16);
+            const float *eb = sBs + (f / KS) * DK + c0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) fr.set(e, fr.get(e) * eb[(e & 3) + 16 * (e >> 2)]);
+            store_frag<E>(Rq + f * 512, lane, fr);
+        };
+        // K e^{Gam_C - Gam}, transposed, in the scan's order: fragment (t, s)
+        // holds key channels 16t + i over chunk rows 32s + kk(g, e).
+        auto form_k = [&](int f) {
+            const int ch = (f >> 1) * kSub + li;
+            const float ce0 = sCe[(2 * (f & 1)) * DK + ch], ce1 = sCe[(2 * (f & 1) + 1) * DK + ch];
+            Frag<E> fr;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int row = (f & 1) * kSlab + kk_of(lg, e);
+                fr.set(e, sKQ[row * KQP + ch] * (e < 4 ? ce0 : ce1));
+            }
+            store_frag<E>(Rk + f * 512, lane, fr);
+        };
         // ---- off-diagonal blocks of Tm on fp32 matrix cores ----
         // level 1 (waves 0, 1), in place: Tm_10 = -Tm_11 (A_10 Tm_00), Tm_32 = -Tm_33 (A_32 Tm_22).
-        // Meanwhile waves 2..7 write Q e^Gam = (q P) e^{Gam_s} in the scan's
-        // fragment order: fragment (m, s) holds row 16m + i, channels
-        // 32s + kk(g, e).
+        // Meanwhile waves 2..7 write Q e^Gam, or, fused, K e^{Gam_C - Gam}
+        // (its k Qf rows then take Q e^Gam and w).
         if (wave >= 2) {
-            for (int f = wave - 2; f < 4 * KS; f += 6) {
-                const int row = (f / KS) * kSub + li, c0 = (f % KS) * kSlab + 4 * lg;
-                Frag<E> fr = frag_from_runs<E>(sQP + row * KPP + c0, sQP + row * KPP + c0 + 16);
-                const float *eb = sBs + (f / KS) * DK + c0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) fr.set(e, fr.get(e) * eb[(e & 3) + 16 * (e >> 2)]);
-                store_frag<E>(Rq + f * 512, lane, fr);
+            if constexpr (FUSED) {
+                for (int f = wave - 2; f < 2 * KT; f += 6) form_k(f);
+            } else {
+                for (int f = wave - 2; f < 4 * KS; f += 6) form_q(f);
             }
         }
         if (wave < 2) {
@@ -593,20 +802,12 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
         __syncthreads();
         // level 2 (waves 0..3, output tile (ti, tj)), straight into the Tm
         // diag(beta) fragments (2 + ti, 0): Tm[32:64, 0:32] = -Tm_hi (A[32:64, 0:32] Tm_lo).
-        // Meanwhile waves 4..7 write K e^{Gam_C - Gam}, transposed, in the
-        // scan's order: fragment (t, s) holds key channels 16t + i over chunk
-        // rows 32s + kk(g, e).
+        // Meanwhile waves 4..7 write K e^{Gam_C - Gam}, or, fused, Q e^Gam.
         if (wave >= 4) {
-            for (int f = wave - 4; f < 2 * KT; f += 4) {
-                const int ch = (f >> 1) * kSub + li;
-                const float ce0 = sCe[(2 * (f & 1)) * DK + ch], ce1 = sCe[(2 * (f & 1) + 1) * DK + ch];
-                Frag<E> fr;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int row = (f & 1) * kSlab + kk_of(lg, e);
-                    fr.set(e, sKQ[row * KQP + ch] * (e < 4 ? ce0 : ce1));
-                }
-                store_frag<E>(Rk + f * 512, lane, fr);
+            if constexpr (FUSED) {
+                for (int f = wave - 4; f < 4 * KS; f += 4) form_q(f);
+            } else {
+                for (int f = wave - 4; f < 2 * KT; f += 4) form_k(f);
             }
         }
         if (wave < 4) {
@@ -667,7 +868,11 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 mma(acc, tm_frag(m, 0), vf[0]);
                 if (m >= 2) mma(acc, tm_frag(m, 1), vf[1]);
-                store4<E>(Ru + wave * (64 * 16) + m * 256 + lane * 4, acc);
+                if constexpr (FUSED) {
+                    ureg[m] = bf16x4{(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+                } else {
+                    store4<E>(Ru + wave * (64 * 16) + m * 256 + lane * 4, acc);
+                }
             }
         }
         {
@@ -706,9 +911,78 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
         // w and u no longer read, and its first barrier orders everything
         // after it behind this chunk's w and u.
         if constexpr (LD::NB == 1) __syncthreads();
+        if constexpr (FUSED) {
+            // ---- the chunk's state step, wave w < d_v / 16 on its slice:
+            // U = u - w S, O = Q~ S + A_qk U, S = diag(e^{Gam_C}) S + K~^T U,
+            // all operands from LDS but u (this wave's registers) ----
+            if (wave < VT) {
+                Frag<E> SB[KS];
+#pragma unroll
+                for (int s = 0; s < KS; ++s) SB[s] = frag_from_tiles<E>(S[2 * s], S[2 * s + 1]);
+                // row tile m of U: lane holds U[16m + 4g + r][16 wave + i]
+                f32x4 U[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) U[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) mma(U[m], load_frag<E>(sW + (m * KS + s) * 512, lane), SB[s]);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) U[m] = raw_to_f32(ureg[m]) - U[m];
+                Frag<E> UB[2];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) UB[s] = frag_from_tiles<E>(U[2 * s], U[2 * s + 1]);
+                // O, transposed: lane holds row 16m + i, columns 16 wave + 4g + r
+                f32x4 O[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    O[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) mma(O[m], SB[s], load_frag<E>(sQt + (m * KS + s) * 512, lane));
+#pragma unroll
+                    for (int s = 0; s <= (m >> 1); ++s)
+                        mma(O[m], UB[s], load_frag<E>(sAq + tri_frag(m, s) * 512, lane));
+                }
+#pragma unroll
+                for (int t = 0; t < KT; ++t) {
+                    S[t] *= *reinterpret_cast<const f32x4 *>(sDec + t * kSub + 4 * lg);
+                    mma(S[t], load_frag<E>(sKt + (2 * t) * 512, lane), UB[0]);
+                    mma(S[t], load_frag<E>(sKt + (2 * t + 1) * 512, lane), UB[1]);
+                }
+                E *const orow = static_cast<E *>(fa.o) + ((size_t)(cur.row0 + li) * H + cur.h) * DV +
+                                wave * kSub + 4 * lg;
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    if (m * kSub + li < C) store4<E>(orow + (size_t)m * kSub * H * DV, O[m] * fa.scale);
+            }
+            __syncthreads();   // the next chunk's factor phase rewrites every operand
+            if (nj == 0) {     // the chain is done: its state out, the next chain's in
+                state_store(ch);
+                ch = nch_ch;
+                if (ch.c >= 0) state_load(ch);
+            }
+            jcur = nj;
+        }
         buf ^= LD::NB - 1;
         cur = nxt;
     }
+}
+
+template <typename E, int DK, int DV>
+__global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta,
+    const int32_t *__restrict__ cu, int T, int N, int H, int c_lo, int c_hi,
+    E *__restrict__ ws, float *__restrict__ ws_dec, FuseArgs fa) {
+    intra_chunks<E, DK, DV, false>(q, k, v, g, beta, cu, T, N, H, c_lo, c_hi, ws, ws_dec, fa);
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kIntraThreads, 1) void kda_fused_prefill_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta,
+    const int32_t *__restrict__ cu, int T, int N, int H, FuseArgs fa) {
+    intra_chunks<bf16, DK, DV, true>(q, k, v, g, beta, cu, T, N, H, 0, 0, nullptr, nullptr, fa);
 }
 
 // ---------------------------------------------------------------------------
@@ -770,7 +1044,7 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
     const int32_t *__restrict__ cu, const int32_t *__restrict__ slots,
     const float *state_in, float *state_out, E *__restrict__ o,
     int T, int N, int H, int num_slots, float scale, int64_t slot_stride, int64_t head_stride,
-    int c_lo, int c_hi, float *__restrict__ carry) {
+    int c_lo, int c_hi, float *__restrict__ carry, int fuse_max) {
     constexpr int VT = DV / kSub, KS = DK / kSlab;
     constexpr int TPW = DK / 64;                       // key tiles per wave
     using L = WsLayout<E, DK, DV>;
@@ -810,6 +1084,7 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
     // sequence with no rows is passed through by the window that holds its
     // (empty) first chunk id.
     const int nch_all = (sp.len + kChunk - 1) / kChunk;
+    if (nch_all <= fuse_max) return;                   // a fused chain
     const int j_lo = max(0, c_lo - sp.first_chunk);
     const int j_hi = min(nch_all, c_hi - sp.first_chunk);
     if (nch_all == 0 ? (sp.first_chunk < c_lo || sp.first_chunk >= c_hi) : j_lo >= j_hi) return;
@@ -1049,6 +1324,9 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
 template <typename E, int DK, int DV>
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     const PrefillPlan pl = prefill_plan(a.T, a.N, a.H, DK, DV, sizeof(E) == 2, a.window_chunks);
+    const FuseArgs fa{a.slots, a.state_in, a.state_out, a.o, a.num_slots, a.scale,
+                      a.slot_stride, a.head_stride,
+                      prefill_fuse_max(a.T, a.N, a.H, sizeof(E) == 2, a.fuse_chunks)};
     char *const base = reinterpret_cast<char *>(a.workspace);
     E *const ws = reinterpret_cast<E *>(base);
     float *const ws_dec = reinterpret_cast<float *>(base + pl.dec_offset);
@@ -1070,7 +1348,8 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
         constexpr int NS = decltype(ns)::value;
         kda_scan_kernel<E, DK, DV, NS><<<dim3((int)(slices / NS)), dim3(256), 0, stream>>>(
             ws, ws_dec, a.cu_seqlens, a.slots, a.state_in, a.state_out, static_cast<E *>(a.o),
-            a.T, a.N, a.H, a.num_slots, a.scale, a.slot_stride, a.head_stride, c_lo, c_hi, carry);
+            a.T, a.N, a.H, a.num_slots, a.scale, a.slot_stride, a.head_stride, c_lo, c_hi, carry,
+            fa.fuse_max);
         return hipGetLastError();
     };
     auto scan_window = [&](int c_lo, int c_hi) -> hipError_t {
@@ -1091,7 +1370,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
         const int grid = (int)(items < (long long)a.num_cus ? items : (long long)a.num_cus);
         kda_intra_kernel<E, DK, DV><<<dim3(grid), dim3(kIntraThreads), 0, stream>>>(
             static_cast<const E *>(a.q), static_cast<const E *>(a.k), static_cast<const E *>(a.v),
-            a.g, a.beta, a.cu_seqlens, a.T, a.N, a.H, c_lo, c_hi, ws, ws_dec);
+            a.g, a.beta, a.cu_seqlens, a.T, a.N, a.H, c_lo, c_hi, ws, ws_dec, fa);
         // A failed intra launch leaves stale records: the scan must not run
         // on them and overwrite o and the caller's states.
         hipError_t e = hipGetLastError();
@@ -1100,6 +1379,18 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
         e = scan_window(c_lo, c_hi);
         if (e != hipSuccess) return e;
         mark();
+    }
+    if constexpr (sizeof(E) == 2) {
+        if (fa.fuse_max >= 0) {
+            const long long chains = (long long)a.N * a.H;
+            const int grid = (int)(chains < (long long)a.num_cus ? chains : (long long)a.num_cus);
+            kda_fused_prefill_kernel<DK, DV><<<dim3(grid), dim3(kIntraThreads), 0, stream>>>(
+                static_cast<const E *>(a.q), static_cast<const E *>(a.k), static_cast<const E *>(a.v),
+                a.g, a.beta, a.cu_seqlens, a.T, a.N, a.H, fa);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            mark();
+        }
     }
     return hipSuccess;
 }
@@ -1172,6 +1463,13 @@ PrefillPlan prefill_plan(int T, int N, int H, int dk, int dv, bool bf16, int win
     const size_t carry = p.windows > 1 ? (size_t)N * H * dv * dk * 4 : 0;
     p.bytes = p.carry_offset + carry;
     return p;
+}
+
+int prefill_fuse_max(int T, int N, int H, bool bf16, int fuse_chunks) {
+    (void)H;
+    if (!bf16 || fuse_chunks < 0) return -1;
+    if (fuse_chunks > 0) return fuse_chunks;
+    return KDA_FUSE_DEFAULT(T, N);
 }
 
 size_t prefill_workspace_bytes(int T, int N, int H, int dk, int dv, bool bf16, int window_chunks) {

@@ -33,7 +33,7 @@ class PrefillDesc(ctypes.Structure):
                 ("num_slots", ctypes.c_int32), ("io_dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("state_slot_stride", ctypes.c_int64),
                 ("state_head_stride", ctypes.c_int64), ("conv_mode", ctypes.c_int32),
-                ("window_chunks", ctypes.c_int32)]
+                ("window_chunks", ctypes.c_int32), ("fuse_chunks", ctypes.c_int32)]
 
 
 class ConvDesc(ctypes.Structure):
@@ -80,6 +80,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                            vp, sz, vp, ctypes.POINTER(ctypes.c_void_p), i32]
     lib.kda_prefill_windows.restype = i32
     lib.kda_prefill_windows.argtypes = [ctypes.POINTER(PrefillDesc)]
+    lib.kda_prefill_fuse_chunks.restype = i32
+    lib.kda_prefill_fuse_chunks.argtypes = [ctypes.POINTER(PrefillDesc)]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp,
                                     i32, i32, i32, i32, i32, i32, f32, vp]
@@ -179,10 +181,10 @@ def check_prefill_inputs(g, cu_seqlens, slots=None, num_slots=None, stream=None)
 
 
 def make_desc(T, N, H, d_k, d_v, num_slots, io_dtype, scale=1.0, slot_stride=0,
-              head_stride=0, conv_mode=0, window_chunks=0) -> PrefillDesc:
+              head_stride=0, conv_mode=0, window_chunks=0, fuse_chunks=0) -> PrefillDesc:
     return PrefillDesc(int(T), int(N), int(H), int(d_k), int(d_v), int(num_slots),
                        int(io_dtype), float(scale), int(slot_stride), int(head_stride),
-                       int(conv_mode), int(window_chunks))
+                       int(conv_mode), int(window_chunks), int(fuse_chunks))
 
 
 def conv_extent(num_slots, H, d_k, d_v, strides) -> int:
@@ -251,6 +253,14 @@ def prefill_windows(T, N, H, d_k, d_v, dtype=torch.bfloat16, window_chunks=0) ->
     return int(load_library().kda_prefill_windows(ctypes.byref(d)))
 
 
+def prefill_fuse_chunks(T, N, H, d_k, d_v, dtype=torch.bfloat16, fuse_chunks=0) -> int:
+    """Most chunks of a sequence that a prefill call of these sizes runs in
+    the fused prefill (``kda_prefill_fuse_chunks``; -1: none).  When it is
+    not negative the fused kernel runs after the windows."""
+    d = make_desc(T, N, H, d_k, d_v, N, _io_code(dtype), fuse_chunks=fuse_chunks)
+    return int(load_library().kda_prefill_fuse_chunks(ctypes.byref(d)))
+
+
 def prefill_workspace_size(T, N, H, d_k, d_v, dtype=torch.bfloat16, conv=False,
                            window_chunks=0) -> int:
     d = make_desc(T, N, H, d_k, d_v, N, _io_code(dtype), conv_mode=1 if conv else 0,
@@ -262,7 +272,7 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
                   slots=None, num_slots=None, scale=1.0, workspace=None, stream=None,
                   events=None, state_slot_stride=0, state_head_stride=0, conv_weight=None,
                   conv_window=None, conv_activation="none", conv_strides=(0, 0, 0, 0),
-                  check_inputs=False, window_chunks=0):
+                  check_inputs=False, window_chunks=0, fuse_chunks=0):
     """KDA chunked prefill over packed sequences (see ``kda_chunk_prefill``).
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype); g: [T, H, d_k]
@@ -277,14 +287,17 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
     end (``kda_chunk_prefill_conv``); the window is updated in place.
     events: optional list of recorded torch.cuda.Event(enable_timing=True)
     objects: the first is recorded before the first kernel and the i-th after
-    the i-th kernel launch (intra and scan of each window in turn; 2 W + 1
-    events for W = prefill_windows(...) windows; ``kda_chunk_prefill_timed``).  check_inputs: first run the opt-in check
+    the i-th kernel launch (intra and scan of each window in turn, then the
+    fused prefill when prefill_fuse_chunks(...) >= 0; 2 W + 1 or 2 W + 2
+    events for W = prefill_windows(...) windows; ``kda_chunk_prefill_timed``).
+    check_inputs: first run the opt-in check
     of the device data (``kda_prefill_check``, which synchronises) and raise
     ValueError if it fails.  Tensors the call allocates (o when None, the
     workspace when None) come from the launch stream's memory pool.
     window_chunks: chunk ids per window (kda.h, kda_prefill_windows); 0 lets
-    the library choose.  Returns
-    o [T, H, d_v].
+    the library choose.  fuse_chunks: bf16 sequences of at most this many
+    chunks run in the fused prefill (kda.h, kda_prefill_fuse_chunks); 0 lets
+    the library choose, a negative value fuses none.  Returns o [T, H, d_v].
     """
     lib = load_library()
     _dev(q, "q")
@@ -320,7 +333,8 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
     if conv_weight is not None:
         conv = _conv_desc(conv_weight, conv_window, H, dk, dv, q.dtype, conv_strides, num_slots)
     desc = make_desc(T, N, H, dk, dv, num_slots, io, scale, state_slot_stride, state_head_stride,
-                     _conv_mode(conv_activation) if conv is not None else 0, window_chunks)
+                     _conv_mode(conv_activation) if conv is not None else 0, window_chunks,
+                     fuse_chunks)
     need = int(lib.kda_prefill_workspace_size(ctypes.byref(desc)))
     if workspace is None:
         # Allocated from the launch stream's pool: when it is freed on return
@@ -348,7 +362,8 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, state_in=None, state_out=None, o
 
 def chunk_prefill_no_alloc(q, k, v, g, beta, cu_seqlens, o, state_in=None, state_out=None,
                            slots=None, num_slots=None, scale=1.0, stream=None,
-                           state_slot_stride=0, state_head_stride=0, window_chunks=0):
+                           state_slot_stride=0, state_head_stride=0, window_chunks=0,
+                           fuse_chunks=0):
     """chunk_prefill through ``kda_chunk_prefill_static``, for callers that
     cannot allocate: o is required, no workspace is passed and nothing is
     allocated, here or in the library (its workspace is a static device array
@@ -379,7 +394,7 @@ def chunk_prefill_no_alloc(q, k, v, g, beta, cu_seqlens, o, state_in=None, state
         raise ValueError("o is required: this entry point allocates nothing")
     _dev(o, "o", q.dtype, (T, H, dv))
     desc = make_desc(T, N, H, dk, dv, num_slots, io, scale, state_slot_stride, state_head_stride,
-                     window_chunks=window_chunks)
+                     window_chunks=window_chunks, fuse_chunks=fuse_chunks)
     _check(lib.kda_chunk_prefill_static(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                         _ptr(cu_seqlens), _ptr(state_in), _ptr(state_out),
                                         _ptr(o), _ptr(slots), ctypes.byref(desc),

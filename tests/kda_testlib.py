@@ -51,7 +51,7 @@ def rel_err(x, ref):
 
 
 def gpu_prefill(case, pool=None, o_init=None, in_place=True, state_in_null=False,
-                state_out_null=False, num_slots=None, stream=None):
+                state_out_null=False, num_slots=None, stream=None, fuse_chunks=0):
     """Run kda_chunk_prefill on a workloads.Case.  Returns (o f32 numpy,
     state_out numpy or None)."""
     dt = torch_dtype(case.io_dtype)
@@ -73,7 +73,7 @@ def gpu_prefill(case, pool=None, o_init=None, in_place=True, state_in_null=False
     else:
         o = dev(o_init, dt)
     lap.chunk_prefill(q, k, v, g, beta, cu, state_in=pin, state_out=pout, o=o, slots=slots,
-                      num_slots=num_slots, scale=case.scale, stream=stream)
+                      num_slots=num_slots, scale=case.scale, stream=stream, fuse_chunks=fuse_chunks)
     torch.cuda.synchronize()
     return (o.float().cpu().numpy(),
             None if pout is None else pout.cpu().numpy())

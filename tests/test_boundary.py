@@ -48,7 +48,7 @@ def test_header_declares_expected_entry_points():
               "kda_status_string", "kda_version", "kda_chunk_prefill_timed",
               "kda_decode_step_lines", "kda_decode_tokens", "kda_chunk_prefill_conv",
               "kda_decode_step_conv", "kda_prefill_check", "kda_chunk_prefill_static",
-              "kda_prefill_windows"):
+              "kda_prefill_windows", "kda_prefill_fuse_chunks"):
         assert n in names
 
 
@@ -58,7 +58,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 105
+    assert lib.kda_version() == 106
     for code in range(9):
         s = lib.kda_status_string(code).decode()
         assert s and s != "unknown status"
@@ -71,6 +71,22 @@ def _desc(**kw):
     d.update(kw)
     return K.make_desc(d["T"], d["N"], d["H"], d["dk"], d["dv"], d["slots"], d["io"], d["scale"],
                        d["ss"], d["hs"], d["conv"])
+
+
+def test_fuse_chunks_policy(lib):
+    """kda_prefill_fuse_chunks: a positive request is taken as is for bf16, a
+    negative one fuses nothing, fp32 never fuses, an invalid desc gives -1."""
+    def f(fc, io=K.KDA_BF16, **kw):
+        d = dict(T=8192, N=16, H=32, dk=128, dv=128, slots=64)
+        d.update(kw)
+        desc = K.make_desc(d["T"], d["N"], d["H"], d["dk"], d["dv"], d["slots"], io,
+                           fuse_chunks=fc)
+        return lib.kda_prefill_fuse_chunks(ctypes.byref(desc))
+    assert f(5) == 5 and f(64) == 64
+    assert f(-1) == -1 and f(-7) == -1
+    assert f(5, io=K.KDA_F32) == -1 and f(0, io=K.KDA_F32) == -1
+    assert f(3, dk=96) == -1
+    assert lib.kda_prefill_fuse_chunks(None) == -1
 
 
 def _ws_formula(T, N, H, dk, dv, es):

@@ -71,7 +71,7 @@ def _kernels():
 
 def test_every_kernel_is_present():
     names = " ".join(k["name"] for k in _kernels())
-    for kern in ("kda_intra_kernel", "kda_scan_kernel", "kda_decode_kernel",
+    for kern in ("kda_intra_kernel", "kda_fused_prefill_kernel", "kda_scan_kernel", "kda_decode_kernel",
                  "kda_decode_tokens_kernel", "kda_decode_conv_kernel", "kda_conv_kernel",
                  "kda_conv_window_kernel"):
         assert kern in names, kern

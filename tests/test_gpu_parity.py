@@ -386,7 +386,7 @@ def test_many_pairs_ragged(dk, dv):
     slots[9] = -1
     c = W.random_case(430 + dk + dv, lengths, H=4, d_k=dk, d_v=dv, io_dtype="bf16",
                       num_slots=80, slots=slots)
-    assert _scan_slices_per_workgroup(c.N * c.H * (dv // 16), dv) == (4 if dv == 128 else 2)
+    assert _scan_slices_per_workgroup(c.N * c.H * (dv // 16), dv) == 4
     announce("many pairs %s" % c.name)
     o_g, _, _, _, _ = _check_case(c)
     cu = c.cu_seqlens
@@ -602,3 +602,88 @@ def test_windows_full_size(workload, window_chunks):
         outs.append((o, pool))
     assert lap.prefill_windows(c.T, c.N, c.H, c.d_k, c.d_v, dt, window_chunks=window_chunks) == 4
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+# ---------------------------------------------------------------------------
+# The fused prefill: whole (sequence, head) chains in one workgroup
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,dk,dv", [(20, 128, 128), (70, 128, 128), (20, 64, 64), (70, 64, 128),
+                                     (20, 128, 64)])
+def test_fused_and_windowed_chains_in_one_call(n, dk, dv):
+    """fuse_chunks = 3: sequences of at most three chunks run in the fused
+    prefill, longer ones in the intra-chunk kernel and scan, in the same
+    call.  Fewer than 64 sequences take the ranked chain order, more the
+    natural one; empty and one-row sequences, a padded slot and a pool
+    updated in place included."""
+    rng = np.random.default_rng(800 + n + dk + dv)
+    lengths = [int(x) for x in rng.choice([0, 1, 5, 64, 65, 130, 192, 193, 300, 700], size=n)]
+    slots = [int(s) for s in rng.permutation(n + 10)[:n]]
+    slots[3] = -1
+    c = W.random_case(810 + n + dk + dv, lengths, H=3, d_k=dk, d_v=dv, io_dtype="bf16",
+                      num_slots=n + 10, slots=slots)
+    assert lap.prefill_fuse_chunks(c.T, c.N, c.H, dk, dv, torch.bfloat16, fuse_chunks=3) == 3
+    o_g, _, _, _, _ = _check_case(c, fuse_chunks=3)
+    cu = c.cu_seqlens
+    assert np.all(o_g[cu[3]:cu[4]] == 3.0)             # the padded sequence keeps its rows
+
+
+@pytest.mark.parametrize("state", ["in_place", "null_in", "null_out"])
+def test_fused_state_handling(state):
+    """Every chain fused: states read from and written to the pool (in
+    place), started from zero (state_in NULL, empty sequences then write
+    zeros), or not written (state_out NULL)."""
+    c = W.random_case(830, [0, 1, 64, 65, 100, 0, 129, 17], H=4, d_k=128, d_v=128,
+                      io_dtype="bf16", num_slots=12)
+    kw = {"state_in_null": state == "null_in", "state_out_null": state == "null_out"}
+    o_init = np.full((c.T, c.H, c.d_v), 3.0, dtype=np.float32)
+    announce("fused prefill %s (%s)" % (c.name, state))
+    o_g, pool_g = gpu_prefill(c, o_init=o_init, fuse_chunks=64, **kw)
+    pool = c.state_pool if state != "null_in" else np.zeros_like(c.state_pool)
+    o_r, pool_r, _ = oracle_prefill(c, pool=pool, o_init=o_init)
+    if state == "null_out":
+        pool_g = pool_r = None
+    eo, es = per_sequence_errors(c, o_g, o_r, pool_g, pool_r)
+    announce("  max relative error: o %.3g, state %.3g" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_fused_full_packed_chunk():
+    """The full packed chunk (16 sequences in 8192 rows, H = 32, d = 128)
+    with every chain fused, against the oracle, and the same call with none
+    fused."""
+    c = W.packed_varlen_prefill()
+    assert lap.prefill_fuse_chunks(c.T, c.N, c.H, 128, 128, torch.bfloat16, fuse_chunks=64) == 64
+    _check_case(c, fuse_chunks=64)
+    _check_case(c, fuse_chunks=-1)
+
+
+def test_fused_with_windows_matches_one_window():
+    """Windows apply to the chains that are not fused: a call with fused short
+    chains and windows of two chunk ids gives the bits of the same call in
+    one window."""
+    lengths = [3, 700, 64, 0, 500, 129, 1, 900]
+    c = W.random_case(840, lengths, H=2, d_k=128, d_v=128, io_dtype="bf16", num_slots=8)
+    dt = torch.bfloat16
+    outs = []
+    for wc in (0, 2):
+        pool = dev(c.state_pool)
+        o = torch.full((c.T, c.H, c.d_v), 3.0, dtype=dt, device="cuda")
+        announce("prefill %s window_chunks=%d fuse_chunks=3" % (c.name, wc))
+        lap.chunk_prefill(dev(c.q, dt), dev(c.k, dt), dev(c.v, dt), dev(c.g), dev(c.beta),
+                          dev(c.cu_seqlens), state_in=pool, state_out=pool, o=o,
+                          slots=dev(c.slots), window_chunks=wc, fuse_chunks=3)
+        torch.cuda.synchronize()
+        outs.append((o, pool))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    o_r, pool_r, _ = oracle_prefill(c, o_init=np.full((c.T, c.H, c.d_v), 3.0))
+    eo, es = per_sequence_errors(c, outs[1][0].float().cpu().numpy(), o_r,
+                                 outs[1][1].cpu().numpy(), pool_r)
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_fused_is_bf16_only():
+    """fp32 calls never fuse: the fused kernel keeps bf16 operands."""
+    assert lap.prefill_fuse_chunks(1000, 10, 2, 64, 64, torch.float32, fuse_chunks=5) == -1
+    c = W.random_case(850, [10, 70, 0, 130], H=2, d_k=64, d_v=64, io_dtype="f32")
+    _check_case(c, fuse_chunks=5)
