@@ -148,11 +148,12 @@ typedef struct {
 
 /*
  * Number of windows of chunk ids a prefill call with `desc` runs as (0 if
- * desc is invalid): each window is an intra-chunk kernel that writes the
- * records of its chunks into the workspace and a state scan that consumes
- * them, so the workspace holds one window's records (the prhub report on
- * SGLang PR #32890, section "实现拆解", splits the prefill into the same two
- * stages).
+ * desc is invalid, or if every sequence runs in the fused prefill because
+ * kda_prefill_fuse_chunks(desc) * 64 >= total_rows): each window is an
+ * intra-chunk kernel that writes the records of its chunks into the
+ * workspace and a state scan that consumes them, so the workspace holds one
+ * window's records (the prhub report on SGLang PR #32890, section "实现拆解",
+ * splits the prefill into the same two stages).
  */
 int32_t kda_prefill_windows(const kda_prefill_desc_t *desc);
 
@@ -168,7 +169,9 @@ int32_t kda_prefill_windows(const kda_prefill_desc_t *desc);
  * for many short sequences and not for long ones.  Returns F for `desc`
  * (-1: no sequence is fused, or desc is invalid): desc->fuse_chunks when it
  * is positive, none when it is negative, else the library's choice from the
- * sizes alone.
+ * sizes alone: 8 when total_rows <= 64 num_seqs, 4 when total_rows <=
+ * 128 num_seqs, none otherwise.  Results agree with the unfused path to the
+ * usual bf16 rounding (the same operands, summed in another order).
  */
 int32_t kda_prefill_fuse_chunks(const kda_prefill_desc_t *desc);
 
@@ -200,6 +203,8 @@ size_t kda_prefill_workspace_size(const kda_prefill_desc_t *desc);
  *     sequence copies its state through.
  *   - otherwise the sequence is a padded row: its o rows and every state slot
  *     are left untouched.
+ * bf16 sequences of at most kda_prefill_fuse_chunks(desc) chunks run in the
+ * fused prefill, the others in the windows of intra-chunk kernel and scan.
  * Slots not named by any live sequence are never read or written.
  *
  * The state pools are addressed by lines as described above (dense when the

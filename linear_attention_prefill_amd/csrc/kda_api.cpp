@@ -259,6 +259,9 @@ extern "C" {
 
 int32_t kda_prefill_windows(const kda_prefill_desc_t *desc) {
     if (check_desc(desc) != KDA_OK) return 0;
+    const int fm = kda::prefill_fuse_max(desc->total_rows, desc->num_seqs, desc->num_heads,
+                                         desc->io_dtype == KDA_BF16, desc->fuse_chunks);
+    if (fm >= 0 && (long long)fm * 64 >= desc->total_rows) return 0;   // every sequence fused
     return kda::prefill_plan(desc->total_rows, desc->num_seqs, desc->num_heads, desc->d_k,
                              desc->d_v, desc->io_dtype == KDA_BF16, desc->window_chunks).windows;
 }

@@ -67,9 +67,6 @@ constexpr int kScanWarmAhead = 2;      // chunks between a scan stage's record a
 #ifndef KDA_SINGLE_CHAIN
 #define KDA_SINGLE_CHAIN 0
 #endif
-#ifndef KDA_FUSE_DEFAULT
-#define KDA_FUSE_DEFAULT(T, N) -1
-#endif
 
 // LDS of the intra-chunk kernel.  For bf16, V is staged as a row-major tile
 // and read back as fragments; for fp32 (twice the bytes) it is read from
@@ -1363,7 +1360,10 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     // a scan launch that reads them while they are recent (the workspace
     // holds one window's records and is reused by the next).
     mark();
-    for (int w = 0; w < pl.windows; ++w) {
+    // No sequence has more than T rows: when the fused prefill takes
+    // sequences of T rows, the intra-chunk kernel and scan have nothing to do.
+    const bool all_fused = fa.fuse_max >= 0 && (long long)fa.fuse_max * kChunk >= a.T;
+    for (int w = 0; w < pl.windows && !all_fused; ++w) {
         const int c_lo = w * pl.window_chunks;
         const int c_hi = c_lo + pl.window_chunks < pl.chunk_ids ? c_lo + pl.window_chunks : pl.chunk_ids;
         const long long items = (long long)(c_hi - c_lo) * a.H;
@@ -1465,11 +1465,22 @@ PrefillPlan prefill_plan(int T, int N, int H, int dk, int dv, bool bf16, int win
     return p;
 }
 
+// Default: the fused prefill for calls whose sequences average at most two
+// chunks, taking sequences of up to 8 chunks when they average one chunk or
+// less and up to 4 otherwise.  The fused kernel runs a chain's chunks one
+// after another at about 10 us a chunk, which beats the intra-chunk kernel
+// plus scan only for short chains: 16 packed sequences (average 8 chunks,
+// longest 37) 250 us a step with none fused, 258 us fusing those of up to
+// 2 chunks; 128 sequences averaging one chunk 457 -> 360 us (8 chunks);
+// 64 sequences of 2 chunks 343 -> 264 us (4); 256 sequences of 32 rows
+// 698 -> 518 us (H = 32, d = 128).
 int prefill_fuse_max(int T, int N, int H, bool bf16, int fuse_chunks) {
     (void)H;
     if (!bf16 || fuse_chunks < 0) return -1;
     if (fuse_chunks > 0) return fuse_chunks;
-    return KDA_FUSE_DEFAULT(T, N);
+    if ((long long)T <= (long long)kChunk * N) return 8;
+    if ((long long)T <= 2LL * kChunk * N) return 4;
+    return -1;
 }
 
 size_t prefill_workspace_bytes(int T, int N, int H, int dk, int dv, bool bf16, int window_chunks) {

@@ -245,11 +245,14 @@ def _check_pool(p, name, num_slots, H, dk, dv, slot_stride, head_stride):
         _dev(p, name, torch.float32, (num_slots, H, dv, dk))
 
 
-def prefill_windows(T, N, H, d_k, d_v, dtype=torch.bfloat16, window_chunks=0) -> int:
+def prefill_windows(T, N, H, d_k, d_v, dtype=torch.bfloat16, window_chunks=0,
+                    fuse_chunks=0) -> int:
     """Windows of chunk ids a prefill call of these sizes runs as
     (``kda_prefill_windows``): its kernels are an intra-chunk kernel and a
-    state scan per window, in that order."""
-    d = make_desc(T, N, H, d_k, d_v, N, _io_code(dtype), window_chunks=window_chunks)
+    state scan per window, in that order (none when every sequence runs in
+    the fused prefill)."""
+    d = make_desc(T, N, H, d_k, d_v, N, _io_code(dtype), window_chunks=window_chunks,
+                  fuse_chunks=fuse_chunks)
     return int(load_library().kda_prefill_windows(ctypes.byref(d)))
 
 

@@ -87,6 +87,16 @@ def test_fuse_chunks_policy(lib):
     assert f(5, io=K.KDA_F32) == -1 and f(0, io=K.KDA_F32) == -1
     assert f(3, dk=96) == -1
     assert lib.kda_prefill_fuse_chunks(None) == -1
+    # the library's choice: by the average sequence length
+    assert f(0) == -1                                  # 16 sequences in 8192 rows
+    assert f(0, N=1) == -1
+    assert f(0, N=64) == 4 and f(0, N=100) == 4        # at most two chunks on average
+    assert f(0, N=128) == 8 and f(0, N=300) == 8       # at most one
+    # windows: none when every sequence is fused (F * 64 >= T)
+    d = K.make_desc(8192, 16, 32, 128, 128, 64, K.KDA_BF16, fuse_chunks=128)
+    assert lib.kda_prefill_windows(ctypes.byref(d)) == 0
+    d = K.make_desc(8192, 16, 32, 128, 128, 64, K.KDA_BF16, fuse_chunks=127)
+    assert lib.kda_prefill_windows(ctypes.byref(d)) == 1
 
 
 def _ws_formula(T, N, H, dk, dv, es):

@@ -687,3 +687,20 @@ def test_fused_is_bf16_only():
     assert lap.prefill_fuse_chunks(1000, 10, 2, 64, 64, torch.float32, fuse_chunks=5) == -1
     c = W.random_case(850, [10, 70, 0, 130], H=2, d_k=64, d_v=64, io_dtype="f32")
     _check_case(c, fuse_chunks=5)
+
+
+def test_fused_by_default_for_short_sequences():
+    """The library's choice: 96 sequences of at most one chunk average one
+    chunk, so every sequence runs in the fused prefill (the window of
+    intra-chunk kernel and scan finds nothing to do).  With fuse_chunks
+    covering all T rows that window is not launched at all."""
+    rng = np.random.default_rng(860)
+    lengths = [int(x) for x in rng.integers(1, 65, size=96)]
+    lengths[7] = 0
+    c = W.random_case(861, lengths, H=4, d_k=128, d_v=128, io_dtype="bf16", num_slots=100)
+    assert lap.prefill_fuse_chunks(c.T, c.N, c.H, 128, 128, torch.bfloat16) == 8
+    assert lap.prefill_windows(c.T, c.N, c.H, 128, 128, torch.bfloat16) == 1
+    _check_case(c)
+    every = -(-c.T // 64)
+    assert lap.prefill_windows(c.T, c.N, c.H, 128, 128, torch.bfloat16, fuse_chunks=every) == 0
+    _check_case(c, fuse_chunks=every)
