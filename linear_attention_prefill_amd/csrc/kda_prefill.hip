@@ -157,11 +157,12 @@ struct FuseArgs {
 };
 
 // The body of both persistent 8-wave kernels.  FUSED = false: the
-// intra-chunk kernel, which writes each item's record to the workspace.
+// intra-chunk kernel, which writes each item's record to the workspace (and
+// with SKIP passes over the chunks of sequences the fused prefill takes).
 // FUSED = true (bf16): the fused prefill, which walks whole chains and keeps
 // the record of the current chunk in LDS, where the state step that follows
 // its intra-chunk phases reads it (no record round trip through memory).
-template <typename E, int DK, int DV, bool FUSED>
+template <typename E, int DK, int DV, bool FUSED, bool SKIP>
 __device__ __forceinline__ void intra_chunks(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
@@ -198,8 +199,6 @@ __device__ __forceinline__ void intra_chunks(
     __shared__ __align__(16) float sBeta[kChunk];
     __shared__ int sExact[4 * C4];                     // per block and 4-channel column
     __shared__ int sCu[FUSED ? 1 : kCuCache];
-    __shared__ int sCum[FUSED ? 1 : kCuCache + 1];     // chunks before each sequence (dense walk)
-    __shared__ int sWsum[4];
     // fused: the chunk's K~^T and A_qk fragments and e^{Gam_C}; its Q~ and w
     // fragments take the k Qf rows, which are dead once K~^T is formed
     __shared__ __align__(16) E sKt[FUSED ? DK * kChunk : 8];
@@ -224,35 +223,6 @@ __device__ __forceinline__ void intra_chunks(
     const int cu_v = (cu_reg && lane <= N) ? cu[lane] : 0;
     if (!cu_reg && cu_lds)
         for (int i = tid; i <= N; i += NTH) sCu[i] = cu[i];
-    // Dense walk (one window, N < kCuCache): the chunks this kernel runs
-    // (sequences of more than fuse_max chunks) are numbered 0 .. R - 1 in
-    // sequence order and the grid steps over those numbers.  The id walk
-    // below also steps over the gap id each sequence leaves in the closed-form
-    // chunk ids, which idles workgroups when sequences are short (N sequences
-    // of one chunk: every other id is a gap).
-    const bool dense = !FUSED && N < kCuCache && c_lo == 0 && c_hi == T / kChunk + N;
-    if (dense) {
-        int x = 0;
-        if (tid < N) {
-            const int s0 = clamp_row(cu[tid], T), s1 = clamp_row(cu[tid + 1], T);
-            x = s1 > s0 ? (s1 - s0 + kChunk - 1) / kChunk : 0;
-            if (x <= fa.fuse_max) x = 0;
-        }
-        if (tid < kCuCache) {
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int y = __shfl_up(x, d);
-                if (lane >= d) x += y;
-            }
-            if (lane == 63) sWsum[wave] = x;
-        }
-        __syncthreads();
-        if (tid < kCuCache) {
-            for (int w = 0; w < wave; ++w) x += sWsum[w];
-            sCum[tid + 1] = x;
-            if (tid == 0) sCum[0] = 0;
-        }
-    }
     // Tm diag(beta) fragments (m, s), s <= m / 2: lane (i, g) holds row
     // 16 m + i, columns 32 s + kk(g, e), as the w and u products take them.
     // Their right halves for even m are the zero blocks (0, 1) and (2, 3),
@@ -279,6 +249,8 @@ __device__ __forceinline__ void intra_chunks(
     // h) on this walk that belongs to a sequence (ids between sequences'
     // chunk ranges are skipped).
     const int step_q = stride / H, step_r = stride % H;
+    // rows beyond which a sequence is not fused
+    const int fuse_rows = fa.fuse_max * kChunk;
     auto step_down = [&](int &cid, int &h) {
         h -= step_r;
         cid -= step_q;
@@ -297,7 +269,7 @@ __device__ __forceinline__ void intra_chunks(
             const int start = clamp_row(cu_at(lo), T), end = clamp_row(cu_at(lo + 1), T);
             const int len = end > start ? end - start : 0;
             const int jc = cid - (start / kChunk + lo);
-            if (jc >= 0 && jc * kChunk < len && (len + kChunk - 1) / kChunk > fa.fuse_max)
+            if (jc >= 0 && jc * kChunk < len && (!SKIP || len > fuse_rows))
                 return ChunkRef{cid * H + h, cid, h, start + jc * kChunk, min(kChunk, len - jc * kChunk)};
         }
         return ChunkRef{-1, 0, 0, 0, 0};
@@ -419,24 +391,6 @@ __device__ __forceinline__ void intra_chunks(
     };
     bf16x4 ureg[4];                                    // fused: this wave's u tile, row tile m
 
-    // dense walk: real item r = k H + h (k-th chunk run here, head h), taken
-    // from the last one down in steps of the grid
-    auto find_real = [&](int r) -> ChunkRef {
-        if (r < 0) return ChunkRef{-1, 0, 0, 0, 0};
-        const int kc = r / H, h = r - kc * H;
-        int lo = 0, hi = N - 1;                        // the last sequence with sCum <= kc
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (sCum[mid] <= kc) lo = mid; else hi = mid - 1;
-        }
-        const int start = clamp_row(cu_at(lo), T), end = clamp_row(cu_at(lo + 1), T);
-        const int len = end > start ? end - start : 0;
-        const int jc = kc - sCum[lo];
-        const int cid = start / kChunk + lo + jc;
-        return ChunkRef{cid * H + h, cid, h, start + jc * kChunk, min(kChunk, len - jc * kChunk)};
-    };
-    const int real_items = dense ? __builtin_amdgcn_readfirstlane(sCum[N]) * H : 0;
-    int rcur = real_items - 1 - (int)blockIdx.x;
 
     ChunkRef cur;
     FChain ch{-1, 0, 0, 0, 0, 0, 0};
@@ -445,8 +399,6 @@ __device__ __forceinline__ void intra_chunks(
         ch = next_chain((int)blockIdx.x);
         cur = item_of(ch, 0);
         if (ch.c >= 0) state_load(ch);
-    } else if (dense) {
-        cur = find_real(rcur);
     } else {
         const int item0 = c_hi * H - 1 - (int)blockIdx.x;
         cur = find_chunk(item0 / H, item0 % H);
@@ -490,10 +442,6 @@ __device__ __forceinline__ void intra_chunks(
                 }
                 return item_of(nch_ch, nj);
             } else {
-                if (dense) {
-                    rcur -= stride;
-                    return find_real(rcur);
-                }
                 int ncid = cur.cid, nh = cur.h;
                 step_down(ncid, nh);
                 return find_chunk(ncid, nh);
@@ -965,13 +913,18 @@ __device__ __forceinline__ void intra_chunks(
     }
 }
 
-template <typename E, int DK, int DV>
+// SKIP: pass over the chunks of sequences of at most fuse_max chunks (the
+// fused prefill's); a separate instantiation, since the test in the chunk
+// walk costs the plain kernel about a microsecond.
+template <typename E, int DK, int DV, bool SKIP>
 __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu, int T, int N, int H, int c_lo, int c_hi,
-    E *__restrict__ ws, float *__restrict__ ws_dec, FuseArgs fa) {
-    intra_chunks<E, DK, DV, false>(q, k, v, g, beta, cu, T, N, H, c_lo, c_hi, ws, ws_dec, fa);
+    E *__restrict__ ws, float *__restrict__ ws_dec, int fuse_max) {
+    FuseArgs fa{};
+    fa.fuse_max = fuse_max;
+    intra_chunks<E, DK, DV, false, SKIP>(q, k, v, g, beta, cu, T, N, H, c_lo, c_hi, ws, ws_dec, fa);
 }
 
 template <int DK, int DV>
@@ -979,7 +932,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_fused_prefill_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu, int T, int N, int H, FuseArgs fa) {
-    intra_chunks<bf16, DK, DV, true>(q, k, v, g, beta, cu, T, N, H, 0, 0, nullptr, nullptr, fa);
+    intra_chunks<bf16, DK, DV, true, false>(q, k, v, g, beta, cu, T, N, H, 0, 0, nullptr, nullptr, fa);
 }
 
 // ---------------------------------------------------------------------------
@@ -1368,9 +1321,10 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
         const int c_hi = c_lo + pl.window_chunks < pl.chunk_ids ? c_lo + pl.window_chunks : pl.chunk_ids;
         const long long items = (long long)(c_hi - c_lo) * a.H;
         const int grid = (int)(items < (long long)a.num_cus ? items : (long long)a.num_cus);
-        kda_intra_kernel<E, DK, DV><<<dim3(grid), dim3(kIntraThreads), 0, stream>>>(
+        auto intra = fa.fuse_max >= 0 ? kda_intra_kernel<E, DK, DV, true> : kda_intra_kernel<E, DK, DV, false>;
+        intra<<<dim3(grid), dim3(kIntraThreads), 0, stream>>>(
             static_cast<const E *>(a.q), static_cast<const E *>(a.k), static_cast<const E *>(a.v),
-            a.g, a.beta, a.cu_seqlens, a.T, a.N, a.H, c_lo, c_hi, ws, ws_dec, fa);
+            a.g, a.beta, a.cu_seqlens, a.T, a.N, a.H, c_lo, c_hi, ws, ws_dec, fa.fuse_max);
         // A failed intra launch leaves stale records: the scan must not run
         // on them and overwrite o and the caller's states.
         hipError_t e = hipGetLastError();
