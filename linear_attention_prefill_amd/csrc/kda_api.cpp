@@ -193,6 +193,7 @@ kda_status_t prefill_impl(const void *q, const void *k, const void *v, const flo
         c.qc = base; c.kc = base + nq; c.vc = base + 2 * nq;
         c.cu_seqlens = cu_seqlens; c.slots = slots;
         c.T = d.total_rows; c.N = d.num_seqs; c.H = d.num_heads; c.num_slots = d.num_slots;
+        c.num_cus = device_cus(s);
         const hipError_t e = bf ? dispatch_conv_front<bf16>(c, d.d_k, d.d_v, s)
                                 : dispatch_conv_front<float>(c, d.d_k, d.d_v, s);
         if (e != hipSuccess) return KDA_ERR_HIP;

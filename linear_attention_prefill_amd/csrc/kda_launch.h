@@ -81,6 +81,7 @@ struct ConvArgs {
     ConvWin win;
     int T, N, H, num_slots;
     int silu;
+    int num_cus = 0;                // compute units of the device (persistent grid)
 };
 
 template <typename E, int DK, int DV>

@@ -23,7 +23,7 @@ pytestmark = [pytest.mark.gpu,
 
 
 def run_prefill_conv(c, weight, window_dev, dt, act, strides=(0, 0, 0, 0), o_init=None,
-                     pool=None):
+                     pool=None, fuse_chunks=0):
     q, k, v = dev(c.q, dt), dev(c.k, dt), dev(c.v, dt)
     o = dev(o_init, dt) if o_init is not None else torch.zeros((c.T, c.H, c.d_v), dtype=dt,
                                                                 device="cuda")
@@ -31,14 +31,20 @@ def run_prefill_conv(c, weight, window_dev, dt, act, strides=(0, 0, 0, 0), o_ini
     lap.chunk_prefill(q, k, v, dev(c.g), dev(c.beta), dev(c.cu_seqlens), state_in=p, state_out=p,
                       o=o, slots=dev(c.slots), num_slots=c.state_pool.shape[0], scale=c.scale,
                       conv_weight=dev(weight), conv_window=window_dev, conv_activation=act,
-                      conv_strides=strides)
+                      conv_strides=strides, fuse_chunks=fuse_chunks)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), p.cpu().numpy()
 
 
-@pytest.mark.parametrize("dk,dv,io,act", [(128, 128, "bf16", "silu"), (64, 64, "f32", "none"),
-                                          (64, 128, "bf16", "none"), (128, 64, "f32", "silu")])
-def test_prefill_conv_parity(dk, dv, io, act):
+@pytest.mark.parametrize("dk,dv,io,act,fuse", [(128, 128, "bf16", "silu", -1),
+                                               (64, 64, "f32", "none", -1),
+                                               (64, 128, "bf16", "none", -1),
+                                               (128, 64, "f32", "silu", -1),
+                                               (128, 128, "bf16", "silu", 1),
+                                               (64, 64, "bf16", "none", 64)])
+def test_prefill_conv_parity(dk, dv, io, act, fuse):
+    """fuse: bf16 sequences of at most this many chunks run in the fused
+    prefill on the convolved inputs (1: the short ones; 64: all)."""
     lengths = [0, 1, 2, 3, 63, 64, 65, 130, 5]
     S = 12
     slots = [3, 0, 7, 11, -1, 5, 9, 2, 13]
@@ -47,9 +53,9 @@ def test_prefill_conv_parity(dk, dv, io, act):
     weight, window = W.draw_conv(202, S, 3, dk, dv, io)
     dt = torch_dtype(io)
     o_init = np.full((c.T, c.H, c.d_v), 2.0, dtype=np.float32)
-    announce("prefill conv %s act=%s" % (c.name, act))
+    announce("prefill conv %s act=%s fuse=%d" % (c.name, act, fuse))
     win_d = dev(window, dt)
-    o_g, pool_g = run_prefill_conv(c, weight, win_d, dt, act, o_init=o_init)
+    o_g, pool_g = run_prefill_conv(c, weight, win_d, dt, act, o_init=o_init, fuse_chunks=fuse)
     win_g = win_d.float().cpu().numpy()
     o_r, pool_r, _, win_r = oracle.chunk_prefill_conv(c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens,
                                                       weight, window, c.state_pool, c.slots,

@@ -68,9 +68,15 @@ def gap_mask(S, H, dk, dv, ss, hs):
     return m
 
 
-@pytest.mark.parametrize("dk,dv,io,in_place", [(128, 128, "bf16", True), (64, 128, "f32", True),
-                                               (128, 64, "bf16", False)])
-def test_prefill_with_line_addressed_pools(dk, dv, io, in_place):
+@pytest.mark.parametrize("dk,dv,io,in_place,fuse", [(128, 128, "bf16", True, -1),
+                                                    (64, 128, "f32", True, -1),
+                                                    (128, 64, "bf16", False, -1),
+                                                    (128, 128, "bf16", True, 3),
+                                                    (64, 64, "bf16", False, 64)])
+def test_prefill_with_line_addressed_pools(dk, dv, io, in_place, fuse):
+    """fuse: sequences of at most this many chunks run in the fused prefill
+    (3: some fused, some not; 64: all of them), which addresses the lines
+    itself."""
     c = W.random_case(61 + dk + dv, [70, 0, 129, 5, 64], H=3, d_k=dk, d_v=dv, io_dtype=io,
                       num_slots=7, slots=[5, 2, -1, 0, 6])
     S, H = c.state_pool.shape[0], c.H
@@ -82,10 +88,11 @@ def test_prefill_with_line_addressed_pools(dk, dv, io, in_place):
     pout = pin if in_place else dev(np.full_like(flat_in, fill))
     o_init = np.full((c.T, c.H, c.d_v), 3.0, dtype=np.float32)
     o = dev(o_init, dt)
-    announce("prefill lines %s in_place=%s" % (c.name, in_place))
+    announce("prefill lines %s in_place=%s fuse=%d" % (c.name, in_place, fuse))
     lap.chunk_prefill(dev(c.q, dt), dev(c.k, dt), dev(c.v, dt), dev(c.g), dev(c.beta),
                       dev(c.cu_seqlens), state_in=pin, state_out=pout, o=o, slots=dev(c.slots),
-                      num_slots=S, scale=c.scale, state_slot_stride=ss, state_head_stride=hs)
+                      num_slots=S, scale=c.scale, state_slot_stride=ss, state_head_stride=hs,
+                      fuse_chunks=fuse)
     torch.cuda.synchronize()
     flat_out = pout.cpu().numpy()
     o_g = o.float().cpu().numpy()

@@ -47,7 +47,10 @@ def test_conv_prefill_on_a_side_stream():
     np.testing.assert_array_equal(win.float().cpu().numpy(), win_r.astype(np.float32))
 
 
-def test_prefill_graph_replays_match_eager():
+@pytest.mark.parametrize("fuse", [-1, 64])
+def test_prefill_graph_replays_match_eager(fuse):
+    """fuse = 64: every sequence in the fused prefill (no intra-chunk kernel
+    or scan launched); -1: none."""
     c = W.random_case(311, [200, 1, 77], H=3, d_k=128, d_v=64, io_dtype="bf16", num_slots=4)
     dt = torch.bfloat16
     a = _prefill_args(c, dt)
@@ -59,7 +62,8 @@ def test_prefill_graph_replays_match_eager():
 
     def call():
         lap.chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu_seqlens"],
-                          state_in=pin, state_out=pout, o=o, slots=a["slots"], workspace=ws)
+                          state_in=pin, state_out=pout, o=o, slots=a["slots"], workspace=ws,
+                          fuse_chunks=fuse)
 
     announce("prefill eager reference")
     call()
