@@ -45,6 +45,12 @@
 // the record bytes each CU takes in, which a workgroup takes in once for its
 // NS slices: each call uses the largest NS of 1, 2 or 4 (bf16 for NS > 1)
 // that still leaves every CU a workgroup.
+// kda_fused_prefill_kernel (bf16): the intra-chunk kernel's body walking
+// whole (sequence, head) chains; each chunk's operands stay in LDS and a
+// sixth phase applies them to the chain's state, which the waves keep in
+// registers (wave w: value columns 16w .. 16w + 15).  Calls choose it for
+// short sequences (kda_prefill_fuse_chunks), since a chain's chunks run one
+// after another.
 #include <mutex>
 #include <type_traits>
 
