@@ -1,11 +1,13 @@
 #!/usr/bin/env python3
 """KDA prefill throughput on one MI355X, with the roofline of the dominant kernel.
 
-    python bench.py [--steps K] [--warmup W] [--workload packed|single|long|decode|decode_tokens]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload packed|single|short|long|decode|decode_tokens]
                     [--conv] [--tokens-mode MODE] [--no-extra] [--no-cpu-baseline]
 
-A step is one kda_chunk_prefill call (intra-chunk kernel + state scan) over
-one 8192-row chunk, with inputs already resident in HBM.  The default
+A step is one kda_chunk_prefill call (intra-chunk kernel + state scan, or the
+fused prefill for short sequences) over one 8192-row chunk, with inputs
+already resident in HBM.  The default
 workload is the packed chunk the metric names: 16 sequences of Dirichlet
 lengths in 8192 rows, H=32, d_k=d_v=128, bf16 q/k/v/o, fp32 g/beta, initial
 states gathered from a 64-slot fp32 pool by an int32 slot index and final
@@ -28,9 +30,10 @@ Prints ONE JSON line.  Besides the throughput it reports:
                 match), `traffic_ratio` their ratio to the algorithmic bytes;
   path          the whole step against the HBM roof and the bf16 MFMA roof;
   cpu_baseline  the fp64 oracle timed on the host cores on the same inputs;
-  kernels       both kernels' average durations;
+  kernels       the kernels' average durations;
   extra         the other workloads, each with its own roofline and CPU
-                baseline: one 8192-row sequence, the 262,144-token sequence
+                baseline: one 8192-row sequence, 128 short sequences in 8192
+                rows (the fused prefill), the 262,144-token sequence
                 fed as 32 chained 8192-row calls (per call and for all rows),
                 the 64-sequence decode step; plus the conv front end and the
                 multi-token decode.
@@ -431,6 +434,14 @@ def prefill_line(case, r, src_hash, conv=False):
     return line
 
 
+def short_seqs_prefill():
+    """128 sequences (Dirichlet lengths, longest 285 rows) in 8192 rows, H = 32,
+    d = 128, bf16, states from a 128-slot pool: a call the library runs in the
+    fused prefill."""
+    from linear_attention_prefill_amd import workloads as W
+    return W.packed_varlen_prefill(n=128, num_slots=128)
+
+
 def time_long_context(steps, warmup, torch, lap, log_fn):
     """The 262,144-token sequence as 32 chained 8192-row calls (state carried
     in a one-slot pool).  A pass is all 32 calls; `steps` passes are timed
@@ -486,7 +497,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["packed", "single", "long", "decode", "decode_tokens"],
+    ap.add_argument("--workload", choices=["packed", "single", "short", "long", "decode",
+                                           "decode_tokens"],
                     default="packed",
                     help="packed: 16 sequences in 8192 rows (default, the metric's chunk); "
                          "single: 1 x 8192 rows; long: 262,144 rows as 32 chained calls; "
@@ -580,7 +592,8 @@ def main():
         return
 
     t0 = time.time()
-    case = W.packed_varlen_prefill() if args.workload == "packed" else W.single_seq_prefill()
+    case = {"packed": W.packed_varlen_prefill, "single": W.single_seq_prefill,
+            "short": short_seqs_prefill}[args.workload]()
     log("generated %s in %.1f s" % (case.name, time.time() - t0))
     T, H, dk, dv = case.T, case.H, case.d_k, case.d_v
 
@@ -627,6 +640,16 @@ def main():
         if not args.no_cpu_baseline:
             lo["cpu_baseline"] = cpu_baseline(other, extra_cpu_s, s0=slots0(other))
         extra["single" if args.workload == "packed" else "packed"] = lo
+
+        sc = short_seqs_prefill()
+        rs = time_prefill(sc, args.steps, args.warmup, args.copies, torch, lap)
+        ls = prefill_line(sc, rs, src_hash)
+        ls["fuse_chunks"] = lap.prefill_fuse_chunks(sc.T, sc.N, sc.H, sc.d_k, sc.d_v)
+        log("%s: %.1f us/step (fused %.1f us)" % (sc.name, rs["ms_per_step"] * 1e3,
+                                                  rs["fused_ms"] * 1e3))
+        if not args.no_cpu_baseline:
+            ls["cpu_baseline"] = cpu_baseline(sc, extra_cpu_s, s0=slots0(sc))
+        extra["short_seqs"] = ls
 
         calls, rl = time_long_context(max(3, args.steps // 4), 1, torch, lap, log)
         ll = {"workload": "long_context_32x8192_H32_d128_bf16",
