@@ -229,6 +229,67 @@ __device__ __forceinline__ void intra_chunks(
     const int cu_v = (cu_reg && lane <= N) ? cu[lane] : 0;
     if (!cu_reg && cu_lds)
         for (int i = tid; i <= N; i += NTH) sCu[i] = cu[i];
+    // SKIP, one window: the sequences this launch runs (more than fuse_max
+    // chunks) listed in LDS with their chunk prefix, when they number at most
+    // kCuCache, so that the grid steps over their chunks only; a call whose
+    // sequences are all fused then has nothing to walk (the id walk would look
+    // each id up to pass it over: 44 us for 128 sequences at H = 32).  More
+    // sequences, or windows, take the id walk.
+    __shared__ int sLong[SKIP ? kCuCache : 1];
+    __shared__ int sLcum[SKIP ? kCuCache + 1 : 1];
+    __shared__ int sWs[2][NTH / 64];
+    int nlong = -1;                                    // -1: the id walk
+    if constexpr (SKIP) {
+        if (c_lo == 0 && c_hi == T / kChunk + N) {
+            int count = 0, chunks = 0;                 // running totals, uniform
+            for (int base = 0; base < N; base += NTH) {
+                const int n = base + tid;
+                int nc = 0;
+                if (n < N) {
+                    const int s0 = clamp_row(cu[n], T), s1 = clamp_row(cu[n + 1], T);
+                    nc = s1 > s0 ? (s1 - s0 + kChunk - 1) / kChunk : 0;
+                    if (nc <= fa.fuse_max) nc = 0;
+                }
+                const int f = nc > 0 ? 1 : 0;
+                int fs = f, cs = nc;                   // inclusive scans over the wave
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const int y = __shfl_up(fs, d), z = __shfl_up(cs, d);
+                    if (lane >= d) {
+                        fs += y;
+                        cs += z;
+                    }
+                }
+                if (lane == 63) {
+                    sWs[0][wave] = fs;
+                    sWs[1][wave] = cs;
+                }
+                __syncthreads();
+                int fo = 0, co = 0, ft = 0, ct = 0;
+#pragma unroll
+                for (int w = 0; w < NTH / 64; ++w) {
+                    if (w < wave) {
+                        fo += sWs[0][w];
+                        co += sWs[1][w];
+                    }
+                    ft += sWs[0][w];
+                    ct += sWs[1][w];
+                }
+                const int pos = count + fo + fs - f;
+                if (f && pos < kCuCache) {
+                    sLong[pos] = n;
+                    sLcum[pos] = chunks + co + cs - nc;
+                }
+                count += ft;
+                chunks += ct;
+                __syncthreads();                       // sWs is reused
+            }
+            if (count <= kCuCache) {
+                nlong = count;
+                if (tid == 0) sLcum[count] = chunks;
+            }
+        }
+    }
     // Tm diag(beta) fragments (m, s), s <= m / 2: lane (i, g) holds row
     // 16 m + i, columns 32 s + kk(g, e), as the w and u products take them.
     // Their right halves for even m are the zero blocks (0, 1) and (2, 3),
@@ -398,6 +459,25 @@ __device__ __forceinline__ void intra_chunks(
     bf16x4 ureg[4];                                    // fused: this wave's u tile, row tile m
 
 
+    // SKIP list walk: item r = k H + h, the k-th listed chunk and head h,
+    // from the last one down in steps of the grid
+    auto find_long = [&](int r) -> ChunkRef {
+        if (r < 0) return ChunkRef{-1, 0, 0, 0, 0};
+        const int kc = r / H, h = r - kc * H;
+        int lo = 0, hi = nlong - 1;                    // the last listed sequence with sLcum <= kc
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sLcum[mid] <= kc) lo = mid; else hi = mid - 1;
+        }
+        const int n = __builtin_amdgcn_readfirstlane(sLong[lo]);
+        const int start = clamp_row(cu_at(n), T), end = clamp_row(cu_at(n + 1), T);
+        const int len = end > start ? end - start : 0;
+        const int jc = kc - sLcum[lo];
+        const int cid = start / kChunk + n + jc;
+        return ChunkRef{cid * H + h, cid, h, start + jc * kChunk, min(kChunk, len - jc * kChunk)};
+    };
+    int rcur = 0;
+
     ChunkRef cur;
     FChain ch{-1, 0, 0, 0, 0, 0, 0};
     int jcur = 0;
@@ -405,6 +485,9 @@ __device__ __forceinline__ void intra_chunks(
         ch = next_chain((int)blockIdx.x);
         cur = item_of(ch, 0);
         if (ch.c >= 0) state_load(ch);
+    } else if (SKIP && nlong >= 0) {
+        rcur = __builtin_amdgcn_readfirstlane(sLcum[nlong]) * H - 1 - (int)blockIdx.x;
+        cur = find_long(rcur);
     } else {
         const int item0 = c_hi * H - 1 - (int)blockIdx.x;
         cur = find_chunk(item0 / H, item0 % H);
@@ -448,6 +531,10 @@ __device__ __forceinline__ void intra_chunks(
                 }
                 return item_of(nch_ch, nj);
             } else {
+                if (SKIP && nlong >= 0) {
+                    rcur -= stride;
+                    return find_long(rcur);
+                }
                 int ncid = cur.cid, nh = cur.h;
                 step_down(ncid, nh);
                 return find_chunk(ncid, nh);

@@ -704,3 +704,18 @@ def test_fused_by_default_for_short_sequences():
     every = -(-c.T // 64)
     assert lap.prefill_windows(c.T, c.N, c.H, 128, 128, torch.bfloat16, fuse_chunks=every) == 0
     _check_case(c, fuse_chunks=every)
+
+
+@pytest.mark.parametrize("n_long", [40, 290])
+def test_fused_with_many_unfused_sequences(n_long):
+    """fuse_chunks = 1 with 300 sequences: the intra-chunk kernel lists the
+    unfused ones (n_long of them, two or three chunks each) and walks their
+    chunks only, or, past 256 of them, walks the chunk ids and passes over the
+    fused ones."""
+    rng = np.random.default_rng(870 + n_long)
+    lengths = [int(x) for x in rng.integers(65, 190, size=n_long)] + \
+              [int(x) for x in rng.integers(0, 65, size=300 - n_long)]
+    lengths = [lengths[i] for i in rng.permutation(300)]
+    c = W.random_case(871 + n_long, lengths, H=2, d_k=64, d_v=64, io_dtype="bf16",
+                      num_slots=310)
+    _check_case(c, fuse_chunks=1)
