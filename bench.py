@@ -29,6 +29,8 @@ Prints ONE JSON line.  Besides the throughput it reports:
                 (profiles/traffic.json, reported while the kernel sources
                 match), `traffic_ratio` their ratio to the algorithmic bytes;
   path          the whole step against the HBM roof and the bf16 MFMA roof;
+  intra_mfma    the intra-chunk contractions' algorithmic flops over the
+                intra kernel's time, against the bf16 matrix-core peak;
   cpu_baseline  the fp64 oracle timed on the host cores on the same inputs;
   kernels       the kernels' average durations;
   extra         the other workloads, each with its own roofline and CPU
@@ -115,8 +117,10 @@ def path_bytes(T, H, dk, dv, es, n_live, state_in, state_out):
             + (n_live * state if state_in else 0) + (n_live * state if state_out else 0))
 
 
-def path_flops(lengths, H, dk, dv):
-    """Triangle-aware flops of the chunk form per (chunk, head), summed."""
+def path_flops(lengths, H, dk, dv, intra_only=False):
+    """Triangle-aware flops of the chunk form per (chunk, head), summed; with
+    intra_only, the intra-chunk contractions alone (A_kk, A_qk, the inverse,
+    w and u)."""
     total = 0
     for L in lengths:
         for c0 in range(0, int(L), 64):
@@ -124,10 +128,11 @@ def path_flops(lengths, H, dk, dv):
             tri = C * (C + 1) // 2
             f = 2 * tri * dk * 2                 # A_kk, A_qk
             f += 2 * tri * (dk + dv)             # w, u (triangular Tm)
-            f += 2 * C * dk * dv * 2             # w S, Q~ S
-            f += 2 * tri * dv                    # A_qk U
-            f += 2 * C * dk * dv                 # K~^T U
             f += C * C * C // 3                  # inverse (approx.)
+            if not intra_only:
+                f += 2 * C * dk * dv * 2         # w S, Q~ S
+                f += 2 * tri * dv                # A_qk U
+                f += 2 * C * dk * dv             # K~^T U
             total += f
     return total * H
 
@@ -431,6 +436,15 @@ def prefill_line(case, r, src_hash, conv=False):
                  "TFLOP/s": pf / step_s / 1e12,
                  "frac_mfma_bf16": pf / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS},
     }
+    if r["intra_ms"] > 0:
+        # the intra-chunk contractions against the bf16 matrix-core peak, over
+        # the intra kernel's whole time (its loads, stores and VALU work
+        # included; profiles/ holds the counter-measured MFMA figures)
+        fi = path_flops(lengths, H, dk, dv, intra_only=True)
+        ti = r["intra_ms"] * 1e-3
+        line["intra_mfma"] = {"kernel": "kda_intra_kernel", "algorithmic_flops": fi,
+                              "TFLOP/s": fi / ti / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                              "frac": fi / ti / 1e12 / MFMA_BF16_PEAK_TFLOPS}
     return line
 
 
@@ -626,6 +640,7 @@ def main():
                    "initial_state": "pool-gathered" if r["state_in"] else "zero",
                    "input_copies_rotated": args.copies},
         "roofline": head["roofline"],
+        "intra_mfma": head.get("intra_mfma"),
         "kernels": head["kernels"],
         "path": head["path"],
         "kernel_source_hash": src_hash,
