@@ -178,8 +178,9 @@ int32_t kda_prefill_fuse_chunks(const kda_prefill_desc_t *desc);
 /*
  * Bytes of device workspace kda_chunk_prefill needs for `desc` (0 if desc is
  * invalid).  The workspace holds the per-chunk operands that pass from the
- * intra-chunk kernel to the state scan, and with a conv mode the convolved
- * q, k and v.  As in the "kern" page, section "The manifest", workspace is
+ * intra-chunk kernel to the state scan, and, when a conv mode runs the conv
+ * as a pass of its own (see kda_chunk_prefill_conv), the convolved q, k and
+ * v.  As in the "kern" page, section "The manifest", workspace is
  * scratch that lasts one call; the caller allocates it, as its hosts
  * allocate their own pools (same page, section "Hosts"), and may reuse it
  * for every call whose size it covers once the previous call on it is done
@@ -257,9 +258,15 @@ kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v
  * kda_chunk_prefill_timed with the short conv front end (desc->conv_mode not
  * KDA_CONV_NONE; see "Short conv front end" above): q, k and v are the raw
  * inputs, conv->window is read and then rewritten, and the rest of the step
- * runs on the convolved values.  The conv runs first, then the window
- * update, then the kernels that `events` (optional, as for
- * kda_chunk_prefill_timed) bracket.  Errors as for kda_chunk_prefill, plus
+ * runs on the convolved values.  For bf16 with d_k = d_v and no fused
+ * sequence (kda_prefill_fuse_chunks is -1) the conv is folded into the
+ * intra-chunk kernel's loads, which convolve the rows they read and round
+ * them to bf16 as the pass would write them; the window update follows the
+ * last intra-chunk launch, after the kernels that `events` (optional, as for
+ * kda_chunk_prefill_timed) bracket.  Otherwise the conv runs first as a pass
+ * of its own that writes the convolved q, k and v into the workspace, then
+ * the window update, then the bracketed kernels.  Both orders give the same
+ * values.  Errors as for kda_chunk_prefill, plus
  * KDA_ERR_NULL for a NULL conv, weight or window, and KDA_ERR_SHAPE for a
  * conv mode out of range or window strides that break the rules above.
  * kda_chunk_prefill and kda_chunk_prefill_timed return KDA_ERR_NULL for a

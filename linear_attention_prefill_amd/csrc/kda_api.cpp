@@ -4,6 +4,10 @@
 #include "kda.h"
 #include "kda_launch.h"
 
+#ifndef KDA_CONV_FOLD
+#define KDA_CONV_FOLD 1
+#endif
+
 #include <limits.h>
 
 #include <atomic>
@@ -142,6 +146,25 @@ kda_status_t check_conv(int mode, const kda_conv_t *conv, int H, int dk, int dv,
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// The conv runs folded into the intra-chunk kernel's loads for bf16 with
+// d_k = d_v when no sequence is fused, else as a pass of its own that writes
+// the convolved q, k, v into the workspace.
+bool conv_folded(const kda_prefill_desc_t &d) {
+    return d.conv_mode != KDA_CONV_NONE && d.io_dtype == KDA_BF16 && d.d_k == d.d_v && KDA_CONV_FOLD &&
+           kda::prefill_fuse_max(d.total_rows, d.num_seqs, d.num_heads, true, d.fuse_chunks) < 0;
+}
+
+// workspace bytes of a valid desc: the records, and the convolved q, k, v
+// when the conv runs as a pass of its own
+size_t prefill_need(const kda_prefill_desc_t &d) {
+    const bool bf = d.io_dtype == KDA_BF16;
+    size_t n = kda::prefill_workspace_bytes(d.total_rows, d.num_seqs, d.num_heads, d.d_k, d.d_v, bf,
+                                            d.window_chunks);
+    if (d.conv_mode != KDA_CONV_NONE && !conv_folded(d))
+        n += kda::conv_workspace_bytes(d.total_rows, d.num_heads, d.d_k, d.d_v, bf);
+    return n;
+}
+
 kda_status_t prefill_impl(const void *q, const void *k, const void *v, const float *g,
                           const float *beta, const int32_t *cu_seqlens, const float *state_in,
                           float *state_out, void *o, const int32_t *slots,
@@ -160,9 +183,7 @@ kda_status_t prefill_impl(const void *q, const void *k, const void *v, const flo
     const bool bf = d.io_dtype == KDA_BF16;
     const size_t rec_bytes = kda::prefill_workspace_bytes(d.total_rows, d.num_seqs, d.num_heads,
                                                           d.d_k, d.d_v, bf, d.window_chunks);
-    const size_t need = rec_bytes + (with_conv ? kda::conv_workspace_bytes(
-                                                     d.total_rows, d.num_heads, d.d_k, d.d_v, bf)
-                                               : 0);
+    const size_t need = prefill_need(d);
     if (static_ws && need > KDA_STATIC_SCRATCH_BYTES) return KDA_ERR_TOO_LARGE;
     if (need > 0 && !workspace && !static_ws) return KDA_ERR_NULL;
     const void *ptrs[] = {q, k, v, g, beta, cu_seqlens, state_in, state_out, o, slots, workspace};
@@ -185,15 +206,20 @@ kda_status_t prefill_impl(const void *q, const void *k, const void *v, const flo
     (void)hipGetLastError();       // an earlier call's error is not this call's
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.cu_seqlens = cu_seqlens;
+    const bool fold = with_conv && conv_folded(d);
     if (with_conv) {
-        const size_t es = bf ? 2 : 4;
-        char *base = static_cast<char *>(workspace) + align256(rec_bytes);
-        const size_t nq = align256((size_t)d.total_rows * d.num_heads * d.d_k * es);
         c.q = q; c.k = k; c.v = v;
-        c.qc = base; c.kc = base + nq; c.vc = base + 2 * nq;
         c.cu_seqlens = cu_seqlens; c.slots = slots;
         c.T = d.total_rows; c.N = d.num_seqs; c.H = d.num_heads; c.num_slots = d.num_slots;
         c.num_cus = device_cus(s);
+    }
+    if (fold) {
+        a.conv = &c;
+    } else if (with_conv) {
+        const size_t es = bf ? 2 : 4;
+        char *base = static_cast<char *>(workspace) + align256(rec_bytes);
+        const size_t nq = align256((size_t)d.total_rows * d.num_heads * d.d_k * es);
+        c.qc = base; c.kc = base + nq; c.vc = base + 2 * nq;
         const hipError_t e = bf ? dispatch_conv_front<bf16>(c, d.d_k, d.d_v, s)
                                 : dispatch_conv_front<float>(c, d.d_k, d.d_v, s);
         if (e != hipSuccess) return KDA_ERR_HIP;
@@ -275,12 +301,7 @@ int32_t kda_prefill_fuse_chunks(const kda_prefill_desc_t *desc) {
 
 size_t kda_prefill_workspace_size(const kda_prefill_desc_t *desc) {
     if (check_desc(desc) != KDA_OK) return 0;
-    const bool bf = desc->io_dtype == KDA_BF16;
-    size_t n = kda::prefill_workspace_bytes(desc->total_rows, desc->num_seqs, desc->num_heads,
-                                            desc->d_k, desc->d_v, bf, desc->window_chunks);
-    if (desc->conv_mode != KDA_CONV_NONE)
-        n += kda::conv_workspace_bytes(desc->total_rows, desc->num_heads, desc->d_k, desc->d_v, bf);
-    return n;
+    return prefill_need(*desc);
 }
 
 kda_status_t kda_chunk_prefill_timed(const void *q, const void *k, const void *v,

@@ -270,8 +270,19 @@ hipError_t launch_conv_front(const ConvArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <typename E, int DK, int DV>
+hipError_t launch_conv_window(const ConvArgs &a, hipStream_t stream) {
+    constexpr int C = 2 * DK + DV;
+    if (a.T > 0)
+        kda_conv_window_kernel<E, DK, DV><<<dim3(a.N, a.H), dim3(C / 4), 0, stream>>>(
+            static_cast<const E *>(a.q), static_cast<const E *>(a.k), static_cast<const E *>(a.v),
+            a.cu_seqlens, a.slots, static_cast<E *>(a.window), a.win, a.T, a.N, a.H, a.num_slots);
+    return hipGetLastError();
+}
+
 #define KDA_INST(E, DK, DV) \
-    template hipError_t launch_conv_front<E, DK, DV>(const ConvArgs &, hipStream_t);
+    template hipError_t launch_conv_front<E, DK, DV>(const ConvArgs &, hipStream_t); \
+    template hipError_t launch_conv_window<E, DK, DV>(const ConvArgs &, hipStream_t);
 KDA_INST(bf16, 64, 64)
 KDA_INST(bf16, 64, 128)
 KDA_INST(bf16, 128, 64)

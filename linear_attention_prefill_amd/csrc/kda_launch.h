@@ -26,6 +26,10 @@ struct PrefillArgs {
     // each kernel launch (intra and scan of each window in turn)
     const hipEvent_t *events = nullptr;
     int num_events = 0;
+    // the short conv folded into the intra-chunk kernel (bf16, d_k = d_v,
+    // no fused prefill): q, k, v are the raw inputs; the windows are updated
+    // after the intra-chunk launches
+    const struct ConvArgs *conv = nullptr;
 };
 
 // How a prefill call splits into windows of chunk ids and lays out its
@@ -89,6 +93,11 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
 template <typename E, int DK, int DV>
 hipError_t launch_conv_front(const ConvArgs &a, hipStream_t stream);
+
+// Only the window update of the conv front end (the conv itself folded into
+// the intra-chunk kernel).
+template <typename E, int DK, int DV>
+hipError_t launch_conv_window(const ConvArgs &a, hipStream_t stream);
 
 template <typename E, int DK, int DV>
 hipError_t launch_decode_conv(const DecodeArgs &a, const ConvArgs &c, hipStream_t stream);

@@ -143,6 +143,7 @@ template <int L> __device__ __forceinline__ float quad_bcast(float x) { return d
 // A chunk of one head: item = cid * H + h; valid when item >= 0.
 struct ChunkRef {
     int item, cid, h, row0, C;
+    int n, jc;          // sequence, and the chunk's index in it
 };
 
 // Index p = I (I + 1) / 2 + J of the block pair (I, J), J <= I < 4.
@@ -162,21 +163,46 @@ struct FuseArgs {
     int fuse_max;
 };
 
+// The short conv front end folded into the intra-chunk kernel's loads (bf16,
+// d_k = d_v): each factor lane convolves its four rows of k, q and v, taking
+// the three rows before them from the lane below (a DPP row shift) or, for
+// a chunk's first rows, from the rows before the chunk or the sequence's
+// conv window, staged per wave in LDS with the taps of its channels.
+template <typename E> struct ConvFold {
+    const float *weight;        // [H][4][2 d_k + d_v]
+    const E *window;
+    ConvWin win;
+    const int32_t *slots;
+    int num_slots;
+};
+constexpr int kCvFloats = 3 * kConvTaps * 16 + 3 * kConvWindow * 16 / 2;   // per wave: taps, then halo (bf16)
+
+// row_shr:1 within each 16-lane row (the row's first lane gets zeros)
+__device__ __forceinline__ bf16x4 dpp_shr1(const bf16x4 &x) {
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    i32x2 w = __builtin_bit_cast(i32x2, x);
+    w[0] = __builtin_amdgcn_update_dpp(0, w[0], 0x111, 0xF, 0xF, true);
+    w[1] = __builtin_amdgcn_update_dpp(0, w[1], 0x111, 0xF, 0xF, true);
+    return __builtin_bit_cast(bf16x4, w);
+}
+
 // The body of both persistent 8-wave kernels.  FUSED = false: the
 // intra-chunk kernel, which writes each item's record to the workspace (and
 // with SKIP passes over the chunks of sequences the fused prefill takes).
 // FUSED = true (bf16): the fused prefill, which walks whole chains and keeps
 // the record of the current chunk in LDS, where the state step that follows
 // its intra-chunk phases reads it (no record round trip through memory).
-template <typename E, int DK, int DV, bool FUSED, bool SKIP>
+template <typename E, int DK, int DV, bool FUSED, bool SKIP, int CONV = 0>
 __device__ __forceinline__ void intra_chunks(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu, int T, int N, int H, int c_lo, int c_hi,
-    E *__restrict__ ws, float *__restrict__ ws_dec, const FuseArgs &fa) {
+    E *__restrict__ ws, float *__restrict__ ws_dec, const FuseArgs &fa,
+    const ConvFold<E> &cf = ConvFold<E>{}) {
     static_assert(DK == 64 || DK == 128, "d_k");
     static_assert(DV == 64 || DV == 128, "d_v");
     static_assert(!FUSED || sizeof(E) == 2, "the fused prefill is bf16");
+    static_assert(CONV == 0 || (sizeof(E) == 2 && DK == DV && !FUSED), "folded conv: bf16, d_k = d_v");
     using LD = IntraLds<E, DK, DV, FUSED>;
     using L = WsLayout<E, DK, DV>;
     using R4 = typename Raw4<E>::type;
@@ -213,6 +239,9 @@ __device__ __forceinline__ void intra_chunks(
     static_assert(!FUSED || 2 * kChunk * DK * sizeof(E) <= sizeof(sKQ), "Q~ and w in the k Qf rows");
     E *const sQt = reinterpret_cast<E *>(sKQ);         // fused: Q~ fragments
     E *const sW = sQt + kChunk * DK;                   // fused: w fragments
+    // folded conv: this wave's taps and halo rows, in the A_kk rows (dead
+    // from the end of the second inverse level to the next A-block phase)
+    static_assert(CONV == 0 || (kIntraThreads / 64) * kCvFloats <= kChunk * LD::AP, "conv slots");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, lg = lane >> 4;
@@ -220,6 +249,8 @@ __device__ __forceinline__ void intra_chunks(
     // owns channels 4 cq .. + 3, cq = 4 w + c, of rows 4 r .. 4 r + 3: a DPP
     // row of 16 lanes spans the chunk and a quad of lanes one 16-row block.
     const int r4 = lane & 15, cq = 4 * wave + lg, ch0 = 4 * cq;
+    float *const sCv = sA + wave * kCvFloats;          // folded conv: [tensor][tap][16] taps
+    E *const sCvh = reinterpret_cast<E *>(sCv + 3 * kConvTaps * 16);   // [tensor][row][16] halo
     const bool fthread = wave < FW;
     const int stride = gridDim.x;
 
@@ -352,13 +383,15 @@ __device__ __forceinline__ void intra_chunks(
             const int len = end > start ? end - start : 0;
             const int jc = cid - (start / kChunk + lo);
             if (jc >= 0 && jc * kChunk < len && (!SKIP || len > fuse_rows))
-                return ChunkRef{cid * H + h, cid, h, start + jc * kChunk, min(kChunk, len - jc * kChunk)};
+                return ChunkRef{cid * H + h, cid, h, start + jc * kChunk, min(kChunk, len - jc * kChunk),
+                                lo, jc};
         }
-        return ChunkRef{-1, 0, 0, 0, 0};
+        return ChunkRef{-1, 0, 0, 0, 0, 0, 0};
     };
 
     // registers holding the next chunk's raw inputs
     R4 kr[4], qr[4];
+    R4 vr[CONV ? 4 : 1];                               // folded conv: V in the factor lanes' order
     f32x4 gr[4];
     uint4 xv[VPT];
     float bt = 0.f;
@@ -366,19 +399,98 @@ __device__ __forceinline__ void intra_chunks(
     auto load_row = [&](const ChunkRef &ck, int r) {
         const int row = 4 * r4 + r;
         kr[r] = qr[r] = R4{};
+        if constexpr (CONV != 0) vr[r] = R4{};
         gr[r] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (fthread && ck.item >= 0 && row < ck.C) {
             const size_t off = ((size_t)(ck.row0 + row) * H + ck.h) * DK + ch0;
             kr[r] = *reinterpret_cast<const R4 *>(k + off);
             qr[r] = *reinterpret_cast<const R4 *>(q + off);
             gr[r] = *reinterpret_cast<const f32x4 *>(g + off);
+            if constexpr (CONV != 0) vr[r] = *reinterpret_cast<const R4 *>(v + off);
+        }
+    };
+    // Folded conv staging, per wave: taps of its 16 channels (lanes 0..47,
+    // [tensor][tap][4 channels]) and the three rows before the chunk (lanes
+    // 0..35, [tensor][row][4 channels]): rows of the same sequence, its conv
+    // window for a first chunk, or zeros for a padded sequence.  Fetched into
+    // registers a phase ahead (addresses clamped, loads unconditional), then
+    // put into the wave's LDS slot.
+    const float *const cv_weight = cf.weight;
+    const E *const cv_window = cf.window;
+    const ConvWin cv_win = cf.win;
+    const int32_t *const cv_slots = cf.slots;
+    const int cv_nslots = cf.num_slots;
+    f32x4 cw_reg = f32x4{0.f, 0.f, 0.f, 0.f};
+    R4 ch_reg = R4{};
+    bool ch_zero = true;
+    auto conv_fetch = [&](const ChunkRef &ck, int slot) __attribute__((always_inline)) {
+        if constexpr (CONV != 0) {
+            const int hh = ck.item >= 0 ? ck.h : 0;
+            {
+                const int l = lane < 48 ? lane : 47;
+                const int p = l >> 4, j = (l >> 2) & 3, c4 = l & 3;
+                cw_reg = *reinterpret_cast<const f32x4 *>(
+                    cv_weight + ((size_t)hh * kConvTaps + j) * (2 * DK + DV) + p * DK + 16 * wave + 4 * c4);
+            }
+            {
+                const int l = lane < 36 ? lane : 35;
+                const int p = l / 12, i = (l >> 2) % 3, c4 = l & 3;
+                const int ch = 16 * wave + 4 * c4;
+                const bool inseq = ck.item >= 0 && ck.jc > 0;
+                const bool live = ck.item >= 0 && ck.jc == 0 && slot >= 0 && slot < cv_nslots;
+                const int row = inseq ? ck.row0 - kConvWindow + i : 0;
+                // the lane's tensor picked by arithmetic on the pointer values:
+                // a conditional over the captured names becomes a load through
+                // a selected address, which keeps them in private memory
+                const E *const src = reinterpret_cast<const E *>(
+                    reinterpret_cast<uintptr_t>(q) * (p == 0) + reinterpret_cast<uintptr_t>(k) * (p == 1) +
+                    reinterpret_cast<uintptr_t>(v) * (p == 2));
+                const E *const addr = live ? cv_window + cv_win.at(slot, hh, i, p, ch)
+                                           : src + ((size_t)row * H + hh) * DK + ch;
+                ch_reg = *reinterpret_cast<const R4 *>(addr);
+                ch_zero = !(inseq || live);
+            }
+        }
+    };
+    auto conv_put = [&]() __attribute__((always_inline)) {
+        if constexpr (CONV != 0) {
+            if (fthread) {
+                if (lane < 48) *reinterpret_cast<f32x4 *>(sCv + lane * 4) = cw_reg;
+                if (lane < 36) *reinterpret_cast<R4 *>(sCvh + lane * 4) = ch_zero ? R4{} : ch_reg;
+            }
+        }
+    };
+    // The folded conv of one tensor's four rows (in place, rounded to the io
+    // type as the conv pass would write them; rows past the chunk's end stay
+    // zero).
+    auto conv_rows = [&](R4 (&x)[4], int p, int C) __attribute__((always_inline)) {
+        if constexpr (CONV != 0) {
+            R4 m3 = dpp_shr1(x[1]), m2 = dpp_shr1(x[2]), m1 = dpp_shr1(x[3]);
+            if (r4 == 0) {
+                m3 = *reinterpret_cast<const R4 *>(sCvh + (p * 3 + 0) * 16 + 4 * lg);
+                m2 = *reinterpret_cast<const R4 *>(sCvh + (p * 3 + 1) * 16 + 4 * lg);
+                m1 = *reinterpret_cast<const R4 *>(sCvh + (p * 3 + 2) * 16 + 4 * lg);
+            }
+            // one channel at a time: its four taps and seven inputs
+            const float *const wp = sCv + p * kConvTaps * 16 + 4 * lg;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float w0 = wp[c], w1 = wp[16 + c], w2 = wp[32 + c], w3 = wp[48 + c];
+                const float xs[7] = {(float)m3[c],   (float)m2[c],   (float)m1[c],  (float)x[0][c],
+                                     (float)x[1][c], (float)x[2][c], (float)x[3][c]};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float t = conv_act(conv4(w0, w1, w2, w3, xs[r], xs[r + 1], xs[r + 2], xs[r + 3]), CONV == 2);
+                    x[r][c] = (E)(4 * r4 + r < C ? t : 0.f);
+                }
+            }
         }
     };
     auto load_beta = [&](const ChunkRef &ck) {
         bt = (ck.item >= 0 && tid < ck.C) ? beta[(size_t)(ck.row0 + tid) * H + ck.h] : 0.f;
     };
     auto load_v = [&](const ChunkRef &ck) {
-        if constexpr (LD::kStage) {
+        if constexpr (LD::kStage && CONV == 0) {
 #pragma unroll
             for (int p = 0; p < VPT; ++p) {
                 const int u = tid + p * NTH;
@@ -452,9 +564,10 @@ __device__ __forceinline__ void intra_chunks(
         return ch;
     };
     auto item_of = [&](const FChain &ch, int j) -> ChunkRef {
-        if (ch.c < 0) return ChunkRef{-1, 0, 0, 0, 0};
+        if (ch.c < 0) return ChunkRef{-1, 0, 0, 0, 0, 0, 0};
         const int cid = ch.start / kChunk + ch.n + j;
-        return ChunkRef{cid * H + ch.h, cid, ch.h, ch.start + j * kChunk, min(kChunk, ch.len - j * kChunk)};
+        return ChunkRef{cid * H + ch.h, cid, ch.h, ch.start + j * kChunk, min(kChunk, ch.len - j * kChunk),
+                        ch.n, j};
     };
     // key tile t of this wave's state slice, C layout: S[16t + 4g + r][16 wave + i]
     f32x4 S[FUSED ? KT : 1];
@@ -477,7 +590,7 @@ __device__ __forceinline__ void intra_chunks(
     // SKIP list walk: item r = k H + h, the k-th listed chunk and head h,
     // from the last one down in steps of the grid
     auto find_long = [&](int r) -> ChunkRef {
-        if (r < 0) return ChunkRef{-1, 0, 0, 0, 0};
+        if (r < 0) return ChunkRef{-1, 0, 0, 0, 0, 0, 0};
         const int kc = r / H, h = r - kc * H;
         int lo = 0, hi = nlong - 1;                    // the last listed sequence with sLcum <= kc
         while (lo < hi) {
@@ -489,7 +602,7 @@ __device__ __forceinline__ void intra_chunks(
         const int len = end > start ? end - start : 0;
         const int jc = kc - sLcum[lo];
         const int cid = start / kChunk + n + jc;
-        return ChunkRef{cid * H + h, cid, h, start + jc * kChunk, min(kChunk, len - jc * kChunk)};
+        return ChunkRef{cid * H + h, cid, h, start + jc * kChunk, min(kChunk, len - jc * kChunk), n, jc};
     };
     int rcur = 0;
 
@@ -511,6 +624,8 @@ __device__ __forceinline__ void intra_chunks(
     for (int r = 0; r < 4; ++r) load_row(cur, r);
     load_beta(cur);
     load_v(cur);
+    if constexpr (CONV != 0)
+        conv_fetch(cur, cur.item >= 0 ? (cv_slots ? cv_slots[cur.n] : cur.n) : -1);
     // Settle the first chunk's loads here, so that the loop's own prefetches
     // are the only loads in flight at its top.
 #pragma unroll
@@ -518,10 +633,16 @@ __device__ __forceinline__ void intra_chunks(
         settle(kr[r]);
         settle(qr[r]);
         settle(gr[r]);
+        if constexpr (CONV != 0) settle(vr[r]);
     }
 #pragma unroll
     for (int p = 0; p < VPT; ++p) settle(xv[p]);
     settle(bt);
+    if constexpr (CONV != 0) {
+        settle(cw_reg);
+        settle(ch_reg);
+        conv_put();
+    }
 
     int buf = 0;
     while (cur.item >= 0) {
@@ -555,11 +676,20 @@ __device__ __forceinline__ void intra_chunks(
                 return find_chunk(ncid, nh);
             }
         }();
+        // folded conv: the next chunk's slot (its window for a first chunk)
+        const int nslot = CONV != 0 && nxt.item >= 0 ? (cv_slots ? cv_slots[nxt.n] : nxt.n) : -1;
 
         // ---- per-row factors (log2 units); everything derived from k, q, V
         // leaves the registers ----
         if (tid < kChunk) sBeta[tid] = bt;
         if (fthread) {
+            if constexpr (CONV != 0) {
+                conv_rows(vr, 2, C);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) *reinterpret_cast<R4 *>(sV + (4 * r4 + r) * VP + ch0) = vr[r];
+                conv_rows(qr, 0, C);
+                conv_rows(kr, 1, C);
+            }
             // gl: inclusive prefix of g over this lane's 4 rows; ex: the sum over
             // the lanes before it (exclusive row scan); Gs, Ge: Gam at the
             // block's first and last rows; total: Gam at the chunk's last row.
@@ -627,7 +757,7 @@ __device__ __forceinline__ void intra_chunks(
                 *reinterpret_cast<f32x4 *>(Rd + ch0) = d;
             }
         }
-        if constexpr (LD::kStage) {
+        if constexpr (CONV == 0 && LD::kStage) {
 #pragma unroll
             for (int p = 0; p < VPT; ++p) {
                 const int u = tid + p * NTH;
@@ -889,6 +1019,7 @@ __device__ __forceinline__ void intra_chunks(
                       -Tt * *reinterpret_cast<const f32x4 *>(sBeta + tj * kSub + 4 * lg));
         }
         load_row(nxt, 3);
+        conv_fetch(nxt, nslot);
         __syncthreads();
 
         // ---- w and u on the matrix cores, with diag(beta) folded into Tm ----
@@ -963,6 +1094,7 @@ __device__ __forceinline__ void intra_chunks(
         // buffered, the next chunk's factor phase writes only buffers that
         // w and u no longer read, and its first barrier orders everything
         // after it behind this chunk's w and u.
+        conv_put();                                    // the next chunk's taps and halo
         if constexpr (LD::NB == 1) __syncthreads();
         if constexpr (FUSED) {
             // ---- the chunk's state step, wave w < d_v / 16 on its slice:
@@ -1024,15 +1156,18 @@ __device__ __forceinline__ void intra_chunks(
 // SKIP: pass over the chunks of sequences of at most fuse_max chunks (the
 // fused prefill's); a separate instantiation, since the test in the chunk
 // walk costs the plain kernel about a microsecond.
-template <typename E, int DK, int DV, bool SKIP>
+// CONV: 1 or 2 with the short conv folded into the loads (no activation or
+// SiLU); q, k and v are then the raw inputs.
+template <typename E, int DK, int DV, bool SKIP, int CONV>
 __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const int32_t *__restrict__ cu, int T, int N, int H, int c_lo, int c_hi,
-    E *__restrict__ ws, float *__restrict__ ws_dec, int fuse_max) {
+    E *__restrict__ ws, float *__restrict__ ws_dec, int fuse_max, ConvFold<E> cf) {
     FuseArgs fa{};
     fa.fuse_max = fuse_max;
-    intra_chunks<E, DK, DV, false, SKIP>(q, k, v, g, beta, cu, T, N, H, c_lo, c_hi, ws, ws_dec, fa);
+    intra_chunks<E, DK, DV, false, SKIP, CONV>(q, k, v, g, beta, cu, T, N, H, c_lo, c_hi, ws, ws_dec,
+                                               fa, cf);
 }
 
 template <int DK, int DV>
@@ -1429,10 +1564,21 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
         const int c_hi = c_lo + pl.window_chunks < pl.chunk_ids ? c_lo + pl.window_chunks : pl.chunk_ids;
         const long long items = (long long)(c_hi - c_lo) * a.H;
         const int grid = (int)(items < (long long)a.num_cus ? items : (long long)a.num_cus);
-        auto intra = fa.fuse_max >= 0 ? kda_intra_kernel<E, DK, DV, true> : kda_intra_kernel<E, DK, DV, false>;
+        auto intra = fa.fuse_max >= 0 ? kda_intra_kernel<E, DK, DV, true, 0>
+                                      : kda_intra_kernel<E, DK, DV, false, 0>;
+        ConvFold<E> cf{};
+        if constexpr (sizeof(E) == 2 && DK == DV) {
+            if (a.conv) {
+                // the conv folded into the loads; the call never fuses then
+                intra = a.conv->silu ? kda_intra_kernel<E, DK, DV, false, 2>
+                                     : kda_intra_kernel<E, DK, DV, false, 1>;
+                cf = ConvFold<E>{a.conv->weight, static_cast<const E *>(a.conv->window), a.conv->win,
+                                 a.conv->slots, a.conv->num_slots};
+            }
+        }
         intra<<<dim3(grid), dim3(kIntraThreads), 0, stream>>>(
             static_cast<const E *>(a.q), static_cast<const E *>(a.k), static_cast<const E *>(a.v),
-            a.g, a.beta, a.cu_seqlens, a.T, a.N, a.H, c_lo, c_hi, ws, ws_dec, fa.fuse_max);
+            a.g, a.beta, a.cu_seqlens, a.T, a.N, a.H, c_lo, c_hi, ws, ws_dec, fa.fuse_max, cf);
         // A failed intra launch leaves stale records: the scan must not run
         // on them and overwrite o and the caller's states.
         hipError_t e = hipGetLastError();
@@ -1441,6 +1587,11 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
         e = scan_window(c_lo, c_hi);
         if (e != hipSuccess) return e;
         mark();
+    }
+    if (a.conv) {
+        // each sequence's conv window, now that no intra-chunk launch reads it
+        const hipError_t e = launch_conv_window<E, DK, DV>(*a.conv, stream);
+        if (e != hipSuccess) return e;
     }
     if constexpr (sizeof(E) == 2) {
         if (fa.fuse_max >= 0) {

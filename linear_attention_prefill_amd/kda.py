@@ -265,9 +265,9 @@ def prefill_fuse_chunks(T, N, H, d_k, d_v, dtype=torch.bfloat16, fuse_chunks=0) 
 
 
 def prefill_workspace_size(T, N, H, d_k, d_v, dtype=torch.bfloat16, conv=False,
-                           window_chunks=0) -> int:
+                           window_chunks=0, fuse_chunks=0) -> int:
     d = make_desc(T, N, H, d_k, d_v, N, _io_code(dtype), conv_mode=1 if conv else 0,
-                  window_chunks=window_chunks)
+                  window_chunks=window_chunks, fuse_chunks=fuse_chunks)
     return int(load_library().kda_prefill_workspace_size(ctypes.byref(d)))
 
 

@@ -264,13 +264,22 @@ def test_prefill_conv_rejects_bad_arguments(lib):
 
 
 def test_conv_workspace_size(lib):
+    """The convolved q, k, v take workspace only when the conv runs as a pass
+    of its own: fp32, d_k != d_v, or a call that fuses sequences (bf16 with
+    d_k = d_v and nothing fused folds the conv into the intra-chunk loads)."""
     up = lambda x: (x + 255) // 256 * 256
-    for T, H, dk, dv, io, es in [(8192, 32, 128, 128, K.KDA_BF16, 2), (77, 3, 128, 64, K.KDA_F32, 4)]:
-        d0 = K.make_desc(T, 2, H, dk, dv, 2, io, 1.0)
-        d1 = K.make_desc(T, 2, H, dk, dv, 2, io, 1.0, conv_mode=1)
-        extra = 256 + 2 * up(T * H * dk * es) + up(T * H * dv * es)
+    cases = [(8192, 2, 32, 128, 128, K.KDA_BF16, 2, 0, False),
+             (8192, 2, 32, 128, 128, K.KDA_BF16, 2, 1, True),      # fuse one-chunk sequences
+             (8192, 128, 32, 128, 128, K.KDA_BF16, 2, 0, True),    # short: fused by default
+             (8192, 128, 32, 64, 64, K.KDA_BF16, 2, -1, False),
+             (77, 2, 3, 128, 64, K.KDA_BF16, 2, 0, True),
+             (77, 2, 3, 128, 64, K.KDA_F32, 4, 0, True)]
+    for T, N, H, dk, dv, io, es, fuse, pass_of_own in cases:
+        d0 = K.make_desc(T, N, H, dk, dv, N, io, 1.0, fuse_chunks=fuse)
+        d1 = K.make_desc(T, N, H, dk, dv, N, io, 1.0, conv_mode=1, fuse_chunks=fuse)
+        extra = 256 + 2 * up(T * H * dk * es) + up(T * H * dv * es) if pass_of_own else 0
         assert (lib.kda_prefill_workspace_size(ctypes.byref(d1))
-                == lib.kda_prefill_workspace_size(ctypes.byref(d0)) + extra)
+                == lib.kda_prefill_workspace_size(ctypes.byref(d0)) + extra), (T, N, H, dk, dv, io, fuse)
 
 
 def _decode_conv(lib, mode=1, conv="ok", **kw):

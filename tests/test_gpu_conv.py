@@ -23,7 +23,7 @@ pytestmark = [pytest.mark.gpu,
 
 
 def run_prefill_conv(c, weight, window_dev, dt, act, strides=(0, 0, 0, 0), o_init=None,
-                     pool=None, fuse_chunks=0):
+                     pool=None, fuse_chunks=0, window_chunks=0):
     q, k, v = dev(c.q, dt), dev(c.k, dt), dev(c.v, dt)
     o = dev(o_init, dt) if o_init is not None else torch.zeros((c.T, c.H, c.d_v), dtype=dt,
                                                                 device="cuda")
@@ -31,7 +31,7 @@ def run_prefill_conv(c, weight, window_dev, dt, act, strides=(0, 0, 0, 0), o_ini
     lap.chunk_prefill(q, k, v, dev(c.g), dev(c.beta), dev(c.cu_seqlens), state_in=p, state_out=p,
                       o=o, slots=dev(c.slots), num_slots=c.state_pool.shape[0], scale=c.scale,
                       conv_weight=dev(weight), conv_window=window_dev, conv_activation=act,
-                      conv_strides=strides, fuse_chunks=fuse_chunks)
+                      conv_strides=strides, fuse_chunks=fuse_chunks, window_chunks=window_chunks)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), p.cpu().numpy()
 
@@ -68,6 +68,31 @@ def test_prefill_conv_parity(dk, dv, io, act, fuse):
     np.testing.assert_array_equal(win_g, win_r.astype(np.float32))
     cu = c.cu_seqlens
     assert np.all(o_g[cu[4]:cu[5]] == 2.0)          # padded sequence untouched
+
+
+@pytest.mark.parametrize("d,act,window_chunks", [(128, "silu", 0), (128, "none", 3), (64, "silu", 0)])
+def test_folded_conv_matches_conv_pass_bit_for_bit(d, act, window_chunks):
+    """bf16 with d_k = d_v: with nothing fused the conv is folded into the
+    intra-chunk kernel's loads; fuse_chunks = 1 on sequences that all exceed
+    one chunk fuses none of them but runs the conv as a pass of its own.  The
+    fold rounds each convolved row to bf16 as the pass writes it, so o, the
+    states and the windows agree bit for bit (window_chunks = 3: the records
+    of several windows, the conv windows read by every one of them)."""
+    lengths = [65, 130, 64 * 5 + 7, 200, 66, 129]
+    S = 9
+    slots = [3, 0, -1, 8, 5, 20]                    # a padded and an out-of-range slot
+    c = W.random_case(231 + d, lengths, H=4, d_k=d, d_v=d, io_dtype="bf16", num_slots=S,
+                      slots=slots, scale=0.7)
+    weight, window = W.draw_conv(232 + d, S, 4, d, d, "bf16")
+    dt = torch.bfloat16
+    announce("prefill conv fold vs pass %s act=%s window_chunks=%d" % (c.name, act, window_chunks))
+    assert lap.prefill_fuse_chunks(c.T, c.N, c.H, d, d, fuse_chunks=-1) == -1
+    w1, w2 = dev(window, dt), dev(window, dt)
+    o1, p1 = run_prefill_conv(c, weight, w1, dt, act, fuse_chunks=-1, window_chunks=window_chunks)
+    o2, p2 = run_prefill_conv(c, weight, w2, dt, act, fuse_chunks=1, window_chunks=window_chunks)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(p1, p2)
+    np.testing.assert_array_equal(w1.float().cpu().numpy(), w2.float().cpu().numpy())
 
 
 def _tap_major(window, H, dk, dv):
