@@ -473,16 +473,23 @@ __device__ __forceinline__ void intra_chunks(
             }
             // one channel at a time: its four taps and seven inputs
             const float *const wp = sCv + p * kConvTaps * 16 + 4 * lg;
+            float t[4][4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const float w0 = wp[c], w1 = wp[16 + c], w2 = wp[32 + c], w3 = wp[48 + c];
                 const float xs[7] = {(float)m3[c],   (float)m2[c],   (float)m1[c],  (float)x[0][c],
                                      (float)x[1][c], (float)x[2][c], (float)x[3][c]};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float t = conv_act(conv4(w0, w1, w2, w3, xs[r], xs[r + 1], xs[r + 2], xs[r + 3]), CONV == 2);
-                    x[r][c] = (E)(4 * r4 + r < C ? t : 0.f);
-                }
+                for (int r = 0; r < 4; ++r)
+                    t[r][c] = conv_act(conv4(w0, w1, w2, w3, xs[r], xs[r + 1], xs[r + 2], xs[r + 3]), CONV == 2);
+            }
+            // rounded a row at a time; a row past the chunk's end is zero
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                R4 y;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) y[c] = (E)t[r][c];
+                x[r] = 4 * r4 + r < C ? y : R4{};
             }
         }
     };
