@@ -41,10 +41,12 @@ def run_prefill_conv(c, weight, window_dev, dt, act, strides=(0, 0, 0, 0), o_ini
                                                (64, 128, "bf16", "none", -1),
                                                (128, 64, "f32", "silu", -1),
                                                (128, 128, "bf16", "silu", 1),
-                                               (64, 64, "bf16", "none", 64)])
+                                               (64, 64, "bf16", "none", 64),
+                                               (64, 64, "bf16", "silu", -1)])
 def test_prefill_conv_parity(dk, dv, io, act, fuse):
     """fuse: bf16 sequences of at most this many chunks run in the fused
-    prefill on the convolved inputs (1: the short ones; 64: all)."""
+    prefill on the convolved inputs (1: the short ones; 64: all).  bf16 with
+    d_k = d_v and fuse = -1 folds the conv into the intra-chunk kernel."""
     lengths = [0, 1, 2, 3, 63, 64, 65, 130, 5]
     S = 12
     slots = [3, 0, 7, 11, -1, 5, 9, 2, 13]
