@@ -616,6 +616,26 @@ __device__ __forceinline__ void intra_chunks(
     ChunkRef cur;
     FChain ch{-1, 0, 0, 0, 0, 0, 0};
     int jcur = 0;
+    // Chain change, part q of 4: key tiles q KT/4 .. (q+1) KT/4 - 1 of the
+    // finished chain pch go out and the same tiles of chain ch come in.
+    // Spread over four phases, the state's 64 KB each way share the CU's
+    // memory pipeline with the phases' own traffic instead of arriving as
+    // one burst between two chunks.
+    FChain pch{-1, 0, 0, 0, 0, 0, 0};
+    bool pend = false;
+    auto state_swap = [&](int q) {
+        if constexpr (FUSED) {
+            if (!pend || wave >= VT) return;
+            float *dst = fa.state_out ? const_cast<float *>(state_at(fa.state_out, pch)) : nullptr;
+            const float *src = fa.state_in && ch.c >= 0 ? state_at(fa.state_in, ch) : nullptr;
+#pragma unroll
+            for (int u = 0; u < KT / 4; ++u) {
+                const int t = q * (KT / 4) + u;
+                if (dst) *reinterpret_cast<f32x4 *>(dst + t * kSub) = S[t];
+                S[t] = src ? *reinterpret_cast<const f32x4 *>(src + t * kSub) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    };
     if constexpr (FUSED) {
         ch = next_chain((int)blockIdx.x);
         cur = item_of(ch, 0);
@@ -778,6 +798,7 @@ __device__ __forceinline__ void intra_chunks(
         load_v(nxt);
         load_beta(nxt);
         load_row(nxt, 0);
+        state_swap(0);
         __syncthreads();
 
         // ---- A_kk and A_qk blocks, transposed products: lane (i, g) receives
@@ -925,6 +946,7 @@ __device__ __forceinline__ void intra_chunks(
             }
         }
         load_row(nxt, 1);
+        state_swap(1);
         __syncthreads();   // sA holds A_kk below the diagonal and the diagonal inverses
 
         // Q e^Gam = (q P) e^{Gam_s} in the scan's fragment order: fragment
@@ -989,6 +1011,7 @@ __device__ __forceinline__ void intra_chunks(
                           *reinterpret_cast<const f32x4 *>(sBeta + I * kSub + 4 * lg));
         }
         load_row(nxt, 2);
+        state_swap(2);
         __syncthreads();
         // level 2 (waves 0..3, output tile (ti, tj)), straight into the Tm
         // diag(beta) fragments (2 + ti, 0): Tm[32:64, 0:32] = -Tm_hi (A[32:64, 0:32] Tm_lo).
@@ -1027,6 +1050,8 @@ __device__ __forceinline__ void intra_chunks(
         }
         load_row(nxt, 3);
         conv_fetch(nxt, nslot);
+        state_swap(3);
+        pend = false;
         __syncthreads();
 
         // ---- w and u on the matrix cores, with diag(beta) folded into Tm ----
@@ -1148,15 +1173,18 @@ __device__ __forceinline__ void intra_chunks(
                     if (m * kSub + li < C) store4<E>(orow + (size_t)m * kSub * H * DV, O[m] * fa.scale);
             }
             __syncthreads();   // the next chunk's factor phase rewrites every operand
-            if (nj == 0) {     // the chain is done: its state out, the next chain's in
-                state_store(ch);
-                ch = nch_ch;
-                if (ch.c >= 0) state_load(ch);
+            if (nj == 0) {     // the chain is done: its state goes out and the next
+                pch = ch;      // chain's comes in a quarter at a time over the next
+                ch = nch_ch;   // chunk's first four phases (state_swap)
+                pend = true;
             }
             jcur = nj;
         }
         buf ^= LD::NB - 1;
         cur = nxt;
+    }
+    if constexpr (FUSED) {
+        if (pend) state_store(pch);   // the last chain's state (no chunk followed it)
     }
 }
 
