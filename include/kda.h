@@ -70,7 +70,7 @@ typedef enum {
     KDA_ERR_DTYPE = 3,       /* unknown io dtype */
     KDA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
     KDA_ERR_WORKSPACE = 5,   /* workspace missing or too small */
-    KDA_ERR_UNSUPPORTED = 6, /* d_k or d_v not 64 or 128 */
+    KDA_ERR_UNSUPPORTED = 6, /* d_k or d_v not 64 or 128; phase clocks not built in */
     KDA_ERR_HIP = 7,         /* a kernel launch failed */
     KDA_ERR_TOO_LARGE = 8    /* the call needs more than the static scratch holds */
 } kda_status_t;
@@ -416,6 +416,39 @@ kda_status_t kda_chunk_prefill_static(const void *q, const void *k, const void *
 enum { KDA_CHECK_CU_SEQLENS = 1, KDA_CHECK_G = 2, KDA_CHECK_SLOTS = 4 };
 kda_status_t kda_prefill_check(const float *g, const int32_t *cu_seqlens, const int32_t *slots,
                                const kda_prefill_desc_t *desc, int32_t *flags, void *stream);
+
+/*
+ * Phase clocks, for attributing the prefill's time to the phases inside its
+ * kernels from the kernels' own timestamps, as the "kern" page, section "The
+ * harness", attributes time to every call inside the real program.  Only a
+ * library built with KDA_PHASE_CLOCKS records them (python -m
+ * linear_attention_prefill_amd.build --phase-clocks writes
+ * libkda_clocks.so, the same kernels plus the records); any other build
+ * returns KDA_ERR_UNSUPPORTED and touches nothing.
+ *
+ * In such a build, lane 0 of each of the 8 waves of workgroup 0 of the
+ * intra-chunk kernel (kernel = KDA_CLOCK_INTRA) or of the fused prefill
+ * (KDA_CLOCK_FUSED) writes the core clock counter (s_memtime) at each mark
+ * of its first KDA_CLOCK_ITEMS items (chunks, for the fused kernel) into a
+ * device array laid out [wave][item][mark], KDA_CLOCK_MARKS marks an item;
+ * a mark not reached stays as it was (0 after a clear).  Marks: 0 the top
+ * of the item; 1 and 2 before and after the barrier that ends the factor
+ * phase; 3, 4 around the one after the A blocks; 5, 6 after the first
+ * inverse level; 7, 8 after the second; 9, 10 after w and u (the fp32 and
+ * fused builds' barrier there); fused only: 11, 12 around the barrier after
+ * the state step, 13 after the chain bookkeeping.  Later launches overwrite
+ * the array.
+ *
+ * kda_phase_clocks copies the first `count` words (at most 8 * 64 * 16) of
+ * that kernel's array to host_out (when not NULL), then zeroes the whole
+ * array when `clear` is nonzero.  Synchronous (a blocking copy): call it
+ * once the launches to read are done.  Errors: KDA_ERR_SHAPE for an unknown
+ * kernel, KDA_ERR_UNSUPPORTED without the records, KDA_ERR_HIP if the copy
+ * fails.
+ */
+enum { KDA_CLOCK_INTRA = 0, KDA_CLOCK_FUSED = 1, KDA_CLOCK_WAVES = 8, KDA_CLOCK_ITEMS = 64,
+       KDA_CLOCK_MARKS = 16 };
+kda_status_t kda_phase_clocks(int32_t kernel, uint64_t *host_out, size_t count, int32_t clear);
 
 /*
  * Static description of a status code.  Every call validates its arguments

@@ -19,6 +19,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
+# The same kernels with phase clocks recorded (kda_phase_clocks); built only
+# on request, never loaded by the library's own calls.
+CLOCKS_LIB = os.path.join(PKG, "libkda_clocks.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["kda_prefill.hip", "kda_decode.hip", "kda_conv.hip", "kda_check.hip"]
@@ -64,19 +67,23 @@ def _rocm() -> str:
     return os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
-def build(resource_usage: bool = False, verbose: bool = False) -> str:
+def build(resource_usage: bool = False, verbose: bool = False, phase_clocks: bool = False) -> str:
+    """Build libkda.so, or with phase_clocks libkda_clocks.so (-DKDA_PHASE_CLOCKS)."""
     hipcc = _hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    bdir = BUILD + ("_clocks" if phase_clocks else "")
+    lib = CLOCKS_LIB if phase_clocks else LIB
+    extra = ["-DKDA_PHASE_CLOCKS"] if phase_clocks else []
+    os.makedirs(bdir, exist_ok=True)
     jobs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
-        cmd = [hipcc, "-x", "hip", "--offload-arch=" + ARCH, *COMMON, *DEVICE_FLAGS,
+        obj = os.path.join(bdir, src + ".o")
+        cmd = [hipcc, "-x", "hip", "--offload-arch=" + ARCH, *COMMON, *DEVICE_FLAGS, *extra,
                *PER_SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if resource_usage:
             cmd.append("-Rpass-analysis=kernel-resource-usage")
         jobs.append((src, obj, cmd))
     for src in CXX_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(bdir, src + ".o")
         cmd = [hipcc, "-x", "c++", *COMMON, "-D__HIP_PLATFORM_AMD__",
                "-I" + os.path.join(_rocm(), "include"), "-c",
                os.path.join(CSRC, src), "-o", obj]
@@ -93,18 +100,20 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = lib + ".tmp%d" % os.getpid()
     link = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp,
             *[obj for _, obj, _ in jobs]]
     subprocess.check_call(link)
-    os.replace(tmp, LIB)
-    with open(HASH_FILE, "w") as fh:          # which sources this library was built from
+    os.replace(tmp, lib)
+    with open(lib + ".srchash", "w") as fh:   # which sources this library was built from
         fh.write(source_hash() + "\n")
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--resource-usage", action="store_true")
+    ap.add_argument("--phase-clocks", action="store_true",
+                    help="build libkda_clocks.so, whose kernels record phase clocks (kda_phase_clocks)")
     args = ap.parse_args()
-    print(build(resource_usage=args.resource_usage))
+    print(build(resource_usage=args.resource_usage, phase_clocks=args.phase_clocks))

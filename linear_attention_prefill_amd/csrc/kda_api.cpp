@@ -436,7 +436,9 @@ const char *kda_status_string(kda_status_t status) {
         case KDA_ERR_DTYPE: return "unknown io dtype";
         case KDA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case KDA_ERR_WORKSPACE: return "workspace too small";
-        case KDA_ERR_UNSUPPORTED: return "d_k and d_v must be 64 or 128";
+        case KDA_ERR_UNSUPPORTED:
+            return "unsupported: d_k and d_v must be 64 or 128 (phase clocks: a library built with "
+                   "KDA_PHASE_CLOCKS)";
         case KDA_ERR_HIP: return "a HIP kernel launch failed";
         case KDA_ERR_TOO_LARGE:
             return "the call needs more workspace than the static scratch holds "
@@ -445,6 +447,19 @@ const char *kda_status_string(kda_status_t status) {
     return "unknown status";
 }
 
-int32_t kda_version(void) { return 106; }
+static_assert(KDA_CLOCK_WAVES == kda::kClockWaves && KDA_CLOCK_ITEMS == kda::kClockItems &&
+                  KDA_CLOCK_MARKS == kda::kClockMarks,
+              "phase clock layout");
+
+kda_status_t kda_phase_clocks(int32_t kernel, uint64_t *host_out, size_t count, int32_t clear) {
+    if (kernel != KDA_CLOCK_INTRA && kernel != KDA_CLOCK_FUSED) return KDA_ERR_SHAPE;
+    static_assert(sizeof(uint64_t) == sizeof(unsigned long long), "clock words");
+    const hipError_t e = kda::phase_clocks_copy(kernel, reinterpret_cast<unsigned long long *>(host_out),
+                                                host_out ? count : 0, clear != 0);
+    if (e == hipErrorNotSupported) return KDA_ERR_UNSUPPORTED;
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int32_t kda_version(void) { return 107; }
 
 }  // extern "C"

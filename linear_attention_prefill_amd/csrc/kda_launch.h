@@ -115,6 +115,13 @@ hipError_t launch_prefill_check(const float *g, const int32_t *cu, const int32_t
                                 int N, int H, int dk, int num_slots, int32_t *flags,
                                 hipStream_t stream);
 
+// Phase clocks of the intra-chunk and fused kernels (kda_phase_clocks):
+// workgroup 0's waves record the core clock counter at each phase boundary
+// of their first kClockItems items, in a library built with
+// KDA_PHASE_CLOCKS; other builds return hipErrorNotSupported.
+constexpr int kClockWaves = 8, kClockItems = 64, kClockMarks = 16;
+hipError_t phase_clocks_copy(int kernel, unsigned long long *host, size_t count, bool clear);
+
 // Device address of the static scratch that backs kda_chunk_prefill_static
 // on the device `stream` runs on (looked up on the first call per device).
 hipError_t static_scratch(hipStream_t stream, void **ptr);

@@ -68,6 +68,11 @@ namespace kda {
 // computed exactly instead of with split factors.
 constexpr float kDiagSpanLimit = 64.f;
 constexpr int kIntraThreads = 512;     // 8 waves: two per SIMD
+static_assert(kIntraThreads / 64 == kClockWaves, "one clock row per wave");
+#ifdef KDA_PHASE_CLOCKS
+// [kernel: 0 intra-chunk, 1 fused][wave][item][mark] core clock counts
+__device__ unsigned long long g_phase_clock[2 * kClockWaves * kClockItems * kClockMarks];
+#endif
 constexpr int kCuCache = 256;          // sequence bounds kept in LDS when N < this
 constexpr int kScanWarmAhead = 2;      // chunks between a scan stage's record and the one it warms
 #ifndef KDA_SINGLE_CHAIN
@@ -671,8 +676,21 @@ __device__ __forceinline__ void intra_chunks(
         conv_put();
     }
 
+    // Phase clocks (a KDA_PHASE_CLOCKS build only): lane 0 of each wave of
+    // workgroup 0 records the core clock counter at mark i of item clk_it.
+    int clk_it = 0;
+    auto clock_mark = [&](int i) {
+#ifdef KDA_PHASE_CLOCKS
+        if (blockIdx.x == 0 && lane == 0 && clk_it < kClockItems)
+            g_phase_clock[(((FUSED ? 1 : 0) * kClockWaves + wave) * kClockItems + clk_it) * kClockMarks + i] =
+                __builtin_amdgcn_s_memtime();
+#else
+        (void)i;
+#endif
+    };
     int buf = 0;
     while (cur.item >= 0) {
+        clock_mark(0);
         E *const sKP = sKPb + buf * (kChunk * KPP);
         E *const sV = sVb + buf * LD::V_ELEMS;
         float *const sBs = sBsb + buf * (4 * DK);
@@ -799,7 +817,9 @@ __device__ __forceinline__ void intra_chunks(
         load_beta(nxt);
         load_row(nxt, 0);
         state_swap(0);
+        clock_mark(1);
         __syncthreads();
+        clock_mark(2);
 
         // ---- A_kk and A_qk blocks, transposed products: lane (i, g) receives
         // A[16I + i][16J + 4g + r] ----
@@ -947,7 +967,9 @@ __device__ __forceinline__ void intra_chunks(
         }
         load_row(nxt, 1);
         state_swap(1);
+        clock_mark(3);
         __syncthreads();   // sA holds A_kk below the diagonal and the diagonal inverses
+        clock_mark(4);
 
         // Q e^Gam = (q P) e^{Gam_s} in the scan's fragment order: fragment
         // (m, s) holds row 16m + i, channels 32s + kk(g, e).
@@ -1012,7 +1034,9 @@ __device__ __forceinline__ void intra_chunks(
         }
         load_row(nxt, 2);
         state_swap(2);
+        clock_mark(5);
         __syncthreads();
+        clock_mark(6);
         // level 2 (waves 0..3, output tile (ti, tj)), straight into the Tm
         // diag(beta) fragments (2 + ti, 0): Tm[32:64, 0:32] = -Tm_hi (A[32:64, 0:32] Tm_lo).
         // Meanwhile waves 4..7 write K e^{Gam_C - Gam}, or, fused, Q e^Gam.
@@ -1052,7 +1076,9 @@ __device__ __forceinline__ void intra_chunks(
         conv_fetch(nxt, nslot);
         state_swap(3);
         pend = false;
+        clock_mark(7);
         __syncthreads();
+        clock_mark(8);
 
         // ---- w and u on the matrix cores, with diag(beta) folded into Tm ----
         // fragment (m, s) of Tm diag(beta): row 16 m + i, columns 32 s + kk(g, e)
@@ -1127,7 +1153,9 @@ __device__ __forceinline__ void intra_chunks(
         // w and u no longer read, and its first barrier orders everything
         // after it behind this chunk's w and u.
         conv_put();                                    // the next chunk's taps and halo
+        clock_mark(9);
         if constexpr (LD::NB == 1) __syncthreads();
+        clock_mark(10);
         if constexpr (FUSED) {
             // ---- the chunk's state step, wave w < d_v / 16 on its slice:
             // U = u - w S, O = Q~ S + A_qk U, S = diag(e^{Gam_C}) S + K~^T U,
@@ -1172,16 +1200,20 @@ __device__ __forceinline__ void intra_chunks(
                 for (int m = 0; m < 4; ++m)
                     if (m * kSub + li < C) store4<E>(orow + (size_t)m * kSub * H * DV, O[m] * fa.scale);
             }
+            clock_mark(11);
             __syncthreads();   // the next chunk's factor phase rewrites every operand
+            clock_mark(12);
             if (nj == 0) {     // the chain is done: its state goes out and the next
                 pch = ch;      // chain's comes in a quarter at a time over the next
                 ch = nch_ch;   // chunk's first four phases (state_swap)
                 pend = true;
             }
             jcur = nj;
+            clock_mark(13);
         }
         buf ^= LD::NB - 1;
         cur = nxt;
+        ++clk_it;
     }
     if constexpr (FUSED) {
         if (pend) state_store(pch);   // the last chain's state (no chunk followed it)
@@ -1752,5 +1784,31 @@ KDA_INST(float, 64, 128)
 KDA_INST(float, 128, 64)
 KDA_INST(float, 128, 128)
 #undef KDA_INST
+
+// ---------------------------------------------------------------------------
+// Phase clocks (instrumented builds)
+// ---------------------------------------------------------------------------
+
+hipError_t phase_clocks_copy(int kernel, unsigned long long *host, size_t count, bool clear) {
+#ifdef KDA_PHASE_CLOCKS
+    constexpr size_t per = (size_t)kClockWaves * kClockItems * kClockMarks;
+    if (kernel < 0 || kernel > 1) return hipErrorInvalidValue;
+    const size_t off = (size_t)kernel * per * sizeof(unsigned long long);
+    if (host && count) {
+        const hipError_t e = hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_clock),
+                                                 (count < per ? count : per) * sizeof(unsigned long long), off,
+                                                 hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return e;
+    }
+    if (clear) {
+        static const unsigned long long zeros[per] = {};
+        return hipMemcpyToSymbol(HIP_SYMBOL(g_phase_clock), zeros, sizeof(zeros), off, hipMemcpyHostToDevice);
+    }
+    return hipSuccess;
+#else
+    (void)kernel; (void)host; (void)count; (void)clear;
+    return hipErrorNotSupported;
+#endif
+}
 
 }  // namespace kda

@@ -15,6 +15,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkda.so")
+# The same kernels with phase clocks recorded (``build --phase-clocks``).
+CLOCKS_LIB_PATH = os.path.join(_PKG, "libkda_clocks.so")
 
 KDA_F32 = 0
 KDA_BF16 = 1
@@ -105,6 +107,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_version.restype = i32
     lib.kda_version.argtypes = []
+    lib.kda_phase_clocks.restype = ctypes.c_int
+    lib.kda_phase_clocks.argtypes = [i32, vp, sz, i32]
     if path is None:
         _lib = lib
     return lib
@@ -499,3 +503,21 @@ def decode_tokens(q, k, v, g, beta, state_pool, slots, o=None, num_accepted=None
                                  H, dk, dv, num_slots, io, float(scale), 1 if commit else 0,
                                  int(state_slot_stride), int(state_head_stride), _stream(stream)))
     return o
+
+
+# kda.h: KDA_CLOCK_* (the layout of kda_phase_clocks)
+KDA_CLOCK_INTRA, KDA_CLOCK_FUSED = 0, 1
+CLOCK_WAVES, CLOCK_ITEMS, CLOCK_MARKS = 8, 64, 16
+
+
+def phase_clocks(kernel: int, clear: bool = False):
+    """Phase clocks of workgroup 0 of the intra-chunk kernel (KDA_CLOCK_INTRA)
+    or the fused prefill (KDA_CLOCK_FUSED) (``kda_phase_clocks``): an int64
+    array [wave][item][mark] of core clock counts, 0 where not reached.
+    Needs the library built with phase clocks (``load_library(CLOCKS_LIB_PATH)``
+    first); raises KdaError (KDA_ERR_UNSUPPORTED) otherwise."""
+    import numpy as np
+    buf = np.zeros(CLOCK_WAVES * CLOCK_ITEMS * CLOCK_MARKS, dtype=np.uint64)
+    _check(load_library().kda_phase_clocks(int(kernel), buf.ctypes.data, buf.size, 1 if clear else 0))
+    return buf.astype(np.int64).reshape(CLOCK_WAVES, CLOCK_ITEMS, CLOCK_MARKS)
+

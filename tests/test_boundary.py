@@ -48,7 +48,7 @@ def test_header_declares_expected_entry_points():
               "kda_status_string", "kda_version", "kda_chunk_prefill_timed",
               "kda_decode_step_lines", "kda_decode_tokens", "kda_chunk_prefill_conv",
               "kda_decode_step_conv", "kda_prefill_check", "kda_chunk_prefill_static",
-              "kda_prefill_windows", "kda_prefill_fuse_chunks"):
+              "kda_prefill_windows", "kda_prefill_fuse_chunks", "kda_phase_clocks"):
         assert n in names
 
 
@@ -58,11 +58,43 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 106
+    assert lib.kda_version() == 107
     for code in range(9):
         s = lib.kda_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.kda_status_string(99).decode() == "unknown status"
+
+
+def test_phase_clocks_need_the_instrumented_build(lib):
+    """libkda.so records no phase clocks: kda_phase_clocks says so before any
+    HIP call (an unknown kernel is a shape error first)."""
+    import numpy as np
+    buf = np.full(16, 7, dtype=np.uint64)
+    assert lib.kda_phase_clocks(K.KDA_CLOCK_INTRA, buf.ctypes.data, buf.size, 1) == 6
+    assert lib.kda_phase_clocks(K.KDA_CLOCK_FUSED, None, 0, 0) == 6
+    assert lib.kda_phase_clocks(2, buf.ctypes.data, buf.size, 0) == 2
+    assert np.all(buf == 7)
+
+
+def test_phase_clock_build_records_the_phases():
+    """The instrumented build differs only by the records: its kernels read
+    the core clock counter (s_memtime) at every mark, libkda.so's never."""
+    import subprocess
+    import tempfile
+    from linear_attention_prefill_amd import build
+    src = os.path.join(build.CSRC, "kda_prefill.hip")
+    outs = {}
+    for tag, extra in (("plain", []), ("clocks", ["-DKDA_PHASE_CLOCKS"])):
+        with tempfile.TemporaryDirectory() as td:
+            asm = os.path.join(td, "p.s")
+            subprocess.check_call([build._hipcc(), "-x", "hip", "--offload-arch=" + build.ARCH,
+                                   *build.COMMON, *build.DEVICE_FLAGS,
+                                   *build.PER_SOURCE_FLAGS["kda_prefill.hip"], *extra,
+                                   "--cuda-device-only", "-S", src, "-o", asm],
+                                  stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+            outs[tag] = open(asm).read()
+    assert "s_memtime" not in outs["plain"]
+    assert outs["clocks"].count("s_memtime") >= 2 * 13
 
 
 def _desc(**kw):
