@@ -27,7 +27,11 @@ Prints ONE JSON line.  Besides the throughput it reports:
                 without them); `traffic` is that kernel's HBM bytes from the
                 rocprofv3 FETCH_SIZE / WRITE_SIZE counters per step
                 (profiles/traffic.json, reported while the kernel sources
-                match), `traffic_ratio` their ratio to the algorithmic bytes;
+                match), `traffic_ratio` their ratio to the algorithmic bytes,
+                and with it `traffic_GBs` and `traffic_frac_of_copy`, the
+                counter bytes' rate against the copy ceiling below;
+  ceilings      what plain streaming (kda_stream_probe) reaches on this chip
+                in the same run: read, copy and in-place update of 512 MiB;
   path          the whole step against the HBM roof and the bf16 MFMA roof;
   intra_mfma    the intra-chunk contractions' algorithmic flops over the
                 intra kernel's time, against the bf16 matrix-core peak;
@@ -314,6 +318,46 @@ def time_decode_tokens(case, steps, warmup, copies, torch, lap, only=None):
         res[name] = {"us": ms * 1e3, "bytes": nbytes, "GB/s": nbytes / (ms * 1e-3) / 1e9,
                      "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "tokens/s": N * T / (ms * 1e-3)}
+    return res
+
+
+def stream_ceilings(torch, lap, mib=512, grids=(256, 384, 512), reps=10):
+    """What plain streaming reaches on this chip (``kda_stream_probe``: 16-byte
+    nontemporal grid-stride loops): a read, a copy and an in-place update of
+    `mib` MiB, rotating over three buffers so that the 256 MB MALL cannot
+    serve a repeat, each the best over `grids` (workgroups of 256 threads;
+    the rate varies with the grid by up to 20%, and falls off above 768).
+    GB/s of bytes moved (a copy and an update move the buffer twice)."""
+    n = mib << 20
+    bufs = [torch.ones(n // 4, dtype=torch.float32, device="cuda") for _ in range(3)]
+    sink = torch.empty(4 * max(grids), dtype=torch.uint8, device="cuda")
+    K = lap.kda
+    res = {"buffer_MiB": mib, "grids": list(grids), "kernel": "kda_stream_probe"}
+    for name, mode, moved in (("read", K.KDA_STREAM_READ, 1), ("copy", K.KDA_STREAM_COPY, 2),
+                              ("update", K.KDA_STREAM_UPDATE, 2)):
+        best = (0.0, 0)
+        for grid in grids:
+            def run(i):
+                a, b = bufs[i % 3], bufs[(i + 1) % 3]
+                if mode == K.KDA_STREAM_READ:
+                    K.stream_probe(mode, a, sink, grid)
+                elif mode == K.KDA_STREAM_COPY:
+                    K.stream_probe(mode, a, b, grid)
+                else:
+                    K.stream_probe(mode, None, a, grid)
+            for i in range(3):
+                run(i)
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record()
+            for i in range(reps):
+                run(i)
+            end.record()
+            torch.cuda.synchronize()
+            gbs = moved * n / (start.elapsed_time(end) / reps * 1e-3) / 1e9
+            best = max(best, (gbs, grid))
+        res[name + "_GBs"], res[name + "_grid"] = best
+    del bufs
     return res
 
 
@@ -605,6 +649,9 @@ def main():
         print(json.dumps(out), flush=True)
         return
 
+    ceil = stream_ceilings(torch, lap)
+    log("streaming ceilings: read %.0f GB/s, copy %.0f GB/s, in-place update %.0f GB/s"
+        % (ceil["read_GBs"], ceil["copy_GBs"], ceil["update_GBs"]))
     t0 = time.time()
     case = {"packed": W.packed_varlen_prefill, "single": W.single_seq_prefill,
             "short": short_seqs_prefill}[args.workload]()
@@ -643,8 +690,14 @@ def main():
         "intra_mfma": head.get("intra_mfma"),
         "kernels": head["kernels"],
         "path": head["path"],
+        "ceilings": ceil,
         "kernel_source_hash": src_hash,
     }
+    if head["roofline"]["traffic"] is not None:
+        # the dominant kernel's counter-measured bytes against the copy ceiling
+        t_dom = head["kernels"][head["roofline"]["kernel"]]["us"] * 1e-6
+        out["roofline"]["traffic_GBs"] = head["roofline"]["traffic"] / t_dom / 1e9
+        out["roofline"]["traffic_frac_of_copy"] = out["roofline"]["traffic_GBs"] / ceil["copy_GBs"]
     slots0 = lambda c: None if c.state_pool is None else c.state_pool[c.slots]
     if not args.no_extra:
         extra = {}

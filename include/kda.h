@@ -451,6 +451,28 @@ enum { KDA_CLOCK_INTRA = 0, KDA_CLOCK_FUSED = 1, KDA_CLOCK_WAVES = 8, KDA_CLOCK_
 kda_status_t kda_phase_clocks(int32_t kernel, uint64_t *host_out, size_t count, int32_t clear);
 
 /*
+ * Streaming bandwidth probe.  The "kern" page, section "Inside", lists perf
+ * among its test harness's checks; here the reference for a kernel's HBM
+ * rate is what plain streaming reaches on the same chip, measured next to it
+ * (bench.py reports it beside each roofline).  Enqueues on `stream` one
+ * grid-stride kernel of `grid` workgroups of 256 threads over `bytes` bytes
+ * (a multiple of 16) with 16-byte nontemporal accesses:
+ *   KDA_STREAM_READ    reads src; dst is a sink of at least 4 grid bytes,
+ *                      written only if the XOR of the data folds to one
+ *                      fixed 32-bit value;
+ *   KDA_STREAM_COPY    copies src to dst (not overlapping);
+ *   KDA_STREAM_UPDATE  multiplies dst, read as fp32, by 1.0001 in place
+ *                      (src unused, may be NULL).
+ * The caller times it (events on `stream`).  Errors: KDA_ERR_SHAPE for an
+ * unknown mode, grid < 1 or bytes not a multiple of 16; KDA_ERR_NULL;
+ * KDA_ERR_ALIGN for pointers not 16-byte aligned; KDA_ERR_HIP if the launch
+ * fails.
+ */
+enum { KDA_STREAM_READ = 0, KDA_STREAM_COPY = 1, KDA_STREAM_UPDATE = 2 };
+kda_status_t kda_stream_probe(int32_t mode, const void *src, void *dst, size_t bytes, int32_t grid,
+                              void *stream);
+
+/*
  * Static description of a status code.  Every call validates its arguments
  * on the host and returns one of these codes before anything launches, as
  * the "kern" page, section "The manifest", rejects a call outside its bounds

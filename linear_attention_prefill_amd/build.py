@@ -24,7 +24,7 @@ LIB = os.path.join(PKG, "libkda.so")
 CLOCKS_LIB = os.path.join(PKG, "libkda_clocks.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["kda_prefill.hip", "kda_decode.hip", "kda_conv.hip", "kda_check.hip"]
+HIP_SOURCES = ["kda_prefill.hip", "kda_decode.hip", "kda_conv.hip", "kda_check.hip", "kda_stream.hip"]
 CXX_SOURCES = ["kda_api.cpp"]
 
 # Packed fp32 VALU ops are disabled for all device code.

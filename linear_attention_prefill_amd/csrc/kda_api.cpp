@@ -460,6 +460,19 @@ kda_status_t kda_phase_clocks(int32_t kernel, uint64_t *host_out, size_t count, 
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status_t kda_stream_probe(int32_t mode, const void *src, void *dst, size_t bytes, int32_t grid,
+                              void *stream) {
+    if (mode < KDA_STREAM_READ || mode > KDA_STREAM_UPDATE || grid < 1 || bytes % 16 != 0)
+        return KDA_ERR_SHAPE;
+    if (!dst || (mode != KDA_STREAM_UPDATE && !src)) return KDA_ERR_NULL;
+    if (!aligned16(dst) || (src && !aligned16(src))) return KDA_ERR_ALIGN;
+    if (bytes == 0) return KDA_OK;
+    (void)hipGetLastError();       // an earlier call's error is not this call's
+    const hipError_t e =
+        kda::launch_stream_probe(mode, src, dst, bytes, grid, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 int32_t kda_version(void) { return 107; }
 
 }  // extern "C"

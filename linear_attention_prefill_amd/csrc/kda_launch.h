@@ -122,6 +122,11 @@ hipError_t launch_prefill_check(const float *g, const int32_t *cu, const int32_t
 constexpr int kClockWaves = 8, kClockItems = 64, kClockMarks = 16;
 hipError_t phase_clocks_copy(int kernel, unsigned long long *host, size_t count, bool clear);
 
+// Streaming bandwidth probe (kda_stream_probe): mode 0 reads src (dst: a
+// sink of 4 grid bytes), 1 copies src to dst, 2 scales dst in place.
+hipError_t launch_stream_probe(int mode, const void *src, void *dst, size_t bytes, int grid,
+                               hipStream_t stream);
+
 // Device address of the static scratch that backs kda_chunk_prefill_static
 // on the device `stream` runs on (looked up on the first call per device).
 hipError_t static_scratch(hipStream_t stream, void **ptr);

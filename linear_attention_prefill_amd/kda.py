@@ -109,6 +109,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_version.argtypes = []
     lib.kda_phase_clocks.restype = ctypes.c_int
     lib.kda_phase_clocks.argtypes = [i32, vp, sz, i32]
+    lib.kda_stream_probe.restype = ctypes.c_int
+    lib.kda_stream_probe.argtypes = [i32, vp, vp, sz, i32, vp]
     if path is None:
         _lib = lib
     return lib
@@ -520,4 +522,19 @@ def phase_clocks(kernel: int, clear: bool = False):
     buf = np.zeros(CLOCK_WAVES * CLOCK_ITEMS * CLOCK_MARKS, dtype=np.uint64)
     _check(load_library().kda_phase_clocks(int(kernel), buf.ctypes.data, buf.size, 1 if clear else 0))
     return buf.astype(np.int64).reshape(CLOCK_WAVES, CLOCK_ITEMS, CLOCK_MARKS)
+
+
+# kda.h: KDA_STREAM_*
+KDA_STREAM_READ, KDA_STREAM_COPY, KDA_STREAM_UPDATE = 0, 1, 2
+
+
+def stream_probe(mode: int, src, dst, grid: int = 1024, stream=None):
+    """One plain streaming kernel (``kda_stream_probe``) over dst's bytes
+    (src's for a read): read src, copy src to dst, or update dst in place.
+    src, dst: contiguous CUDA tensors; for a read dst is the sink (at least
+    4 grid bytes).  Enqueued on `stream` (default: the current stream)."""
+    nbytes = (src if mode != KDA_STREAM_UPDATE else dst).numel() * \
+        (src if mode != KDA_STREAM_UPDATE else dst).element_size()
+    _check(load_library().kda_stream_probe(int(mode), _ptr(src) if src is not None else None,
+                                           _ptr(dst), nbytes, int(grid), _stream(stream)))
 

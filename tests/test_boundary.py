@@ -48,7 +48,8 @@ def test_header_declares_expected_entry_points():
               "kda_status_string", "kda_version", "kda_chunk_prefill_timed",
               "kda_decode_step_lines", "kda_decode_tokens", "kda_chunk_prefill_conv",
               "kda_decode_step_conv", "kda_prefill_check", "kda_chunk_prefill_static",
-              "kda_prefill_windows", "kda_prefill_fuse_chunks", "kda_phase_clocks"):
+              "kda_prefill_windows", "kda_prefill_fuse_chunks", "kda_phase_clocks",
+              "kda_stream_probe"):
         assert n in names
 
 
@@ -95,6 +96,21 @@ def test_phase_clock_build_records_the_phases():
             outs[tag] = open(asm).read()
     assert "s_memtime" not in outs["plain"]
     assert outs["clocks"].count("s_memtime") >= 2 * 13
+
+
+def test_stream_probe_rejects_bad_arguments(lib):
+    """Host checks of kda_stream_probe, all before any launch (bytes = 0 with
+    valid arguments launches nothing)."""
+    A16, B16 = 0x1000, 0x2000
+    assert lib.kda_stream_probe(3, A16, B16, 1 << 20, 1024, None) == 2       # mode
+    assert lib.kda_stream_probe(-1, A16, B16, 1 << 20, 1024, None) == 2
+    assert lib.kda_stream_probe(1, A16, B16, (1 << 20) + 8, 1024, None) == 2  # not 16-byte units
+    assert lib.kda_stream_probe(1, A16, B16, 1 << 20, 0, None) == 2          # grid
+    assert lib.kda_stream_probe(1, None, B16, 1 << 20, 1024, None) == 1      # copy needs src
+    assert lib.kda_stream_probe(0, A16, None, 1 << 20, 1024, None) == 1      # read needs a sink
+    assert lib.kda_stream_probe(1, A16 + 8, B16, 1 << 20, 1024, None) == 4
+    assert lib.kda_stream_probe(2, None, B16 + 4, 1 << 20, 1024, None) == 4
+    assert lib.kda_stream_probe(2, None, B16, 0, 1024, None) == 0
 
 
 def _desc(**kw):
