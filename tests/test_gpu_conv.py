@@ -106,19 +106,23 @@ def _tap_major(window, H, dk, dv):
     return np.concatenate([q, k, v], axis=2).copy()
 
 
-def test_prefill_conv_tap_major_window_matches_dense():
+@pytest.mark.parametrize("fuse", [0, -1])
+def test_prefill_conv_tap_major_window_matches_dense(fuse):
+    """fuse = 0 fuses the short sequences here and runs the conv as a pass;
+    -1 folds it into the intra-chunk kernel, which then reads the windows
+    through the same strides."""
     H, d, S = 4, 128, 6
     c = W.random_case(211, [70, 3, 200], H=H, d_k=d, d_v=d, io_dtype="bf16", num_slots=S,
                       slots=[4, 1, 0])
     weight, window = W.draw_conv(212, S, H, d, d, "bf16")
     dt = torch.bfloat16
-    announce("prefill conv tap-major %s" % c.name)
+    announce("prefill conv tap-major %s fuse=%d" % (c.name, fuse))
     win_dense = dev(window, dt)
-    o1, p1 = run_prefill_conv(c, weight, win_dense, dt, "silu")
+    o1, p1 = run_prefill_conv(c, weight, win_dense, dt, "silu", fuse_chunks=fuse)
     C = 3 * d
     tm = dev(_tap_major(window, H, d, d), dt)
     strides = (3 * H * C, d, H * C, H * d)
-    o2, p2 = run_prefill_conv(c, weight, tm, dt, "silu", strides=strides)
+    o2, p2 = run_prefill_conv(c, weight, tm, dt, "silu", strides=strides, fuse_chunks=fuse)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(p1, p2)
     np.testing.assert_array_equal(tm.float().cpu().numpy(),
@@ -195,10 +199,12 @@ def test_decode_conv_full_size_with_padding():
     np.testing.assert_array_equal(win_d.float().cpu().numpy(), win_r.astype(np.float32))
 
 
-def test_conv_window_inside_hybrid_page_lines():
+@pytest.mark.parametrize("fuse", [0, -1])
+def test_conv_window_inside_hybrid_page_lines(fuse):
     """kern's hybrid-page line: per head a 64 KiB fp32 state followed by its
     3-row bf16 window (2,304 bytes), 12 heads on 884,736-byte pages.  Prefill
-    and a decode step read and write both through one buffer."""
+    and a decode step read and write both through one buffer (fuse = -1: the
+    prefill's conv folded into the intra-chunk kernel)."""
     H, d, S = 12, 128, 4
     C = 3 * d
     hs = (d * d * 4 + 3 * C * 2) // 4          # 16,960 fp32 words per head
@@ -222,12 +228,12 @@ def test_conv_window_inside_hybrid_page_lines():
     strides = (2 * ss, 2 * hs, C, d)
     dt = torch.bfloat16
     o = torch.zeros((c.T, H, d), dtype=dt, device="cuda")
-    announce("prefill+decode conv in hybrid page lines")
+    announce("prefill+decode conv in hybrid page lines fuse=%d" % fuse)
     lap.chunk_prefill(dev(c.q, dt), dev(c.k, dt), dev(c.v, dt), dev(c.g), dev(c.beta),
                       dev(c.cu_seqlens), state_in=buf, state_out=buf, o=o, slots=dev(c.slots),
                       num_slots=S, state_slot_stride=ss, state_head_stride=hs,
                       conv_weight=dev(weight), conv_window=win_view, conv_activation="silu",
-                      conv_strides=strides)
+                      conv_strides=strides, fuse_chunks=fuse)
     dc = W.random_case(243, [1, 1], H=H, d_k=d, d_v=d, io_dtype="bf16", num_slots=S,
                        slots=[3, 1])
     od = torch.zeros((2, H, d), dtype=dt, device="cuda")
