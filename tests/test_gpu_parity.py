@@ -220,6 +220,17 @@ def test_packed_varlen_prefill_full():
             np.testing.assert_array_equal(pool_g[s], c.state_pool[s])
 
 
+@pytest.mark.parametrize("H,fuse", [(12, 0), (12, 2)])
+def test_packed_prefill_twelve_heads(H, fuse):
+    """The packed chunk's sequences at 12 heads, the per-GPU head count of the
+    pages' tensor-parallel decode groups (kern-k3-pp-prefill, "D: TP8 / EP8 /
+    DCP8"): fewer items than the 32-head call, another slice grouping in the
+    scan; fuse = 2 also runs the fused prefill on the sequences of at most
+    two chunks beside the two kernels."""
+    c = W.packed_varlen_prefill(H=H)
+    _check_case(c, fuse_chunks=fuse)
+
+
 @pytest.mark.timeout(900)
 def test_long_context_continuation():
     """262144 tokens, run twice: as 32 consecutive 8192-row calls with the
