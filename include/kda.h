@@ -428,16 +428,21 @@ kda_status_t kda_prefill_check(const float *g, const int32_t *cu_seqlens, const 
  *
  * In such a build, lane 0 of each of the 8 waves of workgroup 0 of the
  * intra-chunk kernel (kernel = KDA_CLOCK_INTRA) or of the fused prefill
- * (KDA_CLOCK_FUSED) writes the core clock counter (s_memtime) at each mark
- * of its first KDA_CLOCK_ITEMS items (chunks, for the fused kernel) into a
- * device array laid out [wave][item][mark], KDA_CLOCK_MARKS marks an item;
- * a mark not reached stays as it was (0 after a clear).  Marks: 0 the top
- * of the item; 1 and 2 before and after the barrier that ends the factor
- * phase; 3, 4 around the one after the A blocks; 5, 6 after the first
- * inverse level; 7, 8 after the second; 9, 10 after w and u (the fp32 and
- * fused builds' barrier there); fused only: 11, 12 around the barrier after
- * the state step, 13 after the chain bookkeeping.  Later launches overwrite
- * the array.
+ * (KDA_CLOCK_FUSED), or of the 4 waves of workgroup 0 of the state scan
+ * (KDA_CLOCK_SCAN; the longest sequence's first slice group), writes the
+ * core clock counter (s_memtime) at each mark of its first KDA_CLOCK_ITEMS
+ * items (chunks; scan: steps) into a device array laid out
+ * [wave][item][mark], KDA_CLOCK_MARKS marks an item; a mark not reached
+ * stays as it was (0 after a clear).  Intra-chunk and fused marks: 0 the
+ * top of the item; 1 and 2 before and after the barrier that ends the
+ * factor phase; 3, 4 around the one after the A blocks; 5, 6 after the
+ * first inverse level; 7, 8 after the second; 9, 10 after w and u (the fp32
+ * and fused builds' barrier there); fused only: 11, 12 around the barrier
+ * after the state step, 13 after the chain bookkeeping.  Scan marks: 0 the
+ * top of the step; 1 after the barrier that publishes the state tiles; 2
+ * after U = u - w S and the Q~ S part of o; 3 after the barrier that
+ * publishes U; 4 after the state update and the o store.  Later launches
+ * overwrite the array.
  *
  * kda_phase_clocks copies the first `count` words (at most 8 * 64 * 16) of
  * that kernel's array to host_out (when not NULL), then zeroes the whole
@@ -446,8 +451,8 @@ kda_status_t kda_prefill_check(const float *g, const int32_t *cu_seqlens, const 
  * kernel, KDA_ERR_UNSUPPORTED without the records, KDA_ERR_HIP if the copy
  * fails.
  */
-enum { KDA_CLOCK_INTRA = 0, KDA_CLOCK_FUSED = 1, KDA_CLOCK_WAVES = 8, KDA_CLOCK_ITEMS = 64,
-       KDA_CLOCK_MARKS = 16 };
+enum { KDA_CLOCK_INTRA = 0, KDA_CLOCK_FUSED = 1, KDA_CLOCK_SCAN = 2, KDA_CLOCK_WAVES = 8,
+       KDA_CLOCK_ITEMS = 64, KDA_CLOCK_MARKS = 16 };
 kda_status_t kda_phase_clocks(int32_t kernel, uint64_t *host_out, size_t count, int32_t clear);
 
 /*

@@ -452,7 +452,8 @@ static_assert(KDA_CLOCK_WAVES == kda::kClockWaves && KDA_CLOCK_ITEMS == kda::kCl
               "phase clock layout");
 
 kda_status_t kda_phase_clocks(int32_t kernel, uint64_t *host_out, size_t count, int32_t clear) {
-    if (kernel != KDA_CLOCK_INTRA && kernel != KDA_CLOCK_FUSED) return KDA_ERR_SHAPE;
+    if (kernel != KDA_CLOCK_INTRA && kernel != KDA_CLOCK_FUSED && kernel != KDA_CLOCK_SCAN)
+        return KDA_ERR_SHAPE;
     static_assert(sizeof(uint64_t) == sizeof(unsigned long long), "clock words");
     const hipError_t e = kda::phase_clocks_copy(kernel, reinterpret_cast<unsigned long long *>(host_out),
                                                 host_out ? count : 0, clear != 0);

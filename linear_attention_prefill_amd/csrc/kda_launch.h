@@ -115,11 +115,11 @@ hipError_t launch_prefill_check(const float *g, const int32_t *cu, const int32_t
                                 int N, int H, int dk, int num_slots, int32_t *flags,
                                 hipStream_t stream);
 
-// Phase clocks of the intra-chunk and fused kernels (kda_phase_clocks):
+// Phase clocks of the intra-chunk, fused and scan kernels (kda_phase_clocks):
 // workgroup 0's waves record the core clock counter at each phase boundary
-// of their first kClockItems items, in a library built with
+// of their first kClockItems items (scan: steps), in a library built with
 // KDA_PHASE_CLOCKS; other builds return hipErrorNotSupported.
-constexpr int kClockWaves = 8, kClockItems = 64, kClockMarks = 16;
+constexpr int kClockKernels = 3, kClockWaves = 8, kClockItems = 64, kClockMarks = 16;
 hipError_t phase_clocks_copy(int kernel, unsigned long long *host, size_t count, bool clear);
 
 // Streaming bandwidth probe (kda_stream_probe): mode 0 reads src (dst: a

@@ -70,8 +70,8 @@ constexpr float kDiagSpanLimit = 64.f;
 constexpr int kIntraThreads = 512;     // 8 waves: two per SIMD
 static_assert(kIntraThreads / 64 == kClockWaves, "one clock row per wave");
 #ifdef KDA_PHASE_CLOCKS
-// [kernel: 0 intra-chunk, 1 fused][wave][item][mark] core clock counts
-__device__ unsigned long long g_phase_clock[2 * kClockWaves * kClockItems * kClockMarks];
+// [kernel: 0 intra-chunk, 1 fused, 2 scan][wave][item][mark] core clock counts
+__device__ unsigned long long g_phase_clock[kClockKernels * kClockWaves * kClockItems * kClockMarks];
 #endif
 constexpr int kCuCache = 256;          // sequence bounds kept in LDS when N < this
 constexpr int kScanWarmAhead = 2;      // chunks between a scan stage's record and the one it warms
@@ -1447,8 +1447,21 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
     // loop: a conditional load would leave a stage register holding either
     // the old or the new value, and the copy that merges them waits for
     // every load in flight.
+    // Phase clocks (a KDA_PHASE_CLOCKS build only): lane 0 of each wave of
+    // workgroup 0 (the longest chain's first slice group) records the core
+    // clock counter at mark i of step cc.
+    auto clock_mark = [&](int cc, int i) {
+#ifdef KDA_PHASE_CLOCKS
+        if (blockIdx.x == 0 && lane == 0 && cc < kClockItems)
+            g_phase_clock[((2 * kClockWaves + wave) * kClockItems + cc) * kClockMarks + i] =
+                __builtin_amdgcn_s_memtime();
+#else
+        (void)cc; (void)i;
+#endif
+    };
     auto step = [&](Stage &X, int cc, bool refill, bool warm) {
         const int nx = cc + STAGES < nch ? cc + STAGES : nch - 1;
+        clock_mark(cc, 0);
         // publish my state tiles (rounded to E) and read every slab
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns)
@@ -1458,6 +1471,7 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
                 store4<E>(sSb + ns * (KS * 512) + ((t >> 1) * 64 + lane) * 8 + (t & 1) * 4, S[ns][i]);
             }
         __syncthreads();
+        clock_mark(cc, 1);
         if (warm) asm volatile("" ::"v"(X.pf));   // the warm-up word, loaded three steps ago
         // per slice: my tile of U = u - w S (two independent accumulation
         // chains), and the Q~ S part of the output, which does not need U
@@ -1491,6 +1505,7 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
                 }
             }
         }
+        clock_mark(cc, 2);
         if (refill) load_w(X, nx, warm);
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns)
@@ -1510,6 +1525,7 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
                     for (int r = 0; r < 4; ++r) S[ns][i][r] *= dfac[i][r];
         }
         __syncthreads();
+        clock_mark(cc, 3);
         const int row = wave * kSub + li;
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
@@ -1536,6 +1552,7 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
             if (row < sp.len - (j_lo + cc) * kChunk)
                 store4<E>(o + ((size_t)(sp.start + (j_lo + cc) * kChunk + row) * H + h) * DV + j0 + ns * kSub + 4 * lg,
                           (o0[ns] + o1[ns]) * scale);
+        clock_mark(cc, 4);
     };
 
     if (nch > 0) {
@@ -1792,7 +1809,7 @@ KDA_INST(float, 128, 128)
 hipError_t phase_clocks_copy(int kernel, unsigned long long *host, size_t count, bool clear) {
 #ifdef KDA_PHASE_CLOCKS
     constexpr size_t per = (size_t)kClockWaves * kClockItems * kClockMarks;
-    if (kernel < 0 || kernel > 1) return hipErrorInvalidValue;
+    if (kernel < 0 || kernel >= kClockKernels) return hipErrorInvalidValue;
     const size_t off = (size_t)kernel * per * sizeof(unsigned long long);
     if (host && count) {
         const hipError_t e = hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_clock),

@@ -508,14 +508,15 @@ def decode_tokens(q, k, v, g, beta, state_pool, slots, o=None, num_accepted=None
 
 
 # kda.h: KDA_CLOCK_* (the layout of kda_phase_clocks)
-KDA_CLOCK_INTRA, KDA_CLOCK_FUSED = 0, 1
+KDA_CLOCK_INTRA, KDA_CLOCK_FUSED, KDA_CLOCK_SCAN = 0, 1, 2
 CLOCK_WAVES, CLOCK_ITEMS, CLOCK_MARKS = 8, 64, 16
 
 
 def phase_clocks(kernel: int, clear: bool = False):
-    """Phase clocks of workgroup 0 of the intra-chunk kernel (KDA_CLOCK_INTRA)
-    or the fused prefill (KDA_CLOCK_FUSED) (``kda_phase_clocks``): an int64
-    array [wave][item][mark] of core clock counts, 0 where not reached.
+    """Phase clocks of workgroup 0 of the intra-chunk kernel (KDA_CLOCK_INTRA),
+    the fused prefill (KDA_CLOCK_FUSED) or the state scan (KDA_CLOCK_SCAN)
+    (``kda_phase_clocks``): an int64 array [wave][item][mark] of core clock
+    counts, 0 where not reached.
     Needs the library built with phase clocks (``load_library(CLOCKS_LIB_PATH)``
     first); raises KdaError (KDA_ERR_UNSUPPORTED) otherwise."""
     import numpy as np

@@ -6,9 +6,11 @@
 Runs one prefill call of a synthetic workload (the generators of
 ``workloads``) with ``libkda_clocks.so``, whose intra-chunk and fused
 kernels record the core clock counter at every phase boundary of workgroup
-0 (``kda_phase_clocks`` in ``include/kda.h``), and prints for each wave the
-clocks an item spends in each phase and in the barrier that ends it,
-averaged over the items the workgroup ran.  Waves w and w + 4 share a SIMD.
+0 (``kda_phase_clocks`` in ``include/kda.h``), and whose state scan does
+the same for the steps of its workgroup 0 (the longest sequence's first
+slice group), and prints for each wave the clocks an item spends in each
+phase and in the barrier that ends it, averaged over the items the
+workgroup ran.  Waves w and w + 4 of the 8-wave kernels share a SIMD.
 The records cost a few instructions a phase; times are for attribution, the
 uninstrumented library's times are ``bench.py``'s.
 """
@@ -28,6 +30,10 @@ INTERVALS = [("factors", 0, 1), ("bar", 1, 2), ("A blocks", 2, 3), ("bar", 3, 4)
              ("level 1", 4, 5), ("bar", 5, 6), ("level 2", 6, 7), ("bar", 7, 8),
              ("w, u", 8, 9), ("bar", 9, 10), ("state", 10, 11), ("bar", 11, 12),
              ("chain", 12, 13)]
+# a scan step: publish the state tiles (and the barrier), U = u - w S with
+# the Q~ S part of o, publish U (decay, refills, barrier), the state update
+# and the o store
+SCAN_INTERVALS = [("S out+bar", 0, 1), ("U, Q~S", 1, 2), ("U out+bar", 2, 3), ("S, o", 3, 4)]
 
 
 def workload(name: str):
@@ -59,14 +65,15 @@ def run_call(c, conv: bool, reps: int):
     torch.cuda.synchronize()
 
 
-def table(clk: np.ndarray, fused: bool) -> list:
+def table(clk: np.ndarray, fused: bool, intervals=None) -> list:
     """Per-wave mean clocks of each interval over the items whose marks are
     all recorded and in order, and whose next item's top mark came later in
     the same launch.  The last item has no next top mark; a call of several
     windows launches the intra-chunk kernel once per window, and each launch
     rewrites the items it reaches, so an item left from an earlier launch
     (its top mark earlier than the item before it) ends the run."""
-    names = [n for n, a, b in INTERVALS if fused or b <= 10]
+    iv = intervals if intervals is not None else [x for x in INTERVALS if fused or x[2] <= 10]
+    names = [n for n, a, b in iv]
     lines = ["%-5s %5s %8s " % ("wave", "items", "item") + " ".join("%9s" % n for n in names)]
     for w in range(clk.shape[0]):
         rows = []
@@ -74,12 +81,12 @@ def table(clk: np.ndarray, fused: bool) -> list:
             c0, c1 = clk[w, i], clk[w, i + 1]
             if c0[0] == 0 or c1[0] == 0:
                 continue
-            marks = [m for _, a, b in INTERVALS if fused or b <= 10 for m in (a, b)]
+            marks = [m for _, a, b in iv for m in (a, b)]
             if any(c0[m] == 0 for m in marks) or c1[0] <= c0[0]:
                 continue
-            if any(c0[b] < c0[a] for n, a, b in INTERVALS if fused or b <= 10):
+            if any(c0[b] < c0[a] for n, a, b in iv):
                 continue
-            rows.append([c1[0] - c0[0]] + [c0[b] - c0[a] for n, a, b in INTERVALS if fused or b <= 10])
+            rows.append([c1[0] - c0[0]] + [c0[b] - c0[a] for n, a, b in iv])
         if not rows:
             continue
         r = np.mean(np.array(rows, dtype=np.float64), axis=0)
@@ -99,18 +106,20 @@ def main(argv=None) -> int:
     K.load_library()
     c = workload(args.workload)
     run_call(c, args.conv, 3)
-    for kern in (K.KDA_CLOCK_INTRA, K.KDA_CLOCK_FUSED):
+    for kern in (K.KDA_CLOCK_INTRA, K.KDA_CLOCK_FUSED, K.KDA_CLOCK_SCAN):
         K.phase_clocks(kern, clear=True)
     run_call(c, args.conv, 1)
     print("phase clocks (core clocks an item, workgroup 0): %s%s, H=%d, d_k=%d, d_v=%d, %s"
           % (c.name, " + conv (SiLU)" if args.conv else "", c.H, c.d_k, c.d_v, c.io_dtype))
-    for kern, label in ((K.KDA_CLOCK_INTRA, "intra-chunk kernel"), (K.KDA_CLOCK_FUSED, "fused prefill")):
+    for kern, label in ((K.KDA_CLOCK_INTRA, "intra-chunk kernel"), (K.KDA_CLOCK_FUSED, "fused prefill"),
+                        (K.KDA_CLOCK_SCAN, "state scan (steps of the longest chain)")):
         clk = K.phase_clocks(kern)
         if not clk.any():
             print("%s: no items" % label)
             continue
         print("%s:" % label)
-        print("\n".join(table(clk, kern == K.KDA_CLOCK_FUSED)))
+        print("\n".join(table(clk, kern == K.KDA_CLOCK_FUSED,
+                               SCAN_INTERVALS if kern == K.KDA_CLOCK_SCAN else None)))
     return 0
 
 

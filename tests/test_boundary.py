@@ -73,7 +73,8 @@ def test_phase_clocks_need_the_instrumented_build(lib):
     buf = np.full(16, 7, dtype=np.uint64)
     assert lib.kda_phase_clocks(K.KDA_CLOCK_INTRA, buf.ctypes.data, buf.size, 1) == 6
     assert lib.kda_phase_clocks(K.KDA_CLOCK_FUSED, None, 0, 0) == 6
-    assert lib.kda_phase_clocks(2, buf.ctypes.data, buf.size, 0) == 2
+    assert lib.kda_phase_clocks(K.KDA_CLOCK_SCAN, None, 0, 1) == 6
+    assert lib.kda_phase_clocks(3, buf.ctypes.data, buf.size, 0) == 2
     assert np.all(buf == 7)
 
 
@@ -95,7 +96,7 @@ def test_phase_clock_build_records_the_phases():
                                   stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
             outs[tag] = open(asm).read()
     assert "s_memtime" not in outs["plain"]
-    assert outs["clocks"].count("s_memtime") >= 2 * 13
+    assert outs["clocks"].count("s_memtime") >= 2 * 13 + 5
 
 
 def test_stream_probe_rejects_bad_arguments(lib):

@@ -46,3 +46,10 @@ def test_phase_clock_tables(workload, label):
         assert items >= 4
         assert all(p >= 0 for p in phases)
         assert 0 < sum(phases) <= item * 1.05, (w, item, phases)
+    if workload == "packed":
+        # the scan's workgroup 0 runs the longest sequence (37 chunks) of head 0
+        rows = _rows(r.stdout, "state scan (steps of the longest chain)")
+        assert [w for w, *_ in rows] == list(range(4))
+        for w, items, step, phases in rows:
+            assert items >= 30
+            assert 0 < sum(phases) <= step * 1.05, (w, step, phases)
