@@ -1369,19 +1369,23 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
             for (int i = 0; i < TPW; ++i) S[ns][i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
-    // Settle the state load here: otherwise the wait inserted for it at the
-    // top of the chunk loop would also drain every prefetched chunk.
+    // The state load is settled once the first stages' loads are issued
+    // behind it (so both latencies overlap) and before the chunk loop:
+    // otherwise the wait inserted for it at the top of the loop would also
+    // drain every prefetched chunk.
+    auto settle_state = [&]() {
 #pragma unroll
-    for (int ns = 0; ns < NS; ++ns)
+        for (int ns = 0; ns < NS; ++ns)
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
+            for (int i = 0; i < TPW; ++i) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float x = S[ns][i][r];
-                asm volatile("" : "+v"(x));
-                S[ns][i][r] = x;
+                for (int r = 0; r < 4; ++r) {
+                    float x = S[ns][i][r];
+                    asm volatile("" : "+v"(x));
+                    S[ns][i][r] = x;
+                }
             }
-        }
+    };
 
     // Record of chunk cc, by part; each part of a stage is refilled with the
     // chunk STAGES ahead as soon as its last use in the current step has been
@@ -1560,6 +1564,7 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
             Stage X[STAGES];
 #pragma unroll
             for (int i = 0; i < STAGES; ++i) load_stage(X[i], i < nch ? i : nch - 1, false);
+            settle_state();
             int cc = 0;
             for (; cc + STAGES - 1 < nch; cc += STAGES) {
 #pragma unroll
@@ -1573,6 +1578,7 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
             load_stage(A, 0, kWarm);
             load_stage(Bs, nch > 1 ? 1 : 0, false);
             load_stage(Cs, nch > 2 ? 2 : nch - 1, false);
+            settle_state();
             int cc = 0;
             for (; cc + 2 < nch; cc += 3) {
                 step(A, cc, true, kWarm);
