@@ -169,8 +169,8 @@ int32_t kda_prefill_windows(const kda_prefill_desc_t *desc);
  * for many short sequences and not for long ones.  Returns F for `desc`
  * (-1: no sequence is fused, or desc is invalid): desc->fuse_chunks when it
  * is positive, none when it is negative, else the library's choice from the
- * sizes alone: 8 when total_rows <= 64 num_seqs, 4 when total_rows <=
- * 128 num_seqs, none otherwise.  Results agree with the unfused path to the
+ * sizes alone: 8 when total_rows <= 64 num_seqs, 6 when total_rows <=
+ * 128 num_seqs, 8 when total_rows <= 256 num_seqs, none otherwise.  Results agree with the unfused path to the
  * usual bf16 rounding (the same operands, summed in another order).
  */
 int32_t kda_prefill_fuse_chunks(const kda_prefill_desc_t *desc);

@@ -139,7 +139,9 @@ def test_fuse_chunks_policy(lib):
     # the library's choice: by the average sequence length
     assert f(0) == -1                                  # 16 sequences in 8192 rows
     assert f(0, N=1) == -1
-    assert f(0, N=64) == 4 and f(0, N=100) == 4        # at most two chunks on average
+    assert f(0, N=31) == -1                            # more than four chunks on average
+    assert f(0, N=32) == 8 and f(0, N=40) == 8         # at most four
+    assert f(0, N=64) == 6 and f(0, N=100) == 6        # at most two
     assert f(0, N=128) == 8 and f(0, N=300) == 8       # at most one
     # windows: none when every sequence is fused (F * 64 >= T)
     d = K.make_desc(8192, 16, 32, 128, 128, 64, K.KDA_BF16, fuse_chunks=128)
