@@ -474,6 +474,6 @@ kda_status_t kda_stream_probe(int32_t mode, const void *src, void *dst, size_t b
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-int32_t kda_version(void) { return 107; }
+int32_t kda_version(void) { return 108; }
 
 }  // extern "C"

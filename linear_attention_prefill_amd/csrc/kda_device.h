@@ -188,8 +188,12 @@ __device__ __forceinline__ f32x4 raw_to_f32(const bf16x4 &x) {
 // Varlen bookkeeping shared by the prefill kernels.  Sequence n starts at
 // row clamp(cu[n], 0, T) and ends at clamp(cu[n+1], start, T).  Its chunks
 // take the ids floor(start / 64) + n + j, j = 0 .. ceil(len / 64) - 1; these
-// ranges are disjoint across sequences and all ids are below T / 64 + N, so
-// every chunk has a workspace record without any prefix sum over sequences.
+// ranges are disjoint across sequences, so every chunk has a workspace record
+// without any prefix sum over sequences.  The last id of sequence n is at most
+// floor((start + len - 1) / 64) + n <= floor((T - 1) / 64) + N - 1, whatever
+// the offsets, so chunk_id_count ids cover every chunk (at T = 8192, N = 1
+// that is 128 ids, a whole number of 64-chunk windows).
+__host__ __device__ constexpr int chunk_id_count(int T, int N) { return T > 0 ? (T - 1) / kChunk + N : N; }
 struct SeqSpan {
     int start, len, first_chunk;
 };

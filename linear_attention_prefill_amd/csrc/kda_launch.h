@@ -38,7 +38,7 @@ struct PrefillArgs {
 // than one window, the states carried between windows ([N][H][d_v][d_k]
 // fp32).
 struct PrefillPlan {
-    int chunk_ids;          // T / 64 + N
+    int chunk_ids;          // chunk_id_count(T, N): (T - 1) / 64 + N
     int windows;
     int window_chunks;
     size_t dec_offset, carry_offset, bytes;

@@ -276,7 +276,7 @@ __device__ __forceinline__ void intra_chunks(
     __shared__ int sWs[2][NTH / 64];
     int nlong = -1;                                    // -1: the id walk
     if constexpr (SKIP) {
-        if (c_lo == 0 && c_hi == T / kChunk + N) {
+        if (c_lo == 0 && c_hi == chunk_id_count(T, N)) {
             int count = 0, chunks = 0;                 // running totals, uniform
             for (int base = 0; base < N; base += NTH) {
                 const int n = base + tid;
@@ -1743,7 +1743,7 @@ PrefillPlan prefill_plan(int T, int N, int H, int dk, int dv, bool bf16, int win
     PrefillPlan p;
     const size_t es = bf16 ? 2 : 4;
     const size_t rec = ((size_t)kChunk * (3 * dk + dv) + 6 * 512) * es;
-    p.chunk_ids = T / kChunk + N;
+    p.chunk_ids = chunk_id_count(T, N);
     // Default: two windows for calls with few (sequence, head) pairs and
     // enough chunks, one otherwise.  Such calls scan long chains with one
     // slice per workgroup, which take records in at a per-CU rate that is
@@ -1752,7 +1752,11 @@ PrefillPlan prefill_plan(int T, int N, int H, int dk, int dv, bool bf16, int win
     // them (one 8192-row sequence at H = 32: scan 129 -> 109 us, intra
     // 131 -> 145 us, step 256 -> 244 us).  Calls with many pairs run many
     // short chains whose workgroups would each start twice (16 packed
-    // sequences: step 258 -> 277 us with two windows).
+    // sequences: step 258 -> 277 us with two windows).  An 8192-row sequence
+    // has 128 chunk ids, so each of its windows holds 64 chunks x 32 heads =
+    // 8 whole rounds of a 256-workgroup grid; an id count of T / 64 + N gave
+    // the first window 65 chunks and a ninth round for 32 of its workgroups
+    // (step 242 -> 232 us, intra 143 -> 137 us).
     size_t wc = (size_t)p.chunk_ids;
     if (window_chunks > 0) wc = (size_t)window_chunks;
     else if ((long long)N * H <= 64 && p.chunk_ids >= 32) wc = ((size_t)p.chunk_ids + 1) / 2;
@@ -1768,11 +1772,8 @@ PrefillPlan prefill_plan(int T, int N, int H, int dk, int dv, bool bf16, int win
     return p;
 }
 
-// Default: the fused prefill for calls whose sequences average at most two
-// chunks, taking sequences of up to 8 chunks when they average one chunk or
-// less and up to 4 otherwise.  The fused kernel runs a chain's chunks one
-// after another at about 10 us a chunk, which beats the intra-chunk kernel
-// plus scan only for short chains: 16 packed sequences (average 8 chunks,
+// The fused kernel runs a chain's chunks one after another at about 10 us a
+// chunk, which beats the intra-chunk kernel plus scan only for short chains: 16 packed sequences (average 8 chunks,
 // longest 37) 250 us a step with none fused, 258 us fusing those of up to
 // 2 chunks; 128 sequences averaging one chunk 457 -> 360 us (8 chunks);
 // 64 sequences of 2 chunks 343 -> 264 us (4); 256 sequences of 32 rows

@@ -59,7 +59,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 107
+    assert lib.kda_version() == 108
     for code in range(9):
         s = lib.kda_status_string(code).decode()
         assert s and s != "unknown status"
@@ -152,7 +152,8 @@ def test_fuse_chunks_policy(lib):
 
 def _ws_formula(T, N, H, dk, dv, es):
     rec = (64 * (3 * dk + dv) + 6 * 512) * es + dk * 4
-    return (T // 64 + N) * H * rec
+    ids = (T - 1) // 64 + N if T > 0 else N     # the last chunk's id is below this
+    return ids * H * rec
 
 
 def test_workspace_size(lib):

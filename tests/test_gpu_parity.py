@@ -570,7 +570,7 @@ def test_windows_match_one_window(window_chunks, io):
     c = W.random_case(711 + window_chunks, WINDOW_LENGTHS, H=2, d_k=128, d_v=128, io_dtype=io)
     dt = torch_dtype(io)
     nw = lap.prefill_windows(c.T, c.N, c.H, c.d_k, c.d_v, dt, window_chunks=window_chunks)
-    assert nw == -(-(c.T // 64 + c.N) // window_chunks)
+    assert nw == -(-((c.T - 1) // 64 + c.N) // window_chunks)
     outs = []
     for wc in (0, window_chunks):
         pool = dev(c.state_pool)
