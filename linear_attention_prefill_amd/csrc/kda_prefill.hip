@@ -1463,7 +1463,41 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
         (void)cc; (void)i;
 #endif
     };
-    auto step = [&](Stage &X, int cc, bool refill, bool warm) {
+    // A step's tail: the A_qk U part of its output, the output store and
+    // the refill of its stage's last part.  With several slices the tail of
+    // step cc runs in step cc + 1, after that step's first barrier, where it
+    // no longer delays the next publication of S: nothing on the state's
+    // dependent chain (S -> U -> S) waits for it (16 packed sequences: scan
+    // 102.2 -> 100.2 us).  o0, o1 and ub carry a step's values to its tail.
+    constexpr bool kDeferTail = NS > 1;
+    static_assert(!(kDeferTail && kWarm), "the warm-up rotation runs one slice");
+    f32x4 o0[NS], o1[NS];
+    Frag<E> ub[NS][2];
+    // my tile of O = Q~ S + A_qk U, transposed: lane holds row 16 wave + i,
+    // columns j0 + 16 ns + 4g + r
+    auto tail_mma = [&](Stage &X) {
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns) {
+            mma(o0[ns], ub[ns][0], X.af[0]);
+            if (wave >= 2) {
+                if constexpr (KDA_SINGLE_CHAIN && NS > 1) mma(o0[ns], ub[ns][1], X.af[1]);
+                else mma(o1[ns], ub[ns][1], X.af[1]);
+            }
+        }
+    };
+    auto tail_out = [&](Stage &X, int cc, bool refill) {
+        const int nx = cc + STAGES < nch ? cc + STAGES : nch - 1;
+        if (refill) load_k(X, nx);
+        const int row = wave * kSub + li;
+#pragma unroll
+        for (int ns = 0; ns < NS; ++ns)
+            if (row < sp.len - (j_lo + cc) * kChunk)
+                store4<E>(o + ((size_t)(sp.start + (j_lo + cc) * kChunk + row) * H + h) * DV + j0 + ns * kSub + 4 * lg,
+                          (o0[ns] + o1[ns]) * scale);
+    };
+    // Step cc on stage X; Xp is the previous step's stage, whose tail is
+    // pending when tail_p (deferred tails only), refilled when refill_p.
+    auto step = [&](Stage &X, int cc, bool refill, bool warm, Stage &Xp, bool tail_p, bool refill_p) {
         const int nx = cc + STAGES < nch ? cc + STAGES : nch - 1;
         clock_mark(cc, 0);
         // publish my state tiles (rounded to E) and read every slab
@@ -1477,9 +1511,24 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
         __syncthreads();
         clock_mark(cc, 1);
         if (warm) asm volatile("" ::"v"(X.pf));   // the warm-up word, loaded three steps ago
+        // this step's decay factors, one per key row of my tiles
+        float dfac[TPW][4];
+        auto shuffle_decay = [&]() {
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dfac[i][r] = __shfl(X.d, i * kSub + 4 * lg + r);
+        };
+        if constexpr (kDeferTail) {
+            shuffle_decay();
+            if (tail_p) {
+                tail_mma(Xp);
+                tail_out(Xp, cc - 1, refill_p);
+            }
+        }
         // per slice: my tile of U = u - w S (two independent accumulation
         // chains), and the Q~ S part of the output, which does not need U
-        f32x4 un[NS], o0[NS], o1[NS];
+        f32x4 un[NS];
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
             Frag<E> Sb[KS];
@@ -1509,58 +1558,57 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
                 }
             }
         }
+        // the decay of my state tiles (their undecayed copy is in LDS)
+        auto apply_decay = [&](bool pin) {
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns)
+#pragma unroll
+                for (int i = 0; i < TPW; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float x = S[ns][i][r] * dfac[i][r];
+                        if (pin) asm volatile("" : "+v"(x));
+                        S[ns][i][r] = x;
+                    }
+        };
+        // With several slices the multiplies stay here, among the products
+        // above: left to the compiler they and the shuffles they wait on
+        // sink to the top of the state update, on the dependent chain.
+        if constexpr (kDeferTail) apply_decay(true);
         clock_mark(cc, 2);
         if (refill) load_w(X, nx, warm);
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns)
             store4<E>(sUb + ns * 1024 + ((wave >> 1) * 64 + lane) * 8 + (wave & 1) * 4, un[ns]);
         if (refill) load_q(X, nx);
-        {
-            float dfac[TPW][4];
-#pragma unroll
-            for (int i = 0; i < TPW; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dfac[i][r] = __shfl(X.d, i * kSub + 4 * lg + r);
-#pragma unroll
-            for (int ns = 0; ns < NS; ++ns)
-#pragma unroll
-                for (int i = 0; i < TPW; ++i)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) S[ns][i][r] *= dfac[i][r];
+        if constexpr (!kDeferTail) {
+            shuffle_decay();
+            apply_decay(false);
         }
         __syncthreads();
         clock_mark(cc, 3);
-        const int row = wave * kSub + li;
+        // every slice's U at once: one LDS round trip before the products
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns) {
-            Frag<E> ub[2];
-            ub[0] = load_frag<E>(sUb + ns * 1024, lane);
-            ub[1] = load_frag<E>(sUb + ns * 1024 + 512, lane);
-            // my tile of O = Q~ S + A_qk U, transposed: lane holds row
-            // 16 wave + i, columns j0 + 16 ns + 4g + r
-            mma(o0[ns], ub[0], X.af[0]);
-            if (wave >= 2) {
-                if constexpr (KDA_SINGLE_CHAIN && NS > 1) mma(o0[ns], ub[1], X.af[1]);
-                else mma(o1[ns], ub[1], X.af[1]);
-            }
-            // my key tiles of S = diag(e^{Gam_C}) S + K~^T U
-#pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                mma(S[ns][i], X.kf[i][0], ub[0]);
-                mma(S[ns][i], X.kf[i][1], ub[1]);
-            }
+            ub[ns][0] = load_frag<E>(sUb + ns * 1024, lane);
+            ub[ns][1] = load_frag<E>(sUb + ns * 1024 + 512, lane);
         }
-        if (refill) load_k(X, nx);
+        if constexpr (!kDeferTail) tail_mma(X);
+        // my key tiles of S = diag(e^{Gam_C}) S + K~^T U
 #pragma unroll
         for (int ns = 0; ns < NS; ++ns)
-            if (row < sp.len - (j_lo + cc) * kChunk)
-                store4<E>(o + ((size_t)(sp.start + (j_lo + cc) * kChunk + row) * H + h) * DV + j0 + ns * kSub + 4 * lg,
-                          (o0[ns] + o1[ns]) * scale);
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                mma(S[ns][i], X.kf[i][0], ub[ns][0]);
+                mma(S[ns][i], X.kf[i][1], ub[ns][1]);
+            }
+        if constexpr (!kDeferTail) tail_out(X, cc, refill);
         clock_mark(cc, 4);
     };
 
     if (nch > 0) {
         if constexpr (!kWarm) {
+            // step k runs on stage k % STAGES
             Stage X[STAGES];
 #pragma unroll
             for (int i = 0; i < STAGES; ++i) load_stage(X[i], i < nch ? i : nch - 1, false);
@@ -1568,11 +1616,22 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
             int cc = 0;
             for (; cc + STAGES - 1 < nch; cc += STAGES) {
 #pragma unroll
-                for (int i = 0; i < STAGES; ++i) step(X[i], cc + i, true, false);
+                for (int i = 0; i < STAGES; ++i)
+                    step(X[i], cc + i, true, false, X[(i + STAGES - 1) % STAGES], cc + i > 0, true);
             }
 #pragma unroll
             for (int i = 0; i < STAGES - 1; ++i)
-                if (cc + i < nch) step(X[i], cc + i, false, false);
+                if (cc + i < nch)
+                    step(X[i], cc + i, false, false, X[(i + STAGES - 1) % STAGES], cc + i > 0, i == 0);
+            if constexpr (kDeferTail) {
+                // the last step's tail (its stage needs no refill)
+#pragma unroll
+                for (int i = 0; i < STAGES; ++i)
+                    if ((nch - 1) % STAGES == i) {
+                        tail_mma(X[i]);
+                        tail_out(X[i], nch - 1, false);
+                    }
+            }
         } else {
             Stage A, Bs, Cs;
             load_stage(A, 0, kWarm);
@@ -1581,12 +1640,12 @@ __global__ __launch_bounds__(256, 1) void kda_scan_kernel(
             settle_state();
             int cc = 0;
             for (; cc + 2 < nch; cc += 3) {
-                step(A, cc, true, kWarm);
-                step(Bs, cc + 1, true, false);
-                step(Cs, cc + 2, true, false);
+                step(A, cc, true, kWarm, Cs, false, false);
+                step(Bs, cc + 1, true, false, A, false, false);
+                step(Cs, cc + 2, true, false, Bs, false, false);
             }
-            if (cc < nch) step(A, cc, false, kWarm);
-            if (cc + 1 < nch) step(Bs, cc + 1, false, false);
+            if (cc < nch) step(A, cc, false, kWarm, Cs, false, false);
+            if (cc + 1 < nch) step(Bs, cc + 1, false, false, A, false, false);
         }
     }
 
