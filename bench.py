@@ -32,6 +32,8 @@ Prints ONE JSON line.  Besides the throughput it reports:
                 counter bytes' rate against the copy ceiling below;
   ceilings      what plain streaming (kda_stream_probe) reaches on this chip
                 in the same run: read, copy and in-place update of 512 MiB;
+                and the core clocks a bf16 16x16x32 product takes one wave
+                with 1, 2 or 8 independent accumulators (kda_mfma_probe);
   path          the whole step against the HBM roof and the bf16 MFMA roof;
   intra_mfma    the intra-chunk contractions' algorithmic flops over the
                 intra kernel's time, against the bf16 matrix-core peak;
@@ -361,6 +363,17 @@ def stream_ceilings(torch, lap, mib=512, grids=(256, 384, 512), reps=10):
     return res
 
 
+def mfma_rates(lap, iters=4096):
+    """Core clocks per bf16 16x16x32 product that one wave a SIMD issues with
+    1, 2 and 8 independent accumulators (``kda_mfma_probe``): the dependent
+    latency, and the matrix core's throughput, which the published dense
+    peak (2.5 PFLOP/s on 256 CUs at 2.4 GHz) puts at 16 clocks."""
+    r = {c: lap.kda.mfma_probe(c, iters) for c in (1, 2, 8)}
+    return {"kernel": "kda_mfma_probe", "clocks_per_product": {str(c): x["clocks_per_product"]
+                                                               for c, x in r.items()},
+            "core_MHz": r[8]["core_MHz"]}
+
+
 def host_cpus():
     """Threads the CPU baseline uses and what they run on: the CPUs this
     process may run on (sched_getaffinity), capped by a cgroup CPU quota when
@@ -652,6 +665,9 @@ def main():
     ceil = stream_ceilings(torch, lap)
     log("streaming ceilings: read %.0f GB/s, copy %.0f GB/s, in-place update %.0f GB/s"
         % (ceil["read_GBs"], ceil["copy_GBs"], ceil["update_GBs"]))
+    ceil["mfma_bf16_16x16x32"] = mfma_rates(lap)
+    log("bf16 16x16x32 products, one wave a SIMD: %s core clocks each (1, 2, 8 accumulators)"
+        % ", ".join("%.1f" % x for x in ceil["mfma_bf16_16x16x32"]["clocks_per_product"].values()))
     t0 = time.time()
     case = {"packed": W.packed_varlen_prefill, "single": W.single_seq_prefill,
             "short": short_seqs_prefill}[args.workload]()

@@ -376,8 +376,8 @@ kda_status_t kda_decode_tokens(const void *q, const void *k, const void *v,
  * for bit, the same results.  The workspace is a static device array of
  * KDA_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs this
  * call on until the process ends: enough for one packed 8192-row chunk of up
- * to 16 sequences at H = 32, d_k = d_v = 128 in bf16 (317.25 MiB of
- * records).  A call whose kda_prefill_workspace_size exceeds it returns
+ * to 18 sequences at H = 32, d_k = d_v = 128 in bf16 (315.05 MiB of records
+ * for 16 sequences, 319.45 MiB for 18).  A call whose kda_prefill_workspace_size exceeds it returns
  * KDA_ERR_TOO_LARGE before anything runs.  The first call on a device looks
  * up that device's copy of the array (hipGetSymbolAddress); no call
  * allocates.  Every call on one GPU shares its array: calls that overlap on
@@ -476,6 +476,24 @@ kda_status_t kda_phase_clocks(int32_t kernel, uint64_t *host_out, size_t count, 
 enum { KDA_STREAM_READ = 0, KDA_STREAM_COPY = 1, KDA_STREAM_UPDATE = 2 };
 kda_status_t kda_stream_probe(int32_t mode, const void *src, void *dst, size_t bytes, int32_t grid,
                               void *stream);
+
+/*
+ * Matrix-core issue probe.  Like the streaming probe, a reference measured
+ * on the same chip for the perf checks the "kern" page, section "Inside",
+ * lists: here for the kernels' bf16 products.  Enqueues on `stream` one
+ * workgroup of 4 waves (one per SIMD); each wave runs `iters` rounds of
+ * `chains` (1, 2, 4 or 8) bf16 16x16x32 products, one on each of `chains`
+ * independent accumulators, and wave w writes out[2w] = the core clocks
+ * (s_memtime) and out[2w + 1] = the 100 MHz reference ticks (s_memrealtime)
+ * its loop took.  `out` is caller-owned device memory of 12 uint64 (words 8
+ * to 11 are a sink that is written only in a case the probe's data never
+ * reach), 8-byte aligned.  Core clocks per product = out[0] / (iters
+ * chains): with one accumulator each product waits for the one before, with
+ * eight the matrix core's own rate shows.  Errors: KDA_ERR_SHAPE for other
+ * chains or iters outside 1 .. 2^20, KDA_ERR_NULL, KDA_ERR_ALIGN,
+ * KDA_ERR_HIP if the launch fails.
+ */
+kda_status_t kda_mfma_probe(int32_t chains, int32_t iters, uint64_t *out, void *stream);
 
 /*
  * Static description of a status code.  Every call validates its arguments

@@ -24,7 +24,8 @@ LIB = os.path.join(PKG, "libkda.so")
 CLOCKS_LIB = os.path.join(PKG, "libkda_clocks.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["kda_prefill.hip", "kda_decode.hip", "kda_conv.hip", "kda_check.hip", "kda_stream.hip"]
+HIP_SOURCES = ["kda_prefill.hip", "kda_decode.hip", "kda_conv.hip", "kda_check.hip", "kda_stream.hip",
+               "kda_mfma_probe.hip"]
 CXX_SOURCES = ["kda_api.cpp"]
 
 # Packed fp32 VALU ops are disabled for all device code.
@@ -35,7 +36,10 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # around every such use (2 to 5 accumulator moves per product).  Keeping the
 # products' C/D operands in vector registers removes those moves (16 packed
 # sequences: scan 108 -> 103 us).
-PER_SOURCE_FLAGS = {"kda_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# The issue probe uses the same form, so that its rates are the ones the
+# prefill kernels' products see.
+PER_SOURCE_FLAGS = {"kda_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                    "kda_mfma_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",
           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 

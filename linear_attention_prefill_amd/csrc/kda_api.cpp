@@ -474,6 +474,17 @@ kda_status_t kda_stream_probe(int32_t mode, const void *src, void *dst, size_t b
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-int32_t kda_version(void) { return 108; }
+kda_status_t kda_mfma_probe(int32_t chains, int32_t iters, uint64_t *out, void *stream) {
+    if ((chains != 1 && chains != 2 && chains != 4 && chains != 8) || iters < 1 || iters > (1 << 20))
+        return KDA_ERR_SHAPE;
+    if (!out) return KDA_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(out) % 8 != 0) return KDA_ERR_ALIGN;
+    (void)hipGetLastError();       // an earlier call's error is not this call's
+    const hipError_t e = kda::launch_mfma_probe(chains, iters, reinterpret_cast<unsigned long long *>(out),
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int32_t kda_version(void) { return 109; }
 
 }  // extern "C"

@@ -126,6 +126,9 @@ hipError_t phase_clocks_copy(int kernel, unsigned long long *host, size_t count,
 // sink of 4 grid bytes), 1 copies src to dst, 2 scales dst in place.
 hipError_t launch_stream_probe(int mode, const void *src, void *dst, size_t bytes, int grid,
                                hipStream_t stream);
+// One workgroup of 4 waves issuing bf16 16x16x32 products on `chains`
+// (1, 2, 4 or 8) independent accumulators, `iters` rounds; out: 12 words.
+hipError_t launch_mfma_probe(int chains, int iters, unsigned long long *out, hipStream_t stream);
 
 // Device address of the static scratch that backs kda_chunk_prefill_static
 // on the device `stream` runs on (looked up on the first call per device).

@@ -111,6 +111,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.kda_phase_clocks.argtypes = [i32, vp, sz, i32]
     lib.kda_stream_probe.restype = ctypes.c_int
     lib.kda_stream_probe.argtypes = [i32, vp, vp, sz, i32, vp]
+    lib.kda_mfma_probe.restype = ctypes.c_int
+    lib.kda_mfma_probe.argtypes = [i32, i32, vp, vp]
     if path is None:
         _lib = lib
     return lib
@@ -539,3 +541,14 @@ def stream_probe(mode: int, src, dst, grid: int = 1024, stream=None):
     _check(load_library().kda_stream_probe(int(mode), _ptr(src) if src is not None else None,
                                            _ptr(dst), nbytes, int(grid), _stream(stream)))
 
+
+def mfma_probe(chains: int, iters: int = 4096) -> dict:
+    """Core clocks per bf16 16x16x32 product that one wave per SIMD reaches
+    with `chains` independent accumulators (``kda_mfma_probe``), and the core
+    clock over the loop in MHz.  Runs on the current stream and waits."""
+    out = torch.zeros(12, dtype=torch.int64, device="cuda")
+    _check(load_library().kda_mfma_probe(int(chains), int(iters), _ptr(out), _stream(None)))
+    w = out.cpu().numpy()
+    clocks, ticks = int(w[0]), int(w[1])
+    return {"chains": int(chains), "clocks_per_product": clocks / (iters * chains),
+            "core_MHz": 100.0 * clocks / ticks if ticks else float("nan")}

@@ -49,7 +49,7 @@ def test_header_declares_expected_entry_points():
               "kda_decode_step_lines", "kda_decode_tokens", "kda_chunk_prefill_conv",
               "kda_decode_step_conv", "kda_prefill_check", "kda_chunk_prefill_static",
               "kda_prefill_windows", "kda_prefill_fuse_chunks", "kda_phase_clocks",
-              "kda_stream_probe"):
+              "kda_stream_probe", "kda_mfma_probe"):
         assert n in names
 
 
@@ -59,7 +59,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_version() == 108
+    assert lib.kda_version() == 109
     for code in range(9):
         s = lib.kda_status_string(code).decode()
         assert s and s != "unknown status"
@@ -114,6 +114,17 @@ def test_stream_probe_rejects_bad_arguments(lib):
     assert lib.kda_stream_probe(2, None, B16, 0, 1024, None) == 0
 
 
+def test_mfma_probe_rejects_bad_arguments(lib):
+    """Host checks of kda_mfma_probe, all before any launch."""
+    A8 = 0x1000
+    for chains in (0, 3, 5, 16, -1):
+        assert lib.kda_mfma_probe(chains, 64, A8, None) == 2
+    assert lib.kda_mfma_probe(8, 0, A8, None) == 2                            # iters
+    assert lib.kda_mfma_probe(8, (1 << 20) + 1, A8, None) == 2
+    assert lib.kda_mfma_probe(8, 64, None, None) == 1
+    assert lib.kda_mfma_probe(8, 64, A8 + 4, None) == 4
+
+
 def _desc(**kw):
     d = dict(T=8192, N=16, H=32, dk=128, dv=128, slots=64, io=K.KDA_BF16, scale=1.0, ss=0, hs=0,
              conv=0)
@@ -154,6 +165,15 @@ def _ws_formula(T, N, H, dk, dv, es):
     rec = (64 * (3 * dk + dv) + 6 * 512) * es + dk * 4
     ids = (T - 1) // 64 + N if T > 0 else N     # the last chunk's id is below this
     return ids * H * rec
+
+
+def test_static_scratch_holds_the_packed_chunk(lib):
+    """The allocation-free entry point's array holds an 8192-row chunk of up
+    to 18 sequences at H = 32, d = 128, bf16, and no more."""
+    size = lambda n: lib.kda_prefill_workspace_size(ctypes.byref(
+        K.make_desc(8192, n, 32, 128, 128, 64, K.KDA_BF16, 1.0)))
+    assert size(16) == 330350592                      # 315.05 MiB
+    assert size(18) <= K.STATIC_SCRATCH_BYTES < size(19)
 
 
 def test_workspace_size(lib):

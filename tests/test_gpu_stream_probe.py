@@ -1,5 +1,6 @@
 """The streaming bandwidth probe (``kda_stream_probe``) that bench.py's
-ceilings come from: each mode moves exactly the bytes it says."""
+ceilings come from: each mode moves exactly the bytes it says; and the
+matrix-core issue probe (``kda_mfma_probe``) beside it."""
 import pytest
 import torch
 
@@ -30,3 +31,19 @@ def test_stream_probe_modes(n, grid):
     K.stream_probe(K.KDA_STREAM_READ, src, sink, grid)
     torch.cuda.synchronize()
     assert torch.equal(src, keep)
+
+
+def test_mfma_probe_rates():
+    """The matrix-core issue probe: eight independent accumulators reach the
+    bf16 16x16x32 product's throughput (16 clocks at the published 2.5
+    PFLOP/s dense peak, 256 CUs, 2.4 GHz), one accumulator is bound by its
+    dependent latency, and the clock ratio gives a plausible core clock."""
+    K = lap.kda
+    announce("mfma probe chains 1, 2, 8")
+    r = {c: K.mfma_probe(c, 2048) for c in (1, 2, 8)}
+    for c, x in r.items():
+        announce("  chains %d: %.1f core clocks a product at %.0f MHz" % (c, x["clocks_per_product"],
+                                                                        x["core_MHz"]))
+        assert 500 < x["core_MHz"] < 3500
+    assert 15.0 <= r[8]["clocks_per_product"] <= 24.0
+    assert r[1]["clocks_per_product"] > r[2]["clocks_per_product"] >= r[8]["clocks_per_product"]
