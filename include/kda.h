@@ -153,7 +153,13 @@ typedef struct {
  * intra-chunk kernel that writes the records of its chunks into the
  * workspace and a state scan that consumes them, so the workspace holds one
  * window's records (the prhub report on SGLang PR #32890, section "实现拆解",
- * splits the prefill into the same two stages).
+ * splits the prefill into the same two stages).  Chunk ids number the
+ * 64-row chunks of all sequences without a prefix sum: the j-th chunk of
+ * sequence n (rows from start_n) has id floor(start_n / 64) + n + j, and
+ * every id is below floor((total_rows - 1) / 64) + num_seqs (num_seqs when
+ * total_rows is 0); a window takes window_chunks consecutive ids.  The
+ * library's choice: two windows for calls with at most 64 (sequence, head)
+ * pairs and at least 32 ids, one otherwise.
  */
 int32_t kda_prefill_windows(const kda_prefill_desc_t *desc);
 
