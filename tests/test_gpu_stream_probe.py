@@ -39,11 +39,12 @@ def test_mfma_probe_rates():
     PFLOP/s dense peak, 256 CUs, 2.4 GHz), one accumulator is bound by its
     dependent latency, and the clock ratio gives a plausible core clock."""
     K = lap.kda
-    announce("mfma probe chains 1, 2, 8")
-    r = {c: K.mfma_probe(c, 2048) for c in (1, 2, 8)}
+    announce("mfma probe chains 1, 2, 4, 8")
+    r = {c: K.mfma_probe(c, 2048) for c in (1, 2, 4, 8)}
     for c, x in r.items():
         announce("  chains %d: %.1f core clocks a product at %.0f MHz" % (c, x["clocks_per_product"],
                                                                         x["core_MHz"]))
         assert 500 < x["core_MHz"] < 3500
     assert 15.0 <= r[8]["clocks_per_product"] <= 24.0
     assert r[1]["clocks_per_product"] > r[2]["clocks_per_product"] >= r[8]["clocks_per_product"]
+    assert r[4]["clocks_per_product"] <= r[2]["clocks_per_product"]
